@@ -1,0 +1,143 @@
+/*
+ * spec_softmax.h -- C ABI of the MI355X (gfx950) speculative-sampling verify
+ * library libspec_softmax.so.
+ *
+ * The operation is the verify step of speculative sampling (SpS) as stated on
+ * the wikillm.com card for arXiv 2302.01318, "Accelerating Large Language
+ * Model Decoding with Speculative Sampling" (Chen et al., DeepMind):
+ *   - Method, "Algorithm: Speculative Sampling (SpS)" (alg. 2), step 2: the
+ *     target model gives K+1 distributions q_0..q_K for one sequence, q_t
+ *     conditioned on the first t drafted tokens; the draft model gave p_0..p_{K-1}
+ *     and drew token x_t from p_t (step 1).
+ *   - Method, "Decoding transforms": temperature T is applied to both p and q
+ *     before anything else; here q_t = softmax(z^q_t / T), p_t = softmax(z^p_t / T).
+ *   - Method, "Modified rejection sampling" (paper sec. 4.2) and alg. 2 step 3:
+ *     left to right, accept x_t when u_t < min(1, q_t(x_t) / p_t(x_t)); stop at
+ *     the first rejection.
+ *   - Same passage and alg. 2 step 4, with the Pitfalls notes: at the first
+ *     rejection, at position n, draw one token from (q_n - p_n)_+ =
+ *     max(0, q_n - p_n) / sum max(0, q_n - p_n); if the residual has no mass
+ *     fall back to q_n; if all K were accepted draw a bonus token from q_K.
+ *   Each sequence therefore emits between 1 and K+1 tokens.
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller, contiguous,
+ *     row-major, aligned to their element size.  The library keeps no pointer
+ *     after a call returns, allocates no device memory and holds no state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting.  Results are valid once the stream
+ *     reaches that point.
+ *   - Logit layouts: target [B][K+1][V] and draft [B][K][V], V contiguous.
+ *     dtype SPEC_DTYPE_F32 = IEEE binary32, SPEC_DTYPE_BF16 = bfloat16 (the
+ *     upper 16 bits of a binary32).  -inf logits are allowed (probability 0).
+ *   - Row statistics ("stats"): float[rows][2] = {m, s} with
+ *       m = max_x z[x]   (exactly the largest stored logit),
+ *       s = sum_x exp((z[x] - m) / T)   (in [1, V] for a valid row).
+ *     Then q(x) = exp((z[x] - m) / T) / s.  A row that holds a NaN or whose
+ *     maximum is +-inf (all -inf included) defines no distribution: its s is
+ *     NaN.
+ *   - Uniforms: float[B][K+1] in [0, 1): slot [b][t] (t < K) drives accept
+ *     test t, slot [b][K] the final residual/bonus draw.  They are inputs so
+ *     that a run is reproducible; the caller draws them.
+ *   - Argument errors are reported synchronously (status code, nothing
+ *     enqueued).  Bad device data is reported per sequence: a draft token
+ *     outside [0, V) or a row that defines no distribution makes that
+ *     sequence's num_accepted -1 and its out_tokens all -1; no out-of-bounds
+ *     access happens.
+ *   - Limits: 1 <= B, 1 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V,
+ *     T finite and > 0, B*(K+1)*V < 2^62.
+ */
+#ifndef SPEC_SOFTMAX_H
+#define SPEC_SOFTMAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_DTYPE_F32 0
+#define SPEC_DTYPE_BF16 1
+
+#define SPEC_OK 0
+#define SPEC_ERR_INVALID_ARG 1
+#define SPEC_ERR_UNSUPPORTED 2
+#define SPEC_ERR_LAUNCH 3
+
+#define SPEC_MAX_K 64
+#define SPEC_MAX_V (1 << 20)
+
+/*
+ * spec_softmax_stats -- temperature softmax statistics of every row.
+ * Defines: "Decoding transforms" (temperature on both p and q) and alg. 2
+ * step 2 ("K+1 target distributions"); q and p themselves are never stored.
+ *   target_logits  [B][K+1][V]  dtype
+ *   draft_logits   [B][K][V]    dtype
+ *   target_stats   out float[B][K+1][2] = {m, s} per target row
+ *   draft_stats    out float[B][K][2]   = {m, s} per draft row
+ * Every logit is read once.  s is accumulated in fp32 from exp2 with a
+ * row-wise running maximum and combined across threads in fp64; its relative
+ * error is about 1e-7.
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG (null pointer, bad size, dtype or T,
+ * misaligned pointer) or SPEC_ERR_LAUNCH.
+ */
+int spec_softmax_stats(const void* target_logits, const void* draft_logits, int dtype,
+                       int B, int K, int V, float temperature,
+                       float* target_stats, float* draft_stats, void* stream);
+
+/*
+ * spec_verify -- accept scan of every sequence.
+ * Defines: "Modified rejection sampling" (sec. 4.2) and alg. 2 step 3:
+ * accept x_t iff u_t < min(1, q_t(x_t)/p_t(x_t)); with p_t(x_t) = 0 accept iff
+ * q_t(x_t) > 0.  q and p at the drafted token are formed in fp64 from the
+ * stored logit and the row stats.
+ *   draft_tokens   [B][K] int32 (x_t was drawn from p_t)
+ *   uniforms       [B][K+1] float (slots 0..K-1 used here)
+ *   target_stats, draft_stats   as written by spec_softmax_stats
+ *   num_accepted   out int32[B]: n_b in [0, K], or -1 for an invalid sequence
+ *   out_tokens     out int32[B][K+1]: [b][t] = x_t for t < n_b, -1 elsewhere
+ *                  (position n_b is filled by spec_residual_sample)
+ *   probs          optional out float[B][K][2] = {q_t(x_t), p_t(x_t)} for every t
+ *                  (NaN for an invalid sequence); pass NULL to skip
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, const float* uniforms,
+                const float* target_stats, const float* draft_stats,
+                int B, int K, int V, float temperature,
+                int32_t* num_accepted, int32_t* out_tokens, float* probs, void* stream);
+
+/*
+ * spec_residual_sample -- the one final token of every sequence.
+ * Defines: "Modified rejection sampling" (sec. 4.2), alg. 2 step 4 and the
+ * Pitfalls notes.  With n = num_accepted[b]:
+ *   n < K : weights w = max(0, q_n - p_n); if they have no mass, w = q_n;
+ *   n == K: weights w = q_K (bonus token);
+ * and the token is the inverse-CDF draw in ascending token id,
+ *   x* = min { x : sum_{y<=x} w(y) > u_{b,K} * sum_y w(y) },
+ * which never picks a token of weight 0.  The weights, their sums and the
+ * prefix scan are formed in fp64; the row normalisers are recomputed in fp64
+ * from the logits (the fp32 s in the stats is not precise enough to place
+ * the draw).  Only the one or two rows at position n are read.
+ *   num_accepted   int32[B] as written by spec_verify (or chosen by the caller);
+ *                  a value outside [0, K] leaves out_tokens[b] untouched and
+ *                  writes num_emitted[b] = 0
+ *   out_tokens     in/out int32[B][K+1]: writes [b][n] only
+ *   num_emitted    optional out int32[B] = n + 1 (0 when nothing was drawn)
+ * A row at position n that defines no distribution writes out_tokens[b][n] = -1
+ * and num_emitted[b] = 0.
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_residual_sample(const void* target_logits, const void* draft_logits, int dtype,
+                         const float* uniforms, const float* target_stats,
+                         const float* draft_stats, const int32_t* num_accepted,
+                         int B, int K, int V, float temperature,
+                         int32_t* out_tokens, int32_t* num_emitted, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* spec_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_SOFTMAX_H */

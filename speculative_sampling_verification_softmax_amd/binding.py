@@ -1,0 +1,177 @@
+"""ctypes binding of libspec_softmax.so (the C ABI in include/spec_softmax.h).
+
+Argument marshalling only: every step of the verify runs in the HIP kernels.
+torch tensors supply device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``); nothing is computed in Python.
+There is no CPU fallback: if the library is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspec_softmax.so")
+
+SPEC_DTYPE_F32 = 0
+SPEC_DTYPE_BF16 = 1
+SPEC_OK = 0
+SPEC_MAX_K = 64
+SPEC_MAX_V = 1 << 20
+
+EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string")
+
+_lib = None
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (no build, no fallback) and declare signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise SpecError(f"{path} is missing: build it with "
+                        "`python -m speculative_sampling_verification_softmax_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.spec_softmax_stats.argtypes = [vp, vp, i32, i32, i32, i32, f32, vp, vp, vp]
+    L.spec_softmax_stats.restype = i32
+    L.spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp]
+    L.spec_verify.restype = i32
+    L.spec_residual_sample.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32,
+                                       vp, vp, vp]
+    L.spec_residual_sample.restype = i32
+    L.spec_status_string.argtypes = [i32]
+    L.spec_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(rc: int) -> str:
+    return load().spec_status_string(int(rc)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != SPEC_OK:
+        raise SpecError(f"{what}: {status_string(rc)}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _shapes(target: torch.Tensor, draft: torch.Tensor):
+    if target.dim() != 3 or draft.dim() != 3:
+        raise ValueError("target must be [B][K+1][V] and draft [B][K][V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if tuple(draft.shape) != (B, K, V):
+        raise ValueError(f"draft must be {(B, K, V)}, got {tuple(draft.shape)}")
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft must share a dtype")
+    return B, K, V
+
+
+def softmax_stats(target: torch.Tensor, draft: torch.Tensor, T: float,
+                  target_stats: Optional[torch.Tensor] = None,
+                  draft_stats: Optional[torch.Tensor] = None, stream=None):
+    """spec_softmax_stats: returns (target_stats [B][K+1][2], draft_stats [B][K][2])."""
+    B, K, V = _shapes(target, draft)
+    dev = target.device
+    if target_stats is None:
+        target_stats = torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev)
+    if draft_stats is None:
+        draft_stats = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    rc = load().spec_softmax_stats(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target), B, K, V, float(T),
+        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)), _stream(stream))
+    _check(rc, "spec_softmax_stats")
+    return target_stats, draft_stats
+
+
+def verify(target, draft, tokens, uniforms, target_stats, draft_stats, T: float,
+           num_accepted=None, out_tokens=None, probs=True, stream=None):
+    """spec_verify: returns (num_accepted [B], out_tokens [B][K+1], probs [B][K][2] or None)."""
+    B, K, V = _shapes(target, draft)
+    dev = target.device
+    if num_accepted is None:
+        num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if probs is True:
+        probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    elif probs is False:
+        probs = None
+    pp = None if probs is None else _dev(probs, "probs", torch.float32, (B, K, 2))
+    rc = load().spec_verify(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
+        _dev(tokens, "tokens", torch.int32, (B, K)),
+        _dev(uniforms, "uniforms", torch.float32, (B, K + 1)),
+        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)),
+        B, K, V, float(T),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1)), pp, _stream(stream))
+    _check(rc, "spec_verify")
+    return num_accepted, out_tokens, probs
+
+
+def residual_sample(target, draft, uniforms, target_stats, draft_stats, num_accepted, T: float,
+                    out_tokens, num_emitted=True, stream=None):
+    """spec_residual_sample: fills out_tokens[b][num_accepted[b]]; returns num_emitted."""
+    B, K, V = _shapes(target, draft)
+    if num_emitted is True:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=target.device)
+    elif num_emitted is False:
+        num_emitted = None
+    ne = None if num_emitted is None else _dev(num_emitted, "num_emitted", torch.int32, (B,))
+    rc = load().spec_residual_sample(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
+        _dev(uniforms, "uniforms", torch.float32, (B, K + 1)),
+        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        B, K, V, float(T), _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1)), ne,
+        _stream(stream))
+    _check(rc, "spec_residual_sample")
+    return num_emitted
+
+
+def verify_all(target, draft, tokens, uniforms, T: float, stream=None) -> dict:
+    """The whole verify (stats, accept scan, final draw) on one stream."""
+    ts, ds = softmax_stats(target, draft, T, stream=stream)
+    n, out, probs = verify(target, draft, tokens, uniforms, ts, ds, T, stream=stream)
+    ne = residual_sample(target, draft, uniforms, ts, ds, n, T, out, stream=stream)
+    return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=probs,
+                num_emitted=ne)

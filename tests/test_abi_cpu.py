@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/spec_softmax.h declares, and rejects bad arguments synchronously with
+SPEC_ERR_INVALID_ARG (validation runs before any HIP call, so no GPU is needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from speculative_sampling_verification_softmax_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_softmax.h")
+
+
+def _lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from speculative_sampling_verification_softmax_amd import build
+        build.build()
+    return binding.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(spec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(SPEC_\w+)\s+(\S+(?:\s*<<\s*\d+\))?)", text))
+    assert int(consts["SPEC_DTYPE_F32"]) == binding.SPEC_DTYPE_F32
+    assert int(consts["SPEC_DTYPE_BF16"]) == binding.SPEC_DTYPE_BF16
+    assert int(consts["SPEC_MAX_K"]) == binding.SPEC_MAX_K
+    assert eval(consts["SPEC_MAX_V"]) == binding.SPEC_MAX_V
+
+
+def test_status_strings():
+    L = _lib()
+    for rc in range(4):
+        assert L.spec_status_string(rc)
+    assert b"INVALID_ARG" in L.spec_status_string(1)
+    assert L.spec_status_string(99) == b"unknown status"
+
+
+# fake, never-dereferenced addresses: validation must reject before any launch
+P = 4096
+
+
+@pytest.mark.parametrize("args", [
+    dict(tgt=None), dict(dft=None), dict(dtype=2), dict(B=0), dict(K=0),
+    dict(K=binding.SPEC_MAX_K + 1), dict(V=0), dict(V=binding.SPEC_MAX_V + 1),
+    dict(T=0.0), dict(T=-1.0), dict(T=math.nan), dict(T=math.inf),
+    dict(tgt=P + 1), dict(ts=None), dict(ds=None), dict(ts=P + 2),
+])
+def test_stats_rejects_bad_arguments(args):
+    L = _lib()
+    a = dict(tgt=P, dft=P, dtype=1, B=2, K=3, V=100, T=1.0, ts=P, ds=P)
+    a.update(args)
+    rc = L.spec_softmax_stats(a["tgt"], a["dft"], a["dtype"], a["B"], a["K"], a["V"], a["T"],
+                              a["ts"], a["ds"], None)
+    assert rc == 1
+
+
+@pytest.mark.parametrize("missing", ["tok", "uni", "ts", "ds", "nacc", "out"])
+def test_verify_rejects_null_pointers(missing):
+    L = _lib()
+    a = dict(tok=P, uni=P, ts=P, ds=P, nacc=P, out=P)
+    a[missing] = None
+    rc = L.spec_verify(P, P, 0, a["tok"], a["uni"], a["ts"], a["ds"], 2, 3, 100, 1.0,
+                       a["nacc"], a["out"], None, None)
+    assert rc == 1
+
+
+@pytest.mark.parametrize("missing", ["uni", "ts", "ds", "nacc", "out"])
+def test_residual_rejects_null_pointers(missing):
+    L = _lib()
+    a = dict(uni=P, ts=P, ds=P, nacc=P, out=P)
+    a[missing] = None
+    rc = L.spec_residual_sample(P, P, 0, a["uni"], a["ts"], a["ds"], a["nacc"], 2, 3, 100, 1.0,
+                                a["out"], None, None)
+    assert rc == 1
+
+
+def test_residual_rejects_misaligned_optional_output():
+    L = _lib()
+    rc = L.spec_residual_sample(P, P, 0, P, P, P, P, 2, 3, 100, 1.0, P, P + 1, None)
+    assert rc == 1
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    binding_mod = binding
+    saved = binding_mod._lib
+    try:
+        binding_mod._lib = None
+        with pytest.raises(binding.SpecError):
+            binding_mod.load(str(tmp_path / "missing.so"))
+    finally:
+        binding_mod._lib = saved

@@ -1,0 +1,213 @@
+"""GPU edge cases of the verify path, each checked against the oracle (or a
+rule the pages fix): rows that define no distribution, out-of-range tokens,
+-inf masks, p == q, disjoint supports, one-hot rows (the greedy reduction in
+the Pitfalls notes), the zero-residual fallback to q, extreme logits and
+temperatures, and caller-supplied accepted counts."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from speculative_sampling_verification_softmax_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    binding.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(tgt, dft, tok, uni, T, dtype="f32"):
+    if dtype == "bf16":
+        t = torch.from_numpy(tgt).to(torch.bfloat16)
+        d = torch.from_numpy(dft).to(torch.bfloat16)
+    else:
+        t = torch.from_numpy(tgt)
+        d = torch.from_numpy(dft)
+    return dict(target=t.cuda(), draft=d.cuda(), tokens=torch.from_numpy(tok).cuda(),
+                uniforms=torch.from_numpy(uni).cuda(), T=T)
+
+
+def _check(inp, label):
+    say(f"[edge] {label}: shapes {tuple(inp['target'].shape)}")
+    g = parity.gpu_verify(inp)
+    host = synth.to_host_arrays(inp)
+    o = parity.oracle_verify(host)
+    rep = parity.compare(g, o, inp["T"])
+    say(f"[edge] {label}: flagged={len(rep['flagged'])} failures={rep['failures'][:3]}")
+    parity.assert_parity(rep, label)
+    return g, o
+
+
+def _uni(rng, B, K):
+    return (rng.integers(0, 1 << 24, (B, K + 1)) * 2.0 ** -24).astype(np.float32)
+
+
+def _tokens_from(rng, dft, T):
+    B, K, V = dft.shape
+    out = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for t in range(K):
+            r = oracle.softmax_row(np.ascontiguousarray(dft[b, t]), T)
+            out[b, t] = rng.choice(V, p=r[0]) if r is not None else 0
+    return out
+
+
+def test_invalid_rows_and_tokens_get_sentinels():
+    rng = np.random.default_rng(1)
+    B, K, V = 8, 3, 300
+    tgt = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    dft = (tgt[:, :K] + 0.3 * rng.standard_normal((B, K, V))).astype(np.float32)
+    tok = _tokens_from(rng, dft, 1.0)
+    tgt[1, 3, 17] = np.nan          # NaN in a bonus row
+    dft[2, 1, :] = -np.inf          # draft row with no mass
+    tgt[3, 0, 5] = np.inf           # +inf logit
+    tok[4, 2] = V                   # out of range
+    tok[5, 0] = -1
+    tgt[6, 2, :] = -np.inf          # target row with no mass
+    g, o = _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0), "invalid")
+    for b in range(1, 7):
+        assert g["num_accepted"][b] == -1 and np.all(g["out_tokens"][b] == -1)
+        assert g["num_emitted"][b] == 0
+        assert np.isnan(g["probs"][b]).all()
+    assert g["num_accepted"][0] >= 0 and g["num_accepted"][7] >= 0
+    assert np.isnan(g["target_stats"][1, 3, 1]) and np.isnan(g["draft_stats"][2, 1, 1])
+    assert np.isnan(g["target_stats"][3, 0, 1]) and np.isnan(g["target_stats"][6, 2, 1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_masked_rows(dtype):
+    rng = np.random.default_rng(2)
+    B, K, V = 32, 5, 5000
+    tgt = (3 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    dft = (tgt[:, :K] + 0.8 * rng.standard_normal((B, K, V))).astype(np.float32)
+    tgt[rng.random(tgt.shape) < 0.4] = -np.inf
+    dft[rng.random(dft.shape) < 0.4] = -np.inf
+    tgt[:, :, 0] = 0.0
+    dft[:, :, 0] = 0.0
+    inp = _to_dev(tgt, dft, np.zeros((B, K), np.int32), _uni(rng, B, K), 0.9, dtype)
+    host = synth.to_host_arrays(inp)
+    inp["tokens"] = torch.from_numpy(_tokens_from(rng, host["draft"] if dtype == "f32"
+                                                  else _bf16_f32(host["draft"]), 0.9)).cuda()
+    _check(inp, f"masked-{dtype}")
+
+
+def _bf16_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_equal_rows_accept_all_and_bonus():
+    rng = np.random.default_rng(3)
+    B, K, V = 64, 4, 2000
+    tgt = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    dft = np.ascontiguousarray(tgt[:, :K])
+    tok = _tokens_from(rng, dft, 1.0)
+    g, _ = _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0), "p==q")
+    assert np.all(g["num_accepted"] == K)
+
+
+def test_disjoint_supports_reject_first():
+    rng = np.random.default_rng(4)
+    B, K, V = 32, 3, 512
+    tgt = np.full((B, K + 1, V), -np.inf, np.float32)
+    dft = np.full((B, K, V), -np.inf, np.float32)
+    tgt[:, :, :256] = rng.standard_normal((B, K + 1, 256))
+    dft[:, :, 256:] = rng.standard_normal((B, K, 256))
+    tok = _tokens_from(rng, dft, 1.0)
+    g, _ = _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0), "disjoint")
+    assert np.all(g["num_accepted"] == 0)
+    assert np.all(g["out_tokens"][:, 0] < 256)
+
+
+def test_one_hot_rows_greedy_rule():
+    rng = np.random.default_rng(5)
+    B, K, V = 64, 6, 100
+    a_q = rng.integers(0, V, (B, K + 1))
+    a_p = np.where(rng.random((B, K)) < 0.7, a_q[:, :K], rng.integers(0, V, (B, K)))
+    tgt = np.full((B, K + 1, V), -np.inf, np.float32)
+    dft = np.full((B, K, V), -np.inf, np.float32)
+    for b in range(B):
+        tgt[b, np.arange(K + 1), a_q[b]] = 5.0
+        dft[b, np.arange(K), a_p[b]] = 5.0
+    g, _ = _check(_to_dev(tgt, dft, a_p.astype(np.int32), _uni(rng, B, K), 1.0), "one-hot")
+    for b in range(B):
+        mism = np.nonzero(a_p[b] != a_q[b, :K])[0]
+        n = int(mism[0]) if len(mism) else K
+        assert g["num_accepted"][b] == n
+        assert list(g["out_tokens"][b, :n + 1]) == list(a_q[b, :n]) + [a_q[b, n]]
+
+
+@pytest.mark.parametrize("T", [0.05, 0.3, 3.0, 20.0])
+def test_temperature_extremes(T):
+    inp = synth.make_inputs(synth.workload("small", B=32, T=T, name=f"T{T}"), seed=9,
+                            device="cuda")
+    _check(inp, f"T={T}")
+
+
+def test_extreme_logit_magnitudes():
+    rng = np.random.default_rng(6)
+    B, K, V = 16, 3, 1000
+    tgt = (rng.standard_normal((B, K + 1, V)) * 1e4).astype(np.float32)
+    tgt[:, :, :10] = 3e37
+    tgt[:, :, 10:20] = -3e37
+    dft = (tgt[:, :K] + 1e3 * rng.standard_normal((B, K, V))).astype(np.float32)
+    tok = _tokens_from(rng, dft, 1.0)
+    _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0), "extreme")
+
+
+def test_forced_counts_and_zero_residual_fallback():
+    """Caller-supplied accepted counts: identical rows at the rejected position
+    give a residual with no mass, so the draw falls back to q (Pitfalls)."""
+    rng = np.random.default_rng(7)
+    B, K, V = 24, 4, 3000
+    tgt = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    dft = (tgt[:, :K] + 0.5 * rng.standard_normal((B, K, V))).astype(np.float32)
+    n_forced = rng.integers(0, K + 1, B).astype(np.int32)
+    for b in range(0, B, 2):           # identical rows at the forced position
+        if n_forced[b] < K:
+            dft[b, n_forced[b]] = tgt[b, n_forced[b]]
+    n_forced[3] = -1
+    n_forced[5] = K + 1
+    uni = _uni(rng, B, K)
+    inp = _to_dev(tgt, dft, np.zeros((B, K), np.int32), uni, 1.0)
+    ts, ds = binding.softmax_stats(inp["target"], inp["draft"], 1.0)
+    out = torch.full((B, K + 1), 77, dtype=torch.int32, device="cuda")
+    nacc = torch.from_numpy(n_forced).cuda()
+    ne = binding.residual_sample(inp["target"], inp["draft"], inp["uniforms"], ts, ds, nacc, 1.0,
+                                 out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ne = ne.cpu().numpy()
+    ref = oracle.final_draw(tgt, dft, uni, n_forced, 1.0)
+    for b in range(B):
+        n = n_forced[b]
+        if n < 0 or n > K:
+            assert ne[b] == 0 and np.all(out[b] == 77)
+            continue
+        assert ne[b] == n + 1
+        if out[b, n] != ref["token"][b]:
+            assert ref["draw_dist"][b] < parity.BOUNDARY, (b, out[b, n], ref["token"][b])
+        others = np.delete(out[b], n)
+        assert np.all(others == 77)
+    assert np.sum(ref["draw_kind"] == 2) >= 5
+
+
+def test_binding_rejects_bad_tensors():
+    inp = synth.make_inputs("tiny", seed=0, device="cuda")
+    with pytest.raises(ValueError):
+        binding.softmax_stats(inp["target"].cpu(), inp["draft"].cpu(), 1.0)
+    with pytest.raises(binding.SpecError):
+        binding.softmax_stats(inp["target"], inp["draft"], 0.0)
+    with pytest.raises(TypeError):
+        binding.softmax_stats(inp["target"].double(), inp["draft"].double(), 1.0)

@@ -1,0 +1,112 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded input bytes, for every workload shape and for ragged shapes.
+
+Workloads (speculative_sampling_verification_softmax_amd.synth): tiny, batch1,
+small, headline (all sequences checked) and large (a sample of sequences
+checked; the launch is the full B=1024, K=16, V=256000 fp32 batch)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+from speculative_sampling_verification_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    from speculative_sampling_verification_softmax_amd import binding
+    binding.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(wl, seed, B=None, seqs=None, label=""):
+    say(f"[case] {label or wl if isinstance(wl, str) else wl.name} seed={seed} B={B} -> generate")
+    inp = synth.make_inputs(wl, seed=seed, device="cuda", B=B)
+    w = inp["workload"]
+    say(f"[case] {w.name} B={w.B} K={w.K} V={w.V} {w.dtype} T={w.T} -> gpu verify")
+    g = parity.gpu_verify(inp)
+    if seqs is not None:
+        idx = torch.as_tensor(seqs, device="cuda")
+        sub = dict(target=inp["target"][idx], draft=inp["draft"][idx], tokens=inp["tokens"][idx],
+                   uniforms=inp["uniforms"][idx], T=inp["T"])
+        host = synth.to_host_arrays(sub)
+        o = parity.oracle_verify(host)
+    else:
+        host = synth.to_host_arrays(inp)
+        o = parity.oracle_verify(host)
+    rep = parity.compare(g, o, w.T, seqs=None if seqs is None else np.asarray(seqs))
+    say(f"[case] {w.name} seed={seed}: seqs={rep['sequences']} draws={rep['draws']} "
+        f"flagged={len(rep['flagged'])} failures={len(rep['failures'])} "
+        f"stats_rel={rep['stats_max_rel']:.2e} probs_rel={rep['probs_max_rel']:.2e} "
+        f"accept_hist={rep['accept_hist']}")
+    return rep
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_tiny_many_sequences(seed):
+    parity.assert_parity(run_case("tiny", seed, B=4096), "tiny")
+
+
+def test_batch1_latency_shape():
+    total_draws, flagged = 0, 0
+    for seed in range(8):
+        rep = run_case("batch1", seed)
+        assert rep["failures"] == [], rep["failures"]
+        total_draws += rep["draws"]
+        flagged += len(rep["flagged"])
+    assert flagged <= max(1, parity.MAX_FLAGGED_FRACTION * total_draws)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_small_batch(seed):
+    parity.assert_parity(run_case("small", seed), "small")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_headline_all_sequences(seed):
+    rep = run_case("headline", seed)
+    parity.assert_parity(rep, "headline")
+    assert rep["sequences"] == 256
+
+
+def test_large_sampled_sequences():
+    rng = np.random.default_rng(0)
+    seqs = np.sort(rng.choice(1024, size=48, replace=False))
+    rep = run_case("large", 0, seqs=seqs)
+    parity.assert_parity(rep, "large")
+
+
+RAGGED = [
+    # (V, K, dtype, B) -- unaligned rows, tiny rows, the maximum K
+    (1, 1, "bf16", 3), (2, 2, "f32", 5), (63, 3, "bf16", 7), (65, 4, "f32", 9),
+    (777, 5, "bf16", 11), (1001, 2, "f32", 6), (4097, 64, "bf16", 3), (40000, 7, "f32", 5),
+    (129, 64, "f32", 2), (32003, 3, "bf16", 17),
+]
+
+
+@pytest.mark.parametrize("V,K,dtype,B", RAGGED)
+def test_ragged_shapes(V, K, dtype, B):
+    wl = synth.workload("batch1", V=V, K=K, dtype=dtype, B=B, T=0.7, name=f"ragged{V}")
+    rep = run_case(wl, seed=V + K)
+    parity.assert_parity(rep, f"V={V} K={K} {dtype}")
+
+
+def test_repeatable_and_stream_independent():
+    inp = synth.make_inputs("small", seed=5, device="cuda")
+    torch.cuda.synchronize()
+    a = parity.gpu_verify(inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = parity.gpu_verify(inp, stream=s)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
