@@ -3,17 +3,19 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
 
-One step = the whole verify of one batch: spec_softmax_stats (every target and
-draft row), spec_verify (accept scan), spec_residual_sample (residual or bonus
-draw), enqueued back to back on one stream, inputs resident in HBM.  W untimed
-steps, then K timed steps bracketed by device synchronisation.  Prints one
-JSON line on stdout; progress goes to stderr.
+One step = the whole verify of one batch: row statistics of every target and
+draft row, the accept scan and the residual or bonus draw, inputs resident in
+HBM.  --path fused (default) runs it as one spec_verify_fused launch;
+--path three_call as spec_softmax_stats, spec_verify, spec_residual_sample back
+to back on one stream.  W untimed steps, then K timed steps bracketed by device
+synchronisation.  Prints one JSON line on stdout; progress goes to stderr.
 
 Reported:
   value          verified sequences per second (B / seconds per step)
-  roofline       the dominant kernel (stats): algorithmic bytes per launch
-                 (every logit once + stats written) / its mean duration,
-                 timed with events on its own stream inside the timed region
+  roofline       the dominant kernel (fused: the fused kernel, algorithmic
+                 bytes = the whole step's compulsory bytes; three_call: the
+                 stats kernel, every logit once + stats written) / its mean
+                 duration, timed with events on its stream in the timed region
   cpu_baseline   the fp64 CPU oracle on the same input bytes (whole batch,
                  all host threads), sequences per second
 """
@@ -79,6 +81,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--path", default="fused", choices=["fused", "three_call"],
+                    help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
+                         "spec_verify, spec_residual_sample")
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences in the CPU oracle sample (0 = skip)")
     args = ap.parse_args()
@@ -106,7 +111,17 @@ def main() -> int:
     nemit = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    ws = binding.new_workspace(B, K, wl.V, tgt.dtype, dev)
+
+    def step_fused(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.verify_fused(tgt, dft, tok, uni, T, ws, ts, ds, nacc, out, probs, nemit,
+                             stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def step_three(ev=None):
         if ev is not None:
             ev[0].record(stream)
         binding.softmax_stats(tgt, dft, T, ts, ds, stream=stream)
@@ -114,6 +129,8 @@ def main() -> int:
             ev[1].record(stream)
         binding.verify(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, stream=stream)
         binding.residual_sample(tgt, dft, uni, ts, ds, nacc, T, out, nemit, stream=stream)
+
+    step = step_fused if args.path == "fused" else step_three
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -133,12 +150,16 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms = total_ms / args.steps
-    stats_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    log(f"[bench] {ms * 1e3:.1f} us/step, stats kernel {stats_ms * 1e3:.1f} us")
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if args.path == "fused":
+        dom_kernel, dom_bytes = "fused_kernel", step_bytes(wl)
+    else:
+        dom_kernel, dom_bytes = "stats_kernel", stats_bytes(wl)
+    log(f"[bench] {args.path}: {ms * 1e3:.1f} us/step, {dom_kernel} {dom_ms * 1e3:.1f} us")
 
     seqs_per_s = B / (ms * 1e-3)
     gbps_step = step_bytes(wl) / (ms * 1e-3) / 1e9
-    achieved = stats_bytes(wl) / (stats_ms * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     hist = torch.bincount(nacc.clamp(min=0).long(), minlength=K + 1).cpu().tolist()
 
     cpu = None
@@ -160,15 +181,15 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "K": K, "V": wl.V, "logits": wl.dtype,
-                   "T": wl.T, "seed": args.seed},
+                   "T": wl.T, "seed": args.seed, "path": args.path},
         "draft_rows_per_s": B * K / (ms * 1e-3),
         "achieved_GBps": gbps_step,
         "pct_of_peak": 100.0 * gbps_step / HBM_PEAK_GBPS,
         "accepted_hist": hist,
-        "roofline": {"bound": "hbm", "kernel": "stats_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_us": stats_ms * 1e3,
-                     "bytes_per_launch": stats_bytes(wl)},
+                     "traffic": None, "launch_us": dom_ms * 1e3,
+                     "bytes_per_launch": dom_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -50,6 +50,7 @@
 #ifndef SPEC_SOFTMAX_H
 #define SPEC_SOFTMAX_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -133,6 +134,42 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
                          const float* draft_stats, const int32_t* num_accepted,
                          int B, int K, int V, float temperature,
                          int32_t* out_tokens, int32_t* num_emitted, void* stream);
+
+/*
+ * spec_verify_workspace_size -- bytes of device workspace spec_verify_fused
+ * needs for this shape (0 for an invalid shape).  Independent of T.
+ */
+size_t spec_verify_workspace_size(int B, int K, int V, int dtype);
+
+/*
+ * spec_verify_fused -- the whole verify (spec_softmax_stats, spec_verify and
+ * spec_residual_sample together) in one persistent launch, with the same
+ * results.  The residual/bonus work of each sequence runs while the rows of
+ * later sequences are still streaming, so its cost hides under the HBM-bound
+ * row statistics.
+ * Defines: everything cited above (alg. 2 steps 2-4, sec. 4.2, Decoding
+ * transforms, Pitfalls).
+ *   inputs         as for the three calls (target, draft, tokens, uniforms)
+ *   target_stats, draft_stats, num_accepted, out_tokens   outputs as above
+ *   probs, num_emitted   optional outputs as above (NULL to skip)
+ *   workspace      device memory of at least spec_verify_workspace_size(...)
+ *                  bytes, 256-byte aligned, owned by the caller.  It must be
+ *                  all zero before its first use; every completed call leaves
+ *                  it zero again, so it can be reused call after call.  Two
+ *                  calls that are in flight at the same time need two
+ *                  workspaces.  A non-zero third 32-bit word after a call
+ *                  means a wait inside the kernel gave up (never expected);
+ *                  the workspace must then be cleared.
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG (also for a workspace that is too
+ * small or misaligned) or SPEC_ERR_LAUNCH.
+ */
+int spec_verify_fused(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const float* uniforms,
+                      int B, int K, int V, float temperature,
+                      float* target_stats, float* draft_stats,
+                      int32_t* num_accepted, int32_t* out_tokens, float* probs,
+                      int32_t* num_emitted, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* spec_status_string(int status);

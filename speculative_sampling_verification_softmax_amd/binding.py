@@ -23,7 +23,8 @@ SPEC_OK = 0
 SPEC_MAX_K = 64
 SPEC_MAX_V = 1 << 20
 
-EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string")
+EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
+           "spec_verify_workspace_size", "spec_verify_fused")
 
 _lib = None
 
@@ -49,6 +50,11 @@ def load(path: str = LIB_PATH):
     L.spec_residual_sample.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32,
                                        vp, vp, vp]
     L.spec_residual_sample.restype = i32
+    L.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.spec_verify_workspace_size.restype = ctypes.c_size_t
+    L.spec_verify_fused.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                    vp, vp, ctypes.c_size_t, vp]
+    L.spec_verify_fused.restype = i32
     L.spec_status_string.argtypes = [i32]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -175,3 +181,63 @@ def verify_all(target, draft, tokens, uniforms, T: float, stream=None) -> dict:
     ne = residual_sample(target, draft, uniforms, ts, ds, n, T, out, stream=stream)
     return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=probs,
                 num_emitted=ne)
+
+
+def workspace_size(B: int, K: int, V: int, dtype: torch.dtype) -> int:
+    """Bytes of workspace spec_verify_fused needs for this shape."""
+    code = SPEC_DTYPE_F32 if dtype == torch.float32 else SPEC_DTYPE_BF16
+    n = load().spec_verify_workspace_size(B, K, V, code)
+    if n == 0:
+        raise ValueError(f"invalid shape B={B} K={K} V={V}")
+    return int(n)
+
+
+def new_workspace(B: int, K: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """A zeroed workspace for spec_verify_fused (reusable: each completed call
+    leaves it zeroed)."""
+    return torch.zeros(workspace_size(B, K, V, dtype), dtype=torch.uint8, device=device)
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The workspace's error word (0 unless a wait inside the kernel gave up)."""
+    return int(workspace[8:12].view(torch.int32).item())
+
+
+def verify_fused(target, draft, tokens, uniforms, T: float, workspace: torch.Tensor,
+                 target_stats=None, draft_stats=None, num_accepted=None, out_tokens=None,
+                 probs=True, num_emitted=True, stream=None) -> dict:
+    """spec_verify_fused: the whole verify in one launch."""
+    B, K, V = _shapes(target, draft)
+    dev = target.device
+    if target_stats is None:
+        target_stats = torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev)
+    if draft_stats is None:
+        draft_stats = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if probs is True:
+        probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    elif probs is False:
+        probs = None
+    if num_emitted is True:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=dev)
+    elif num_emitted is False:
+        num_emitted = None
+    if workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    rc = load().spec_verify_fused(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
+        _dev(tokens, "tokens", torch.int32, (B, K)),
+        _dev(uniforms, "uniforms", torch.float32, (B, K + 1)), B, K, V, float(T),
+        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1)),
+        None if probs is None else _dev(probs, "probs", torch.float32, (B, K, 2)),
+        None if num_emitted is None else _dev(num_emitted, "num_emitted", torch.int32, (B,)),
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
+    _check(rc, "spec_verify_fused")
+    return dict(target_stats=target_stats, draft_stats=draft_stats, num_accepted=num_accepted,
+                out_tokens=out_tokens, probs=probs, num_emitted=num_emitted)

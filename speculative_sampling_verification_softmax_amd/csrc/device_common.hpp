@@ -4,8 +4,8 @@
 // Compiled with -ffp-contract=off: every floating-point expression rounds
 // exactly as written (fused multiply-adds only where fma()/fmaf() is called),
 // so two evaluations of the same expression on the same inputs always give
-// the same bits.  The residual kernel relies on that to re-derive one chunk's
-// prefix sums identically.
+// the same bits.  The residual draw relies on that to re-derive one chunk's
+// weights identically.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,18 +34,53 @@ __device__ __forceinline__ float logit_f32(const void* base, int64_t i) {
   }
 }
 
+// The 16 bytes at a 16-byte aligned address as fp32 values (8 bf16 or 4 fp32).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& v, float (&x)[16 / Elt<DT>::bytes]) {
+  if constexpr (DT == kBF16) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+  } else {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
+}
+
+// E = 16/elt consecutive logits starting at x0 (a multiple of E); positions at
+// or past V read as -inf.  One 16-byte load when the row start is 16-byte
+// aligned and the group is whole, element loads otherwise.
+template <int DT>
+__device__ __forceinline__ void load_group(const void* row, int64_t x0, int V, bool aligned,
+                                           float (&z)[16 / Elt<DT>::bytes]) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  if (aligned && x0 + E <= V) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
+                                                    x0 * Elt<DT>::bytes);
+    unpack16<DT>(v, z);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      z[e] = (x0 + e < V) ? logit_f32<DT>(row, x0 + e) : -__builtin_huge_valf();
+  }
+}
+
 // A row defines a distribution iff its max is finite and its sum is not NaN.
 __device__ __forceinline__ bool row_ok(float m, float s) {
   return !__builtin_isnan(s) && __builtin_isfinite(m);
 }
 
 // ---------------------------------------------------------------- wave64 ops
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
+// Butterfly sum: every lane ends with the same bits (a+b == b+a exactly).
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = v + __shfl_xor(v, o, kWave);
@@ -54,7 +89,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 // Inclusive prefix sum across the 64 lanes (Hillis-Steele order, fixed).
 __device__ __forceinline__ double wave_incl_scan(double v) {
-  const int lane = threadIdx.x & (kWave - 1);
+  const int lane = lane_id();
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     double o = __shfl_up(v, d, kWave);
@@ -64,13 +99,14 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 }
 
 // ---------------------------------------------------------------- block ops
-// `red` must hold at least BLOCK/64 entries of the reduced type.
+// `red` must hold at least BLOCK/64 entries of the reduced type.  The result
+// is returned to every thread.
 template <int BLOCK>
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
-  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
   __syncthreads();
-  if (lane == 0) red[w] = v;
+  if (lane_id() == 0) red[w] = v;
   __syncthreads();
   float r = red[0];
 #pragma unroll
@@ -81,9 +117,9 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 template <int BLOCK>
 __device__ __forceinline__ double block_sum(double v, double* red) {
   v = wave_sum(v);
-  const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
   __syncthreads();
-  if (lane == 0) red[w] = v;
+  if (lane_id() == 0) red[w] = v;
   __syncthreads();
   double r = red[0];
 #pragma unroll
@@ -92,36 +128,125 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 }
 
 // ---------------------------------------------------------------- fp64 exp
-// exp(d) for d <= 0 with relative error below 1e-13, in the form
-//   d * 64/ln2 = y = k + r,  k = rint(y), |r| <= 1/2,
-//   exp(d) = 2^(k>>6) * 2^((k&63)/64) * 2^(r/64),
-// with 2^(j/64) from a 64-entry table (tab, filled by fill_exp2_table) and
-// 2^(r/64) = exp(r ln2/64) by its degree-4 Taylor polynomial
-// (|r ln2/64| <= 0.0055, truncation error <= 4e-14).  Callers pass y, the
-// argument already multiplied by 64/ln2.  Results below ~2^-1060 flush to 0.
+// exp(d) for d <= 0 with relative error below 2e-13, in the form
+//   d * 256/ln2 = y = k + r,  k = rint(y), |r| <= 1/2,
+//   exp(d) = 2^(k>>8) * 2^((k&255)/256) * 2^(r/256),
+// with 2^(j/256) from a 256-entry table (tab, filled by fill_exp2_table) and
+// 2^(r/256) = exp(r ln2/256) by its degree-3 Taylor polynomial
+// (|r ln2/256| <= 0.00136, truncation error <= 1.5e-13).  Callers pass y, the
+// argument already multiplied by 256/ln2.  Results below ~2^-1062 flush to 0.
 struct Exp64 {
+  static constexpr int kTab = 256;
   static constexpr double kLn2 = 0.693147180559945309417232121458176568;
-  static constexpr double kScale = 64.0 / kLn2;   // 64 / ln 2
-  static constexpr double c1 = kLn2 / 64.0;
+  static constexpr double kScale = 256.0 / kLn2;
+  static constexpr double c1 = kLn2 / 256.0;
   static constexpr double c2 = c1 * c1 / 2.0;
   static constexpr double c3 = c1 * c1 * c1 / 6.0;
-  static constexpr double c4 = c1 * c1 * c1 * c1 / 24.0;
 };
 
 __device__ __forceinline__ void fill_exp2_table(double* tab) {
-  for (int j = threadIdx.x; j < 64; j += blockDim.x) tab[j] = exp2(static_cast<double>(j) / 64.0);
+  for (int j = threadIdx.x; j < Exp64::kTab; j += blockDim.x)
+    tab[j] = exp2(static_cast<double>(j) / Exp64::kTab);
 }
 
+// Branch-free: y below the range (or -inf, NaN) evaluates a clamped argument
+// and selects 0.
 __device__ __forceinline__ double exp64_scaled(double y, const double* tab) {
-  if (!(y > -67900.0)) return 0.0;  // also -inf
-  const double k = rint(y);
-  const double r = y - k;
+  const double yc = fmax(y, -272000.0);
+  const double k = rint(yc);
+  const double r = yc - k;
   const int ki = static_cast<int>(k);
-  double p = fma(r, Exp64::c4, Exp64::c3);
-  p = fma(r, p, Exp64::c2);
+  double p = fma(r, Exp64::c3, Exp64::c2);
   p = fma(r, p, Exp64::c1);
   p = fma(r, p, 1.0);
-  return ldexp(tab[ki & 63] * p, ki >> 6);
+  const double v = ldexp(tab[ki & 255] * p, ki >> 8);
+  return (y > -272000.0) ? v : 0.0;
+}
+
+// ------------------------------------------------- cross-workgroup handoff
+// Values handed from one workgroup to another inside one launch (possibly on
+// another XCD, whose L2 is not coherent with this one) move through
+// device-scope relaxed atomic loads and stores: on gfx950 these are ordinary
+// vector loads/stores with the sc1 bit, which go to the device-coherent
+// level instead of a possibly stale or dirty XCD L2 line.  A publisher makes
+// its sc1 stores complete (store_complete: s_waitcnt on the wave's memory
+// counter) before the workgroup barrier and the counter/flag update that
+// announces them; a consumer reads the flag, then the data, both with sc1.
+// This avoids device-scope fences, which write back and invalidate the whole
+// L2 of the XCD each time.
+__device__ __forceinline__ unsigned atomic_add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned atomic_load_dev(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_dev(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this wave's outstanding memory operations have completed.
+__device__ __forceinline__ void store_complete() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Loads and stores of handed-off values.  XB = false gives plain accesses
+// (single-workgroup or single-kernel use); XB = true the sc1 form above.
+template <bool XB>
+__device__ __forceinline__ float ld(const float* p) {
+  if constexpr (XB) {
+    return __uint_as_float(
+        __hip_atomic_load(reinterpret_cast<const unsigned*>(p), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT));
+  } else {
+    return *p;
+  }
+}
+template <bool XB>
+__device__ __forceinline__ double ld(const double* p) {
+  if constexpr (XB) {
+    return __longlong_as_double(static_cast<long long>(
+        __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT)));
+  } else {
+    return *p;
+  }
+}
+template <bool XB>
+__device__ __forceinline__ int ld(const int* p) {
+  if constexpr (XB) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    return *p;
+  }
+}
+template <bool XB>
+__device__ __forceinline__ void st(float* p, float v) {
+  if constexpr (XB) {
+    __hip_atomic_store(reinterpret_cast<unsigned*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *p = v;
+  }
+}
+template <bool XB>
+__device__ __forceinline__ void st(double* p, double v) {
+  if constexpr (XB) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       static_cast<unsigned long long>(__double_as_longlong(v)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *p = v;
+  }
+}
+template <bool XB>
+__device__ __forceinline__ void st(int* p, int v) {
+  if constexpr (XB) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *p = v;
+  }
 }
 
 }  // namespace spec

@@ -1,11 +1,13 @@
-// kernels.hpp -- the three verify kernels for gfx950.
+// kernels.hpp -- the verify kernels for gfx950 and the device functions they
+// share.
 //
 //   stats_kernel     one workgroup per logit row: max m and s = sum exp((z-m)/T)
 //   verify_kernel    one wave per sequence: q, p at the drafted tokens, accept
 //                    tests, first rejection
-//   residual_kernel  one workgroup per sequence: fp64 residual (or bonus)
-//                    weights on the row(s) at the first rejection, chunk sums,
-//                    prefix scan and inverse-CDF draw
+//   residual_kernel  one workgroup per sequence: residual (or bonus) weights on
+//                    the row(s) at the first rejection and the inverse-CDF draw
+//   fused_kernel     persistent: all of the above in one launch, with the
+//                    residual work interleaved with the row streaming
 //
 // What is computed: wikillm.com card for arXiv 2302.01318, Method
 // ("Modified rejection sampling", paper sec. 4.2; "Algorithm: Speculative
@@ -16,22 +18,23 @@
 
 namespace spec {
 
-// ============================================================== stats_kernel
+// ================================================================ row stats
 //
-// HBM-bound streaming reduction.  Rows are split into an unaligned head, a
-// body of 16-byte vectors (8 bf16 or 4 fp32 per load, fully coalesced across
-// the wave) and a tail.  Each thread keeps a running (m, s): a group of
-// VPG vectors is loaded, its max taken, s rescaled once per group, then
-// s += exp2((x - m) * log2(e)/T) per element (x - m is exact for bf16
-// inputs; only the product by the constant rounds).  Thread partials are
-// brought to the row max and summed in fp64.
+// HBM-bound streaming reduction of one row.  The row is split into an
+// unaligned head, a body of 16-byte vectors (8 bf16 or 4 fp32 per load, fully
+// coalesced across the wave) and a tail.  Each thread keeps a running max m
+// and sum s: a group of VPG vectors is loaded, its max taken, the group's
+// terms exp2((x - m) * log2(e)/T) summed in fp32 (x - m is exact for bf16
+// inputs; only the product by the constant rounds), and the group sum added
+// to s, carried in fp64 and rescaled only when the max grows.  Thread partials
+// are brought to the row max and summed in fp64.  Relative error of s: a few
+// 1e-7.
 
 struct RowAcc {
   float m = -__builtin_huge_valf();
-  float s = 0.f;
+  double s = 0.0;
 };
 
-// Fold n values (already in fp32) into the running (m, s).
 template <int N>
 __device__ __forceinline__ void fold(RowAcc& a, const float (&x)[N], float c2) {
   float g = x[0];
@@ -40,50 +43,22 @@ __device__ __forceinline__ void fold(RowAcc& a, const float (&x)[N], float c2) {
   const float mn = fmaxf(a.m, g);
   // While every value seen is -inf the shift is 0 and all terms are exp2(-inf)=0.
   const float ms = (mn == -__builtin_huge_valf()) ? 0.f : mn;
-  float s = a.s * __builtin_amdgcn_exp2f((a.m - ms) * c2);
+  float gs = 0.f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) s = s + __builtin_amdgcn_exp2f((x[i] - ms) * c2);
+  for (int i = 0; i < N; ++i) gs = gs + __builtin_amdgcn_exp2f((x[i] - ms) * c2);
+  const float scale = (mn == a.m) ? 1.f : __builtin_amdgcn_exp2f((a.m - ms) * c2);
+  a.s = fma(a.s, static_cast<double>(scale), static_cast<double>(gs));
   a.m = mn;
-  a.s = s;
 }
 
-template <int DT>
-__device__ __forceinline__ void unpack(const uint4& v, float (&x)[16 / Elt<DT>::bytes]) {
-  if constexpr (DT == kBF16) {
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-  } else {
-    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
-  }
-}
-
+// {m, s} of one row, returned to every thread of the block.  A row with no
+// finite maximum gets s = NaN (NaN logits already make s NaN).
 template <int BLOCK, int DT, int VPG>
-__global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ tgt,
-                                                      const void* __restrict__ dft,
-                                                      int64_t n_tgt_rows, int V, float c2,
-                                                      float* __restrict__ tstats,
-                                                      float* __restrict__ dstats) {
+__device__ __forceinline__ void row_stats(const char* row, int V, float c2, float* red_f,
+                                          double* red_d, float& m_out, float& s_out) {
   constexpr int EB = Elt<DT>::bytes;
-  constexpr int EPV = 16 / EB;  // elements per 16-byte vector
-  __shared__ float red_f[BLOCK / kWave];
-  __shared__ double red_d[BLOCK / kWave];
-
-  int64_t r = blockIdx.x;
-  const char* row;
-  float* out;
-  if (r < n_tgt_rows) {
-    row = static_cast<const char*>(tgt) + r * static_cast<int64_t>(V) * EB;
-    out = tstats + 2 * r;
-  } else {
-    r -= n_tgt_rows;
-    row = static_cast<const char*>(dft) + r * static_cast<int64_t>(V) * EB;
-    out = dstats + 2 * r;
-  }
+  constexpr int EPV = 16 / EB;
   const int tid = threadIdx.x;
-
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
   int head = static_cast<int>(((16 - (addr & 15)) & 15) / EB);
   if (head > V) head = V;
@@ -91,7 +66,6 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ t
   const int tail0 = head + nvec * EPV;
 
   RowAcc acc;
-  // unaligned head and ragged tail: one element per thread
   if (tid < head) {
     float x[1] = {logit_f32<DT>(row, tid)};
     fold(acc, x, c2);
@@ -100,7 +74,6 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ t
     float x[1] = {logit_f32<DT>(row, tail0 + tid)};
     fold(acc, x, c2);
   }
-
   const uint4* vp = reinterpret_cast<const uint4*>(row + static_cast<int64_t>(head) * EB);
   constexpr int STEP = BLOCK * VPG;
   const int nfull = nvec / STEP;
@@ -113,59 +86,83 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ t
 #pragma unroll
     for (int u = 0; u < VPG; ++u) {
       float xu[EPV];
-      unpack<DT>(v[u], xu);
+      unpack16<DT>(v[u], xu);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
     }
     fold(acc, x, c2);
   }
   for (int i = nfull * STEP + tid; i < nvec; i += BLOCK) {
-    uint4 v = vp[i];
+    const uint4 v = vp[i];
     float x[EPV];
-    unpack<DT>(v, x);
+    unpack16<DT>(v, x);
     fold(acc, x, c2);
   }
-
-  // combine: row max, then every partial rescaled to it and summed in fp64
   const float m = block_max<BLOCK>(acc.m, red_f);
   const float ms = (m == -__builtin_huge_valf()) ? 0.f : m;
-  const double part = static_cast<double>(acc.s * __builtin_amdgcn_exp2f((acc.m - ms) * c2));
+  const float scale = (acc.m == m) ? 1.f : __builtin_amdgcn_exp2f((acc.m - ms) * c2);
+  const double part = acc.s * static_cast<double>(scale);
   const double s = block_sum<BLOCK>(part, red_d);
-  if (tid == 0) {
-    float sf = static_cast<float>(s);
-    if (!__builtin_isfinite(m)) sf = __builtin_nanf("");
+  float sf = static_cast<float>(s);
+  if (!__builtin_isfinite(m)) sf = __builtin_nanf("");
+  m_out = m;
+  s_out = sf;
+}
+
+template <int BLOCK, int DT, int VPG>
+__global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ tgt,
+                                                      const void* __restrict__ dft,
+                                                      int64_t n_tgt_rows, int V, float c2,
+                                                      float* __restrict__ tstats,
+                                                      float* __restrict__ dstats) {
+  __shared__ float red_f[BLOCK / kWave];
+  __shared__ double red_d[BLOCK / kWave];
+  int64_t r = blockIdx.x;
+  const char* row;
+  float* out;
+  if (r < n_tgt_rows) {
+    row = static_cast<const char*>(tgt) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+    out = tstats + 2 * r;
+  } else {
+    r -= n_tgt_rows;
+    row = static_cast<const char*>(dft) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+    out = dstats + 2 * r;
+  }
+  float m, s;
+  row_stats<BLOCK, DT, VPG>(row, V, c2, red_f, red_d, m, s);
+  if (threadIdx.x == 0) {
     out[0] = m;
-    out[1] = sf;
+    out[1] = s;
   }
 }
 
-// ============================================================= verify_kernel
+// =================================================================== verify
 //
 // One wave per sequence; lane t runs accept test t.  q_t(x_t) and p_t(x_t)
 // are formed in fp64 from the stored logit and the row stats, and the test
 // is u < min(1, q/p) written as (u < 1) && (u*p < q), which also covers
 // p = 0 (accept iff q > 0).  The first rejection is the lowest set bit of
-// the wave's reject ballot.
+// the wave's reject ballot.  Must be called by all 64 lanes of one wave.
+// XB: the stats come from other workgroups of the same launch (handoff loads,
+// see device_common.hpp).
 
-template <int DT>
-__global__ __launch_bounds__(kWave) void verify_kernel(
-    const void* __restrict__ tgt, const void* __restrict__ dft,
-    const int32_t* __restrict__ tokens, const float* __restrict__ uni,
-    const float* __restrict__ tstats, const float* __restrict__ dstats,
-    int K, int V, double invT, int32_t* __restrict__ num_accepted,
-    int32_t* __restrict__ out_tokens, float* __restrict__ probs) {
-  const int64_t b = blockIdx.x;
-  const int t = threadIdx.x;
+template <int DT, bool XB>
+__device__ int verify_seq(int64_t b, const void* tgt, const void* dft, const int32_t* tokens,
+                           const float* uni, const float* ts_b, const float* ds_b, int K,
+                           int V, double invT, int32_t* num_accepted, int32_t* out_tokens,
+                           float* probs, bool skip_final) {
+  // ts_b: this sequence's target stats [K+1][2]; ds_b: its draft stats [K][2].
+  // skip_final: leave out_tokens[b][n] to the final draw (written elsewhere).
+  const int t = lane_id();
   const int64_t K1 = K + 1;
   bool valid = true;
   bool reject = false;
   double q = 0.0, p = 0.0;
-  int x = -1;
   if (t < K) {
-    x = tokens[b * K + t];
+    const int x = tokens[b * K + t];
     const int64_t rq = b * K1 + t, rp = b * K + t;
-    const float mq = tstats[2 * rq], sq = tstats[2 * rq + 1];
-    const float mp = dstats[2 * rp], sp = dstats[2 * rp + 1];
+    const float mq = ld<XB>(&ts_b[2 * t]), sq = ld<XB>(&ts_b[2 * t + 1]);
+    const float mp = ld<XB>(&ds_b[2 * t]), sp = ld<XB>(&ds_b[2 * t + 1]);
     valid = row_ok(mq, sq) && row_ok(mp, sp) && x >= 0 && x < V;
     if (valid) {
       const double zq = logit_f32<DT>(tgt, rq * V + x);
@@ -173,270 +170,833 @@ __global__ __launch_bounds__(kWave) void verify_kernel(
       q = exp((zq - static_cast<double>(mq)) * invT) / static_cast<double>(sq);
       p = exp((zp - static_cast<double>(mp)) * invT) / static_cast<double>(sp);
       const double u = uni[b * K1 + t];
-      const bool acc = (u < 1.0) && (u * p < q);
-      reject = !acc;
+      reject = !((u < 1.0) && (u * p < q));
     }
   }
-  if (t == 0) {  // the bonus row is part of the sequence too
-    const int64_t rk = b * K1 + K;
-    valid = valid && row_ok(tstats[2 * rk], tstats[2 * rk + 1]);
-  }
+  if (t == 0)  // the bonus row is part of the sequence too
+    valid = valid && row_ok(ld<XB>(&ts_b[2 * K]), ld<XB>(&ts_b[2 * K + 1]));
   const bool all_valid = __all(valid);
   const unsigned long long rej = __ballot(reject);
   const int n = !all_valid ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : K);
   if (t == 0) num_accepted[b] = n;
-  for (int pos = t; pos <= K; pos += kWave) {
-    out_tokens[b * K1 + pos] = (pos < n) ? tokens[b * K + pos] : -1;
-  }
+  for (int pos = t; pos <= K; pos += kWave)
+    if (!(skip_final && pos == n)) out_tokens[b * K1 + pos] = (pos < n) ? tokens[b * K + pos] : -1;
   if (probs != nullptr && t < K) {
     const float nan = __builtin_nanf("");
     probs[2 * (b * K + t)] = all_valid ? static_cast<float>(q) : nan;
     probs[2 * (b * K + t) + 1] = all_valid ? static_cast<float>(p) : nan;
   }
+  return n;
 }
 
-// =========================================================== residual_kernel
+template <int DT>
+__global__ __launch_bounds__(kWave) void verify_kernel(
+    const void* __restrict__ tgt, const void* __restrict__ dft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uni,
+    const float* __restrict__ tstats, const float* __restrict__ dstats, int K, int V,
+    double invT, int32_t* __restrict__ num_accepted, int32_t* __restrict__ out_tokens,
+    float* __restrict__ probs) {
+  const int64_t b = blockIdx.x;
+  (void)verify_seq<DT, false>(b, tgt, dft, tokens, uni, tstats + 2 * b * (K + 1),
+                              dstats + 2 * b * K, K, V, invT, num_accepted, out_tokens, probs,
+                              false);
+}
+
+// ================================================================= residual
 //
-// One workgroup per sequence, on the row(s) at position n = num_accepted[b].
-// Weights (all fp64):
-//   residual  w(x) = max(0, e_q(x)/S_q - e_p(x)/S_p),  e(x) = exp((z(x)-m)/T)
+// Weights at position n = num_accepted[b] (all fp64, e(x) = exp((z(x)-m)/T)):
+//   residual  w(x) = max(0, e_q(x)/S_q - e_p(x)/S_p)
 //   fallback  w(x) = e_q(x) when the residual has no mass
 //   bonus     w(x) = e_q(x) on row K
 // (the draw is invariant to a common scale, so bonus/fallback weights stay
-// unnormalised).  S_q, S_p are recomputed in fp64 here.
+// unnormalised) and x* = min{x : sum_{y<=x} w(y) > u * sum_y w(y)}.
 //
-// Draw: the row is cut into chunks of 64*E tokens (E per lane, contiguous per
-// lane, lanes contiguous).  Pass B: every wave computes, per chunk, lane sums
-// in token order and their inclusive wave scan; the chunk total goes to LDS.
-// Pass C (wave 0): running prefix over chunk totals in chunk order, target =
-// u * S_w with S_w the final running value, first chunk whose inclusive prefix
-// exceeds the target.  Pass D (wave 0): the chosen chunk's lane sums and scan
-// are re-derived with the same code (identical bits under fp-contract=off),
-// then the first lane and the first token whose cumulative weight exceeds the
-// target.  A token of weight 0 is never chosen; if rounding leaves no
-// crossing (u*S_w >= S_w is impossible for u < 1, but u >= 1 or a NaN u is
-// tolerated) the last token of positive weight is chosen, as the oracle does.
+// The row is cut into chunks of 64*E tokens (E per lane, contiguous per lane,
+// lanes contiguous); one wave owns a chunk at a time and loads the next one
+// while it computes the current one.
+//
+// Fast path, one sweep over the row(s): every token's e_q, e_p (fp64 table
+// exponential) go into the normalisers S_q, S_p; the sign of the residual is
+// decided with the fp32 normalisers s~ from the stats, e_q*s~_p versus
+// e_p*s~_q, with a relative margin kDelta.  Tokens clearly positive add e_q
+// and e_p to the chunk's sums A_c, B_c; tokens clearly negative add nothing;
+// the few inside the margin are recorded (up to kUncMax per chunk) and
+// resolved once S_q, S_p are exact.  Then W_c = A_c/S_q - B_c/S_p (+ the
+// resolved tokens).  If the exact ratio S_q/S_p falls outside s~_q/s~_p by
+// more than kDelta/4, a chunk records more uncertain tokens than it can hold,
+// or the residual has no mass, the draw takes the exact slow path instead:
+// normalisers first, then every chunk's weights, two sweeps.
+//
+// Draw: running prefix over chunk totals in chunk order (wave 0), the first
+// chunk whose inclusive prefix exceeds u*S_w, then that chunk's weights are
+// re-derived token by token with the exact definition, and the first lane and
+// token whose cumulative weight exceeds the target are chosen.  A token of
+// weight 0 is never chosen; if rounding leaves no crossing, the last token of
+// positive weight is chosen, as the oracle does.
 
 enum : int { kModeResidual = 0, kModeBonus = 1 };
+constexpr int kUncMax = 2;
+constexpr double kDelta = 1.0 / 65536.0;
 
-// Weights of the E tokens of lane `lane` in chunk `c`; tokens >= V get 0.
-template <int DT, int E>
-__device__ __forceinline__ void lane_weights(const void* qrow, const void* prow, int V, int c,
-                                             int lane, int mode, double mq, double mp,
-                                             double yscale, double iq, double ip,
-                                             const double* tab, double (&w)[E]) {
-  const int64_t x0 = static_cast<int64_t>(c) * (kWave * E) + static_cast<int64_t>(lane) * E;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int64_t x = x0 + e;
-    double v = 0.0;
-    if (x < V) {
-      const double zq = logit_f32<DT>(qrow, x);
-      const double eq = exp64_scaled((zq - mq) * yscale, tab);
-      if (mode == kModeResidual) {
-        const double zp = logit_f32<DT>(prow, x);
-        const double ep = exp64_scaled((zp - mp) * yscale, tab);
-        const double d = eq * iq - ep * ip;
-        v = d > 0.0 ? d : 0.0;
-      } else {
-        v = eq;
-      }
-    }
-    w[e] = v;
+struct DrawRows {
+  const void* qrow;
+  const void* prow;
+  int V;
+  int mode;
+  bool aligned;       // both rows start on 16-byte boundaries
+  double yscale;      // (1/T) * 256/ln2
+  double mq, mp;      // row maxima (exact stored logits)
+  double sq_t, sp_t;  // fp32 normalisers from the stats (approximate)
+};
+
+// The rows at position n of sequence b and their stats.  Returns false when a
+// row there defines no distribution.
+template <int DT>
+__device__ __forceinline__ bool make_draw_rows(int64_t b, int n, int K, int V, const void* tgt,
+                                               const void* dft, float mq, float sq, float mp,
+                                               float sp, double yscale, DrawRows& R) {
+  constexpr int EB = Elt<DT>::bytes;
+  const bool resid = n < K;
+  const int64_t rq = b * (K + 1) + n, rp = resid ? b * K + n : 0;
+  R.qrow = static_cast<const char*>(tgt) + rq * static_cast<int64_t>(V) * EB;
+  R.prow = static_cast<const char*>(dft) + rp * static_cast<int64_t>(V) * EB;
+  R.V = V;
+  R.mode = resid ? kModeResidual : kModeBonus;
+  R.aligned =
+      ((reinterpret_cast<uintptr_t>(R.qrow) | reinterpret_cast<uintptr_t>(R.prow)) & 15) == 0;
+  R.yscale = yscale;
+  R.mq = mq;
+  R.mp = resid ? mp : 0.0;
+  R.sq_t = sq;
+  R.sp_t = resid ? sp : 1.0;
+  return row_ok(mq, sq) && (!resid || row_ok(mp, sp));
+}
+
+// e(x) of one token: exp((z - m)/T) = 2^((z - m) * yscale * ln2/256).  The
+// difference is taken first: it is exact (or correctly rounded) whatever the
+// magnitude of the logits, so the maximum gets exactly exp(0) = 1.
+__device__ __forceinline__ double tok_exp(float z, double yscale, double m, const double* tab) {
+  return exp64_scaled((static_cast<double>(z) - m) * yscale, tab);
+}
+
+// Raw 16-byte groups of one lane for one chunk (q row, and p row for a residual).
+struct RawChunk {
+  uint4 q, p;
+};
+
+template <int DT>
+__device__ __forceinline__ bool chunk_full(const DrawRows& R, int c) {
+  constexpr int CH = kWave * (16 / Elt<DT>::bytes);
+  return R.aligned && static_cast<int64_t>(c + 1) * CH <= R.V;
+}
+
+// Issue the loads of a full chunk (both rows together).
+template <int DT>
+__device__ __forceinline__ void chunk_issue(const DrawRows& R, int c, RawChunk& raw) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  const int64_t x0 = static_cast<int64_t>(c) * (kWave * E) + static_cast<int64_t>(lane_id()) * E;
+  const int64_t off = x0 * Elt<DT>::bytes;
+  raw.q = *reinterpret_cast<const uint4*>(static_cast<const char*>(R.qrow) + off);
+  if (R.mode == kModeResidual)
+    raw.p = *reinterpret_cast<const uint4*>(static_cast<const char*>(R.prow) + off);
+}
+
+// The lane's E values of both rows: from the issued loads for a full chunk,
+// element by element (-inf past V) otherwise.
+template <int DT>
+__device__ __forceinline__ void chunk_values(const DrawRows& R, int c, bool full,
+                                             const RawChunk& raw,
+                                             float (&zq)[16 / Elt<DT>::bytes],
+                                             float (&zp)[16 / Elt<DT>::bytes]) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  if (full) {
+    unpack16<DT>(raw.q, zq);
+    if (R.mode == kModeResidual) unpack16<DT>(raw.p, zp);
+  } else {
+    const int64_t x0 =
+        static_cast<int64_t>(c) * (kWave * E) + static_cast<int64_t>(lane_id()) * E;
+    load_group<DT>(R.qrow, x0, R.V, false, zq);
+    if (R.mode == kModeResidual) load_group<DT>(R.prow, x0, R.V, false, zp);
   }
 }
 
+// Exact weights of this lane's E tokens (used to re-derive the chosen chunk).
+template <int DT>
+__device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq, double ip,
+                                             const double* tab,
+                                             double (&w)[16 / Elt<DT>::bytes]) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  RawChunk raw;
+  const bool full = chunk_full<DT>(R, c);
+  if (full) chunk_issue<DT>(R, c, raw);
+  float zq[E], zp[E];
+  chunk_values<DT>(R, c, full, raw, zq, zp);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
+    if (R.mode == kModeResidual) {
+      const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
+      const double d = eq * iq - ep * ip;
+      w[e] = d > 0.0 ? d : 0.0;
+    } else {
+      w[e] = eq;
+    }
+  }
+}
+
+// Per-chunk results of a fast-path sweep (valid in every lane).
+struct ChunkSums {
+  double A, Bv;
+  int n_unc;
+  int unc[kUncMax];
+};
+
+// Fast-path arithmetic of one chunk from its values.  Adds every token's e_q,
+// e_p to the lane's lsq, lsp.
+template <int DT>
+__device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
+                                           const float (&zq)[16 / Elt<DT>::bytes],
+                                           const float (&zp)[16 / Elt<DT>::bytes],
+                                           const double* tab, double& lsq, double& lsp,
+                                           ChunkSums& out) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  double a = 0.0, bb = 0.0;
+  unsigned unc_bits = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
+    lsq = lsq + eq;
+    if (R.mode == kModeResidual) {
+      const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
+      lsp = lsp + ep;
+      const double r = ep * R.sq_t;
+      const double d = fma(eq, R.sp_t, -r);  // e_q s~_p - e_p s~_q
+      const bool certain = fabs(d) > r * kDelta || eq == 0.0;
+      if (certain && d > 0.0) {
+        a = a + eq;
+        bb = bb + ep;
+      }
+      if (!certain) unc_bits |= 1u << e;
+    } else {
+      a = a + eq;
+    }
+  }
+  out.A = wave_sum(a);
+  out.Bv = wave_sum(bb);
+  out.n_unc = 0;
+#pragma unroll
+  for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
+  if (R.mode == kModeResidual) {
+    const int x0 = c * (kWave * E) + lane_id() * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      unsigned long long m = __ballot((unc_bits >> e) & 1u);
+      while (m) {  // wave-uniform; rare
+        const int src = __ffsll(static_cast<long long>(m)) - 1;
+        const int idx = __shfl(x0, src, kWave) + e;
+#pragma unroll
+        for (int j = 0; j < kUncMax; ++j)
+          if (j == out.n_unc) out.unc[j] = idx;
+        out.n_unc += 1;
+        m &= m - 1;
+      }
+    }
+  }
+}
+
+// One wave sweeps chunks c0, c0+stride, ... < c1, loading each next chunk
+// while computing the current one; emit(c, sums) stores a chunk's results.
+template <int DT, typename Emit>
+__device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, int stride,
+                                           const double* tab, double& lsq, double& lsp,
+                                           Emit emit) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  if (c0 >= c1) return;
+  RawChunk cur, nxt;
+  bool cur_full = chunk_full<DT>(R, c0);
+  if (cur_full) chunk_issue<DT>(R, c0, cur);
+  for (int c = c0; c < c1; c += stride) {
+    const int cn = c + stride;
+    const bool nxt_full = cn < c1 && chunk_full<DT>(R, cn);
+    if (nxt_full) chunk_issue<DT>(R, cn, nxt);
+    float zq[E], zp[E];
+    chunk_values<DT>(R, c, cur_full, cur, zq, zp);
+    ChunkSums cs;
+    chunk_sums<DT>(R, c, zq, zp, tab, lsq, lsp, cs);
+    emit(c, cs);
+    cur = nxt;
+    cur_full = nxt_full;
+  }
+}
+
+// Running prefix over W[0..nch) by wave 0; result in sel[] / seld[] (LDS):
+//   sel[0] = chosen chunk (-3: no positive weight), sel[1] = 1 if a crossing
+//   was found, seld[0] = prefix before the chosen chunk, seld[1] = target,
+//   seld[2] = S_w.
+__device__ __forceinline__ void locate_chunk(const double* W, int nch, double u, int* sel,
+                                             double* seld) {
+  const int lane = lane_id();
+  const int per = (nch + kWave - 1) / kWave;
+  const int c0 = lane * per;
+  const int c1 = min(nch, c0 + per);
+  double lt = 0.0;
+  for (int c = c0; c < c1; ++c) lt = lt + W[c];
+  const double li = wave_incl_scan(lt);
+  double run = __shfl_up(li, 1, kWave);
+  if (lane == 0) run = 0.0;
+  double r = run;
+  for (int c = c0; c < c1; ++c) r = r + W[c];
+  const int last_lane = (nch - 1) / per;
+  const double S_w = __shfl(r, last_lane, kWave);
+  const double target = u * S_w;
+  int hit = -1, lastpos = -1;
+  double hit_excl = 0.0, lastpos_excl = 0.0;
+  r = run;
+  for (int c = c0; c < c1; ++c) {
+    const double tc = W[c];
+    const double nr = r + tc;
+    if (tc > 0.0) {
+      if (hit < 0 && nr > target) {
+        hit = c;
+        hit_excl = r;
+      }
+      lastpos = c;
+      lastpos_excl = r;
+    }
+    r = nr;
+  }
+  const unsigned long long hm = __ballot(hit >= 0);
+  const unsigned long long pm = __ballot(lastpos >= 0);
+  int s = -3;
+  double ex = 0.0;
+  if (hm) {
+    const int src = __ffsll(static_cast<long long>(hm)) - 1;
+    s = __shfl(hit, src, kWave);
+    ex = __shfl(hit_excl, src, kWave);
+  } else if (pm) {
+    const int src = 63 - __clzll(static_cast<long long>(pm));
+    s = __shfl(lastpos, src, kWave);
+    ex = __shfl(lastpos_excl, src, kWave);
+  }
+  if (lane == 0) {
+    sel[0] = s;
+    sel[1] = hm ? 1 : 0;
+    seld[0] = ex;
+    seld[1] = target;
+    seld[2] = S_w;
+  }
+}
+
+// Token inside chunk c (wave 0): returns the token id in every lane, or -1.
+template <int DT>
+__device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool crossing, double excl,
+                                             double target, double iq, double ip,
+                                             const double* tab) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  const int lane = lane_id();
+  double w[E];
+  lane_weights<DT>(R, c, iq, ip, tab, w);
+  double ls = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) ls = ls + w[e];
+  const double incl = wave_incl_scan(ls);
+  double lexcl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) lexcl = 0.0;
+  const bool lane_hit = crossing && ls > 0.0 && (excl + incl) > target;
+  const unsigned long long hm = __ballot(lane_hit);
+  const unsigned long long pm = __ballot(ls > 0.0);
+  const int src = hm ? (__ffsll(static_cast<long long>(hm)) - 1)
+                     : (pm ? 63 - __clzll(static_cast<long long>(pm)) : -1);
+  if (src < 0) return -1;
+  int pick = -1;
+  if (lane == src) {
+    const double base = excl + lexcl;
+    int lastpos = -1;
+    double a = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      a = a + w[e];
+      if (w[e] > 0.0) {
+        if (pick < 0 && hm && (base + a) > target) pick = e;
+        lastpos = e;
+      }
+    }
+    if (pick < 0) pick = lastpos;
+  }
+  pick = __shfl(pick, src, kWave);
+  return c * (kWave * E) + src * E + pick;
+}
+
+// LDS the draw routines need, per workgroup.
+template <int BLOCK>
+struct DrawShared {
+  double tab[Exp64::kTab];
+  double red[BLOCK / kWave];
+  float redf[BLOCK / kWave];
+  int sel[4];
+  double seld[4];
+};
+
+// Exact two-sweep draw (whole block).  W: nch doubles of scratch.  Returns the
+// token (every thread), or -1 when no token carries positive weight.
+template <int BLOCK, int DT>
+__device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh) {
+  constexpr int NW = BLOCK / kWave;
+  constexpr int E = 16 / Elt<DT>::bytes;
+  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
+  double iq = 1.0, ip = 1.0;
+  if (R.mode == kModeResidual) {
+    double aq = 0.0, ap = 0.0;
+    for (int c = wv; c < nch; c += NW) {
+      RawChunk raw;
+      const bool full = chunk_full<DT>(R, c);
+      if (full) chunk_issue<DT>(R, c, raw);
+      float zq[E], zp[E];
+      chunk_values<DT>(R, c, full, raw, zq, zp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        aq = aq + tok_exp(zq[e], R.yscale, R.mq, sh.tab);
+        ap = ap + tok_exp(zp[e], R.yscale, R.mp, sh.tab);
+      }
+    }
+    const double Sq = block_sum<BLOCK>(aq, sh.red);
+    const double Sp = block_sum<BLOCK>(ap, sh.red);
+    iq = 1.0 / Sq;
+    ip = 1.0 / Sp;
+  }
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    for (int c = wv; c < nch; c += NW) {
+      double w[E];
+      lane_weights<DT>(R, c, iq, ip, sh.tab, w);
+      double ls = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) ls = ls + w[e];
+      const double incl = wave_incl_scan(ls);
+      if (lane == kWave - 1) W[c] = incl;
+    }
+    __syncthreads();
+    if (wv == 0) locate_chunk(W, nch, u, sh.sel, sh.seld);
+    __syncthreads();
+    const bool empty_residual = R.mode == kModeResidual && !(sh.seld[2] > 0.0);
+    __syncthreads();
+    if (empty_residual && attempt == 0) {
+      R.mode = kModeBonus;  // residual has no mass: draw from q_n
+      continue;
+    }
+    break;
+  }
+  int tok = -1;
+  if (sh.sel[0] >= 0 && wv == 0)
+    tok = draw_in_chunk<DT>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0], sh.seld[1], iq, ip, sh.tab);
+  if (tid == 0) sh.sel[2] = tok;
+  __syncthreads();
+  tok = sh.sel[2];
+  __syncthreads();
+  return tok;
+}
+
+// Fast-path finish (whole block) from the sweep's results: chunk sums A, Bv,
+// uncertain lists, normaliser parts (XB: written by other workgroups).
+// Overwrites A with the chunk totals W_c.  Returns the token, -1 (nothing to
+// draw) or -2 (take the slow path).
+template <int BLOCK, int DT, bool XB>
+__device__ int fast_finish(const DrawRows& R, int nch, double* A, const double* Bv,
+                           const int* unc_n, const int* unc_idx, const double* sq_part,
+                           const double* sp_part, int nparts, double u,
+                           DrawShared<BLOCK>& sh) {
+  const int tid = threadIdx.x, wv = tid / kWave;
+  double Sq = 0.0, Sp = 0.0;
+  for (int i = 0; i < nparts; ++i) {
+    Sq = Sq + ld<XB>(&sq_part[i]);
+    Sp = Sp + ld<XB>(&sp_part[i]);
+  }
+  double iq = 1.0, ip = 1.0;
+  if (R.mode == kModeResidual) {
+    iq = 1.0 / Sq;
+    ip = 1.0 / Sp;
+    bool ok = true;
+    const double ratio = (Sq / Sp) / (R.sq_t / R.sp_t);
+    if (!(fabs(ratio - 1.0) <= kDelta / 4)) ok = false;
+    for (int c = tid; c < nch && ok; c += BLOCK)
+      if (ld<XB>(&unc_n[c]) > kUncMax) ok = false;
+    if (tid == 0) sh.sel[3] = 0;
+    __syncthreads();
+    if (!ok) sh.sel[3] = 1;
+    __syncthreads();
+    const bool slow = sh.sel[3] != 0;
+    __syncthreads();
+    if (slow) return -2;
+    for (int c = tid; c < nch; c += BLOCK) {
+      double W = ld<XB>(&A[c]) * iq - ld<XB>(&Bv[c]) * ip;
+      W = W > 0.0 ? W : 0.0;
+      const int nu = ld<XB>(&unc_n[c]);
+      for (int j = 0; j < nu; ++j) {
+        const int64_t x = ld<XB>(&unc_idx[c * kUncMax + j]);
+        const double eq = tok_exp(logit_f32<DT>(R.qrow, x), R.yscale, R.mq, sh.tab);
+        const double ep = tok_exp(logit_f32<DT>(R.prow, x), R.yscale, R.mp, sh.tab);
+        const double d = eq * iq - ep * ip;
+        W = W + (d > 0.0 ? d : 0.0);
+      }
+      A[c] = W;
+    }
+    __syncthreads();
+  } else if (XB) {
+    // bonus: the chunk sums come from other workgroups; copy them to this
+    // workgroup's plain view before the prefix reads them
+    for (int c = tid; c < nch; c += BLOCK) A[c] = ld<XB>(&A[c]);
+    __syncthreads();
+  }
+  if (wv == 0) locate_chunk(A, nch, u, sh.sel, sh.seld);
+  __syncthreads();
+  if (R.mode == kModeResidual && !(sh.seld[2] > 0.0)) {
+    __syncthreads();
+    return -2;  // residual without mass: the slow path falls back to q
+  }
+  int tok = -1;
+  if (sh.sel[0] >= 0 && wv == 0)
+    tok = draw_in_chunk<DT>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0], sh.seld[1], iq, ip, sh.tab);
+  if (tid == 0) sh.sel[2] = tok;
+  __syncthreads();
+  tok = sh.sel[2];
+  __syncthreads();
+  return tok;
+}
+
+// One workgroup per sequence (the spec_residual_sample path).  Dynamic LDS:
+// the fast layout (A, Bv: nch doubles each; unc_n: nch ints; unc_idx:
+// nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow path.
 template <int BLOCK, int DT>
 __global__ __launch_bounds__(BLOCK) void residual_kernel(
     const void* __restrict__ tgt, const void* __restrict__ dft,
     const float* __restrict__ uni, const float* __restrict__ tstats,
     const float* __restrict__ dstats, const int32_t* __restrict__ nacc, int K, int V,
-    double invT, int32_t* __restrict__ out_tokens, int32_t* __restrict__ num_emitted) {
-  constexpr int EB = Elt<DT>::bytes;
-  constexpr int E = 16 / EB;
-  constexpr int CH = kWave * E;
+    double yscale, int fast, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ num_emitted) {
+  constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int NW = BLOCK / kWave;
-  extern __shared__ double chunk_tot[];  // [nch]
-  __shared__ double tab[64];
-  __shared__ double red[NW];
-  __shared__ int s_sel[2];
-  __shared__ double s_sel_d[2];
-
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
   const int64_t b = blockIdx.x;
   const int64_t K1 = K + 1;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
   const int n = nacc[b];
   if (n < 0 || n > K) {
     if (tid == 0 && num_emitted) num_emitted[b] = 0;
     return;
   }
-  const bool resid = n < K;
-  const int64_t rq = b * K1 + n, rp = b * K + n;
-  const float mqf = tstats[2 * rq], sqf = tstats[2 * rq + 1];
-  float mpf = 0.f, spf = 1.f;
-  if (resid) {
-    mpf = dstats[2 * rp];
-    spf = dstats[2 * rp + 1];
-  }
-  if (!row_ok(mqf, sqf) || !row_ok(mpf, spf)) {
+  DrawRows R;
+  const int64_t rq = b * K1 + n, rp = b * K + (n < K ? n : 0);
+  if (!make_draw_rows<DT>(b, n, K, V, tgt, dft, tstats[2 * rq], tstats[2 * rq + 1],
+                          dstats[2 * rp], dstats[2 * rp + 1], yscale, R)) {
     if (tid == 0) {
       out_tokens[b * K1 + n] = -1;
       if (num_emitted) num_emitted[b] = 0;
     }
     return;
   }
-  const void* qrow = static_cast<const char*>(tgt) + rq * static_cast<int64_t>(V) * EB;
-  const void* prow = static_cast<const char*>(dft) + rp * static_cast<int64_t>(V) * EB;
-  const double mq = mqf, mp = mpf;
-  const double yscale = invT * Exp64::kScale;
-  fill_exp2_table(tab);
+  fill_exp2_table(sh.tab);
   __syncthreads();
-
-  // Pass A: fp64 normalisers of both rows (residual only).
-  double iq = 1.0, ip = 1.0;
-  int mode = kModeBonus;
-  if (resid) {
-    double aq = 0.0, ap = 0.0;
-    for (int64_t x = tid; x < V; x += BLOCK) {
-      aq = aq + exp64_scaled((static_cast<double>(logit_f32<DT>(qrow, x)) - mq) * yscale, tab);
-      ap = ap + exp64_scaled((static_cast<double>(logit_f32<DT>(prow, x)) - mp) * yscale, tab);
-    }
-    const double Sq = block_sum<BLOCK>(aq, red);
-    const double Sp = block_sum<BLOCK>(ap, red);
-    iq = 1.0 / Sq;
-    ip = 1.0 / Sp;
-    mode = kModeResidual;
-  }
-  const int nch = (V + CH - 1) / CH;
+  const int nch = (V + kWave * E - 1) / (kWave * E);
   const double u = uni[b * K1 + K];
-
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    // Pass B: chunk totals.
-    for (int c = wv; c < nch; c += NW) {
-      double w[E];
-      lane_weights<DT, E>(qrow, prow, V, c, lane, mode, mq, mp, yscale, iq, ip, tab, w);
-      double ls = 0.0;
+  int tok = -2;
+  if (fast) {
+    double* A = dyn;
+    double* Bv = A + nch;
+    int* unc_n = reinterpret_cast<int*>(Bv + nch);
+    int* unc_idx = unc_n + nch;
+    double lsq = 0.0, lsp = 0.0;
+    wave_sweep<DT>(R, wv, nch, NW, sh.tab, lsq, lsp, [&](int c, const ChunkSums& cs) {
+      if (lane == 0) {
+        A[c] = cs.A;
+        Bv[c] = cs.Bv;
+        unc_n[c] = cs.n_unc;
 #pragma unroll
-      for (int e = 0; e < E; ++e) ls = ls + w[e];
-      const double incl = wave_incl_scan(ls);
-      if (lane == kWave - 1) chunk_tot[c] = incl;
-    }
-    __syncthreads();
-
-    // Pass C (wave 0): running prefix over chunks, pick the crossing chunk.
-    if (wv == 0) {
-      const int per = (nch + kWave - 1) / kWave;
-      const int c0 = lane * per;
-      const int c1 = min(nch, c0 + per);
-      double lt = 0.0;
-      for (int c = c0; c < c1; ++c) lt = lt + chunk_tot[c];
-      const double li = wave_incl_scan(lt);
-      double run = __shfl_up(li, 1, kWave);
-      if (lane == 0) run = 0.0;
-      // total = running value after the last chunk (held by the lane owning it)
-      const int last_lane = (nch - 1) / per;
-      double run_end = run;
-      for (int c = c0; c < c1; ++c) run_end = run_end + chunk_tot[c];
-      const double S_w = __shfl(run_end, last_lane, kWave);
-      if (attempt == 0 && mode == kModeResidual && !(S_w > 0.0)) {
-        if (lane == 0) s_sel[0] = -2;  // residual has no mass: fall back to q
-      } else {
-        const double target = u * S_w;
-        int hit = -1, lastpos = -1;
-        double hit_excl = 0.0, lastpos_excl = 0.0;
-        double r = run;
-        for (int c = c0; c < c1; ++c) {
-          const double tc = chunk_tot[c];
-          const double nr = r + tc;
-          if (tc > 0.0) {
-            if (hit < 0 && nr > target) {
-              hit = c;
-              hit_excl = r;
-            }
-            lastpos = c;
-            lastpos_excl = r;
-          }
-          r = nr;
-        }
-        const unsigned long long hm = __ballot(hit >= 0);
-        const unsigned long long pm = __ballot(lastpos >= 0);
-        int sel = -3;  // -3: no token carries positive weight (only with bad stats)
-        double sel_excl = 0.0;
-        if (hm) {
-          const int src = __ffsll(static_cast<long long>(hm)) - 1;
-          sel = __shfl(hit, src, kWave);
-          sel_excl = __shfl(hit_excl, src, kWave);
-        } else if (pm) {
-          const int src = 63 - __clzll(static_cast<long long>(pm));
-          sel = __shfl(lastpos, src, kWave);
-          sel_excl = __shfl(lastpos_excl, src, kWave);
-        }
-        if (lane == 0) {
-          s_sel[0] = sel;
-          s_sel[1] = hm ? 1 : 0;
-          s_sel_d[0] = sel_excl;
-          s_sel_d[1] = target;
-        }
+        for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
       }
-    }
+    });
+    const double Sq = block_sum<BLOCK>(lsq, sh.red);
+    const double Sp = block_sum<BLOCK>(lsp, sh.red);
+    tok = fast_finish<BLOCK, DT, false>(R, nch, A, Bv, unc_n, unc_idx, &Sq, &Sp, 1, u, sh);
+  }
+  if (tok == -2) tok = slow_draw<BLOCK, DT>(R, nch, dyn, u, sh);
+  if (tid == 0) {
+    out_tokens[b * K1 + n] = tok;
+    if (num_emitted) num_emitted[b] = tok >= 0 ? n + 1 : 0;
+  }
+}
+
+// ==================================================================== fused
+//
+// One persistent launch for the whole verify.  Work items, handed out in a
+// fixed order by a device-wide counter:
+//   ROW(b, r)    stats of row r of sequence b (the 2K+1 target and draft rows)
+//   SCAN(b)      accept scan of sequence b, once all its rows have stats
+//   SLICE(b, s)  fast-path sweep of chunks [s*CPS, (s+1)*CPS) at position n_b
+// Item order: group g holds ROW(g, *), then SCAN(g - D1), then
+// SLICE(g - D2, *) (D2 > D1), so a sequence's scan and slices are normally
+// ready to run when they are taken, and residual sweeps (fp64 VALU work) run
+// on the same CUs as later rows' streaming (HBM work).  The workgroup that
+// finishes the last SLICE of a sequence draws its final token.
+//
+// Hand-offs (see device_common.hpp): a ROW publishes {m, s} as one 64-bit
+// word in the workspace whose non-zero value is also its ready flag (s is
+// never +0 and NaN is canonical); SCAN polls its sequence's words, clears
+// them, runs the scan and publishes {n, stats at n} then a ready word; SLICE
+// polls that word; slices count themselves on a per-sequence counter whose
+// last increment elects the finisher, which clears the counters.  Every poll
+// waits on items already taken by running workgroups that never wait on
+// later items, so the launch always drains; a poll that exceeds kSpinLimit
+// sets ctl[2] and gives up (not expected; that sequence then has no token).
+//
+// Workspace (zero before the first launch; each completed launch leaves it
+// zero again except the error word ctl[2]):
+//   ctl[0] item counter, ctl[1] exit counter, ctl[2] error word
+//   stat_word[B*(2K+1)]   (target rows b*(K+1)+t, then draft rows)
+//   ready[B], rec[B][8] = {n, mq, sq, mp, sp}, slices_done[B]
+//   sq_part[B][S], sp_part[B][S], A[B][nch], Bv[B][nch], unc_n[B][nch],
+//   unc_idx[B][nch][kUncMax]
+
+struct FusedArgs {
+  const void* tgt;
+  const void* dft;
+  const int32_t* tokens;
+  const float* uni;
+  float* tstats;
+  float* dstats;
+  int32_t* num_accepted;
+  int32_t* out_tokens;
+  float* probs;
+  int32_t* num_emitted;
+  unsigned* ctl;
+  unsigned long long* stat_word;
+  unsigned* ready;
+  int* rec;
+  unsigned* slices_done;
+  double* sq_part;
+  double* sp_part;
+  double* A;
+  double* Bv;
+  int* unc_n;
+  int* unc_idx;
+  int B, K, V;
+  int S;    // slices per sequence
+  int CPW;  // chunks per wave in a slice
+  int nch;  // chunks per row
+  int D1, D2;
+  int nseg;          // item-order segments
+  int seg_g0[8];     // first group of each segment
+  int seg_size[8];   // items per group in each segment
+  unsigned seg_item0[8];  // first item of each segment
+  unsigned total_items;
+  float c2;
+  double invT, yscale;
+};
+
+constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int kFusedMaxRows = 2 * 64 + 1;
+
+template <int BLOCK>
+struct FusedShared {
+  DrawShared<BLOCK> d;
+  float scan_stats[kFusedMaxRows][2];
+  unsigned item, flag;
+};
+
+__device__ __forceinline__ unsigned long long pack_stats(float m, float s) {
+  if (__builtin_isnan(s)) s = __builtin_nanf("");
+  return static_cast<unsigned long long>(__float_as_uint(m)) |
+         (static_cast<unsigned long long>(__float_as_uint(s)) << 32);
+}
+
+// At most 128 VGPRs, so that four 256-thread workgroups share a CU and a
+// row's streaming and another item's fp64 sweep overlap on it.
+template <int BLOCK, int DT, int VPG>
+__global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a) {
+  constexpr int NW = BLOCK / kWave;
+  __shared__ FusedShared<BLOCK> sh;
+  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
+  const int K = a.K, V = a.V;
+  const int64_t K1 = K + 1;
+  const int rows_per = 2 * K + 1;
+  fill_exp2_table(sh.d.tab);
+  unsigned next_item = 0;
+  if (tid == 0) next_item = atomic_add_dev(&a.ctl[0], 1u);
+
+  for (;;) {
     __syncthreads();
-    if (s_sel[0] == -2) {
-      mode = kModeBonus;  // weights e_q on the same row
-      __syncthreads();
+    if (tid == 0) sh.item = next_item;
+    __syncthreads();
+    const unsigned item = sh.item;
+    if (item >= a.total_items) break;
+    if (tid == 0) next_item = atomic_add_dev(&a.ctl[0], 1u);  // used next iteration
+
+    // decode: segment, group, offset within the group
+    int seg = 0;
+    while (seg + 1 < a.nseg && item >= a.seg_item0[seg + 1]) ++seg;
+    const unsigned rel = item - a.seg_item0[seg];
+    const int g = a.seg_g0[seg] + static_cast<int>(rel / a.seg_size[seg]);
+    int off = static_cast<int>(rel % a.seg_size[seg]);
+    const int nrow = g < a.B ? rows_per : 0;
+    const bool has_scan = g >= a.D1 && g - a.D1 < a.B;
+
+    if (off < nrow) {
+      // ---------------------------------------------------------------- ROW
+      const int b = g, r = off;
+      const char* row;
+      float* out;
+      int64_t widx;
+      if (r < K1) {
+        const int64_t rr = static_cast<int64_t>(b) * K1 + r;
+        row = static_cast<const char*>(a.tgt) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
+        out = a.tstats + 2 * rr;
+        widx = static_cast<int64_t>(b) * rows_per + r;
+      } else {
+        const int64_t rr = static_cast<int64_t>(b) * K + (r - K1);
+        row = static_cast<const char*>(a.dft) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
+        out = a.dstats + 2 * rr;
+        widx = static_cast<int64_t>(b) * rows_per + r;
+      }
+      float m, s;
+      row_stats<BLOCK, DT, VPG>(row, V, a.c2, sh.d.redf, sh.d.red, m, s);
+      if (tid == 0) {
+        out[0] = m;
+        out[1] = s;
+        __hip_atomic_store(&a.stat_word[widx], pack_stats(m, s), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
       continue;
     }
-    break;
-  }
+    off -= nrow;
 
-  // Nothing to draw from (every weight 0 or NaN; only reachable with stats
-  // that do not belong to these rows): report no token.
-  if (s_sel[0] < 0) {
-    if (tid == 0) {
-      out_tokens[b * K1 + n] = -1;
-      if (num_emitted) num_emitted[b] = 0;
-    }
-    return;
-  }
-
-  // Pass D (wave 0): re-derive the chosen chunk and find the token.
-  if (wv == 0) {
-    const int c = s_sel[0];
-    const bool crossing = s_sel[1] != 0;
-    const double excl = s_sel_d[0];
-    const double target = s_sel_d[1];
-    double w[E];
-    lane_weights<DT, E>(qrow, prow, V, c, lane, mode, mq, mp, yscale, iq, ip, tab, w);
-    double ls = 0.0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) ls = ls + w[e];
-    const double incl = wave_incl_scan(ls);
-    double lexcl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) lexcl = 0.0;
-    const bool lane_hit = crossing && ls > 0.0 && (excl + incl) > target;
-    const unsigned long long hm = __ballot(lane_hit);
-    const unsigned long long pm = __ballot(ls > 0.0);
-    const int src = hm ? (__ffsll(static_cast<long long>(hm)) - 1)
-                       : (pm ? 63 - __clzll(static_cast<long long>(pm)) : -1);
-    if (src < 0 && lane == 0) {
-      out_tokens[b * K1 + n] = -1;
-      if (num_emitted) num_emitted[b] = 0;
-    }
-    if (lane == src) {
-      const double base = excl + lexcl;
-      int pick = -1, lastpos = -1;
-      double a = 0.0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        a = a + w[e];
-        if (w[e] > 0.0) {
-          if (pick < 0 && hm && (base + a) > target) pick = e;
-          lastpos = e;
+    if (has_scan && off == 0) {
+      // --------------------------------------------------------------- SCAN
+      const int b = g - a.D1;
+      if (wv == 0) {
+        unsigned long long* words = a.stat_word + static_cast<int64_t>(b) * rows_per;
+        bool ok = true;
+        for (int r0 = 0; r0 < rows_per; r0 += kWave) {
+          const int r = r0 + lane;
+          unsigned long long w = 0;
+          unsigned spins = 0;
+          for (;;) {
+            if (r < rows_per)
+              w = __hip_atomic_load(&words[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool all = __all(r >= rows_per || w != 0ull);
+            if (all || spins >= kSpinLimit) break;
+            __builtin_amdgcn_s_sleep(2);
+            ++spins;
+          }
+          ok = ok && spins < kSpinLimit;
+          if (r < rows_per) {
+            sh.scan_stats[r][0] = __uint_as_float(static_cast<unsigned>(w));
+            sh.scan_stats[r][1] = __uint_as_float(static_cast<unsigned>(w >> 32));
+            __hip_atomic_store(&words[r], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        if (!ok) {
+          if (lane == 0) atomic_store_dev(&a.ctl[2], 1u);
+          for (int r = lane; r < rows_per; r += kWave) sh.scan_stats[r][1] = __builtin_nanf("");
+        }
+        // target rows are scan_stats[0..K], draft rows scan_stats[K+1..2K]
+        const int n = verify_seq<DT, false>(b, a.tgt, a.dft, a.tokens, a.uni,
+                                            &sh.scan_stats[0][0], &sh.scan_stats[K1][0], K, V,
+                                            a.invT, a.num_accepted, a.out_tokens, a.probs, true);
+        if (lane == 0) {
+          int* rc = a.rec + 8 * static_cast<int64_t>(b);
+          st<true>(&rc[0], n);
+          if (n >= 0) {
+            st<true>(reinterpret_cast<float*>(&rc[1]), sh.scan_stats[n][0]);
+            st<true>(reinterpret_cast<float*>(&rc[2]), sh.scan_stats[n][1]);
+            if (n < K) {
+              st<true>(reinterpret_cast<float*>(&rc[3]), sh.scan_stats[K1 + n][0]);
+              st<true>(reinterpret_cast<float*>(&rc[4]), sh.scan_stats[K1 + n][1]);
+            }
+          }
+          store_complete();
+          atomic_store_dev(&a.ready[b], 1u);
         }
       }
-      if (pick < 0) pick = lastpos;
-      const int64_t x = static_cast<int64_t>(c) * CH + static_cast<int64_t>(lane) * E + pick;
-      out_tokens[b * K1 + n] = static_cast<int32_t>(x);
-      if (num_emitted) num_emitted[b] = n + 1;
+      continue;
+    }
+    if (has_scan) off -= 1;
+
+    // ---------------------------------------------------------------- SLICE
+    const int b = g - a.D2, sl = off;
+    if (tid == 0) {
+      unsigned spins = 0;
+      while (atomic_load_dev(&a.ready[b]) == 0u && spins < kSpinLimit) {
+        __builtin_amdgcn_s_sleep(2);
+        ++spins;
+      }
+      sh.flag = spins < kSpinLimit ? 1u : 0u;
+      if (!sh.flag) atomic_store_dev(&a.ctl[2], 1u);
+    }
+    __syncthreads();
+    const bool ready = sh.flag != 0;
+    const int* rc = a.rec + 8 * static_cast<int64_t>(b);
+    const int n = ready ? ld<true>(&rc[0]) : -1;
+    DrawRows R;
+    bool rows_valid = false;
+    if (n >= 0 && n <= K) {
+      const float mq = ld<true>(reinterpret_cast<const float*>(&rc[1]));
+      const float sq = ld<true>(reinterpret_cast<const float*>(&rc[2]));
+      const float mp = n < K ? ld<true>(reinterpret_cast<const float*>(&rc[3])) : 0.f;
+      const float sp = n < K ? ld<true>(reinterpret_cast<const float*>(&rc[4])) : 1.f;
+      rows_valid = make_draw_rows<DT>(b, n, K, V, a.tgt, a.dft, mq, sq, mp, sp, a.yscale, R);
+    }
+    const int64_t base = static_cast<int64_t>(b) * a.nch;
+    if (rows_valid) {
+      double lsq = 0.0, lsp = 0.0;
+      const int cps = NW * a.CPW;
+      const int c0 = sl * cps + wv;
+      const int c1 = min(a.nch, (sl + 1) * cps);
+      wave_sweep<DT>(R, c0, c1, NW, sh.d.tab, lsq, lsp, [&](int c, const ChunkSums& cs) {
+        if (lane == 0) {
+          st<true>(&a.A[base + c], cs.A);
+          st<true>(&a.Bv[base + c], cs.Bv);
+          st<true>(&a.unc_n[base + c], cs.n_unc);
+#pragma unroll
+          for (int j = 0; j < kUncMax; ++j) st<true>(&a.unc_idx[(base + c) * kUncMax + j], cs.unc[j]);
+        }
+      });
+      const double Sq = block_sum<BLOCK>(lsq, sh.d.red);
+      const double Sp = block_sum<BLOCK>(lsp, sh.d.red);
+      if (tid == 0) {
+        st<true>(&a.sq_part[static_cast<int64_t>(b) * a.S + sl], Sq);
+        st<true>(&a.sp_part[static_cast<int64_t>(b) * a.S + sl], Sp);
+      }
+    }
+    store_complete();
+    __syncthreads();
+    if (tid == 0) sh.flag = atomic_add_dev(&a.slices_done[b], 1u);
+    __syncthreads();
+    if (sh.flag != static_cast<unsigned>(a.S - 1)) continue;
+
+    // ------------------------------------------- last slice of b: final draw
+    int tok = -1;
+    if (rows_valid) {
+      const double u = a.uni[static_cast<int64_t>(b) * K1 + K];
+      tok = fast_finish<BLOCK, DT, true>(R, a.nch, a.A + base, a.Bv + base, a.unc_n + base,
+                                         a.unc_idx + base * kUncMax,
+                                         a.sq_part + static_cast<int64_t>(b) * a.S,
+                                         a.sp_part + static_cast<int64_t>(b) * a.S, a.S, u,
+                                         sh.d);
+      if (tok == -2) tok = slow_draw<BLOCK, DT>(R, a.nch, a.A + base, u, sh.d);
+    }
+    if (tid == 0) {
+      if (n >= 0 && n <= K) a.out_tokens[static_cast<int64_t>(b) * K1 + n] = tok;
+      if (a.num_emitted) a.num_emitted[b] = (tok >= 0) ? n + 1 : 0;
+      atomic_store_dev(&a.slices_done[b], 0u);
+      atomic_store_dev(&a.ready[b], 0u);
+    }
+  }
+
+  // Last workgroup out resets the item counters for the next launch.
+  if (tid == 0) {
+    const unsigned done = atomic_add_dev(&a.ctl[1], 1u);
+    if (done == gridDim.x - 1) {
+      atomic_store_dev(&a.ctl[0], 0u);
+      atomic_store_dev(&a.ctl[1], 0u);
     }
   }
 }

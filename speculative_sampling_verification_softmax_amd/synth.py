@@ -70,8 +70,9 @@ WORKLOADS = {
 }
 
 
-def workload(name: str, **overrides) -> Workload:
-    return dataclasses.replace(WORKLOADS[name], **overrides)
+def workload(base: str, **overrides) -> Workload:
+    """A named workload with fields overridden (e.g. a smaller B, another V)."""
+    return dataclasses.replace(WORKLOADS[base], **overrides)
 
 
 def _generator(device, seed: int) -> torch.Generator:

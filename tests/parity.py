@@ -19,13 +19,31 @@ MAX_FLAGGED_FRACTION = 1e-4
 PROB_RTOL = 1e-5
 
 
-def gpu_verify(inp: dict, stream=None) -> dict:
+PATHS = ("three_call", "fused")
+
+
+def gpu_verify(inp: dict, stream=None, path: str = "three_call", workspace=None) -> dict:
+    """Run the HIP verify through the C ABI: the three calls, or the fused call
+    (with a fresh zeroed workspace unless one is given)."""
     import torch
     from speculative_sampling_verification_softmax_amd import binding
-    out = binding.verify_all(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
-                             inp["T"], stream=stream)
+    if path == "three_call":
+        out = binding.verify_all(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
+                                 inp["T"], stream=stream)
+    elif path == "fused":
+        B, K1, V = inp["target"].shape
+        if workspace is None:
+            workspace = binding.new_workspace(B, K1 - 1, V, inp["target"].dtype,
+                                              inp["target"].device)
+        out = binding.verify_fused(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
+                                   inp["T"], workspace, stream=stream)
+    else:
+        raise ValueError(path)
     torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in out.items()}
+    res = {k: v.cpu().numpy() for k, v in out.items()}
+    if path == "fused":
+        assert binding.workspace_error(workspace) == 0, "a wait inside the fused kernel gave up"
+    return res
 
 
 def oracle_verify(host: dict, seqs=None, nthreads: int = 0) -> dict:

@@ -108,3 +108,35 @@ def test_binding_fails_loudly_without_library(tmp_path):
             binding_mod.load(str(tmp_path / "missing.so"))
     finally:
         binding_mod._lib = saved
+
+
+def test_workspace_size_host_only():
+    L = _lib()
+    L.spec_verify_workspace_size.restype = ctypes.c_size_t
+    n = L.spec_verify_workspace_size(256, 8, 128256, 1)
+    assert 1 << 20 < n < 8 << 20 and n % 256 == 0
+    assert L.spec_verify_workspace_size(256, 8, 128256, 0) > n  # fp32 chunks are shorter
+    assert L.spec_verify_workspace_size(0, 8, 100, 1) == 0
+    assert L.spec_verify_workspace_size(1, 0, 100, 1) == 0
+    assert L.spec_verify_workspace_size(1, 1, 100, 7) == 0
+
+
+@pytest.mark.parametrize("case", ["null_ws", "small_ws", "misaligned_ws", "null_out", "bad_T"])
+def test_fused_rejects_bad_arguments(case):
+    L = _lib()
+    L.spec_verify_workspace_size.restype = ctypes.c_size_t
+    need = L.spec_verify_workspace_size(2, 3, 100, 1)
+    ws, nbytes, out, T = P * 256, need, P, 1.0
+    if case == "null_ws":
+        ws = None
+    elif case == "small_ws":
+        nbytes = need - 1
+    elif case == "misaligned_ws":
+        ws = P * 256 + 16
+    elif case == "null_out":
+        out = None
+    elif case == "bad_T":
+        T = -1.0
+    rc = L.spec_verify_fused(P, P, 1, P, P, 2, 3, 100, T, P, P, P, out, None, None, ws,
+                             ctypes.c_size_t(nbytes), None)
+    assert rc == 1

@@ -29,12 +29,12 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_case(wl, seed, B=None, seqs=None, label=""):
+def run_case(wl, seed, B=None, seqs=None, label="", path="three_call"):
     say(f"[case] {label or wl if isinstance(wl, str) else wl.name} seed={seed} B={B} -> generate")
     inp = synth.make_inputs(wl, seed=seed, device="cuda", B=B)
     w = inp["workload"]
-    say(f"[case] {w.name} B={w.B} K={w.K} V={w.V} {w.dtype} T={w.T} -> gpu verify")
-    g = parity.gpu_verify(inp)
+    say(f"[case] {w.name} B={w.B} K={w.K} V={w.V} {w.dtype} T={w.T} -> gpu verify ({path})")
+    g = parity.gpu_verify(inp, path=path)
     if seqs is not None:
         idx = torch.as_tensor(seqs, device="cuda")
         sub = dict(target=inp["target"][idx], draft=inp["draft"][idx], tokens=inp["tokens"][idx],
@@ -45,44 +45,49 @@ def run_case(wl, seed, B=None, seqs=None, label=""):
         host = synth.to_host_arrays(inp)
         o = parity.oracle_verify(host)
     rep = parity.compare(g, o, w.T, seqs=None if seqs is None else np.asarray(seqs))
-    say(f"[case] {w.name} seed={seed}: seqs={rep['sequences']} draws={rep['draws']} "
+    say(f"[case] {w.name} seed={seed} {path}: seqs={rep['sequences']} draws={rep['draws']} "
         f"flagged={len(rep['flagged'])} failures={len(rep['failures'])} "
         f"stats_rel={rep['stats_max_rel']:.2e} probs_rel={rep['probs_max_rel']:.2e} "
         f"accept_hist={rep['accept_hist']}")
     return rep
 
 
+@pytest.mark.parametrize("path", parity.PATHS)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_tiny_many_sequences(seed):
-    parity.assert_parity(run_case("tiny", seed, B=4096), "tiny")
+def test_tiny_many_sequences(seed, path):
+    parity.assert_parity(run_case("tiny", seed, B=4096, path=path), "tiny")
 
 
-def test_batch1_latency_shape():
+@pytest.mark.parametrize("path", parity.PATHS)
+def test_batch1_latency_shape(path):
     total_draws, flagged = 0, 0
     for seed in range(8):
-        rep = run_case("batch1", seed)
+        rep = run_case("batch1", seed, path=path)
         assert rep["failures"] == [], rep["failures"]
         total_draws += rep["draws"]
         flagged += len(rep["flagged"])
     assert flagged <= max(1, parity.MAX_FLAGGED_FRACTION * total_draws)
 
 
+@pytest.mark.parametrize("path", parity.PATHS)
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_small_batch(seed):
-    parity.assert_parity(run_case("small", seed), "small")
+def test_small_batch(seed, path):
+    parity.assert_parity(run_case("small", seed, path=path), "small")
 
 
+@pytest.mark.parametrize("path", parity.PATHS)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_headline_all_sequences(seed):
-    rep = run_case("headline", seed)
+def test_headline_all_sequences(seed, path):
+    rep = run_case("headline", seed, path=path)
     parity.assert_parity(rep, "headline")
     assert rep["sequences"] == 256
 
 
-def test_large_sampled_sequences():
+@pytest.mark.parametrize("path", parity.PATHS)
+def test_large_sampled_sequences(path):
     rng = np.random.default_rng(0)
     seqs = np.sort(rng.choice(1024, size=48, replace=False))
-    rep = run_case("large", 0, seqs=seqs)
+    rep = run_case("large", 0, seqs=seqs, path=path)
     parity.assert_parity(rep, "large")
 
 
@@ -94,10 +99,11 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("path", parity.PATHS)
 @pytest.mark.parametrize("V,K,dtype,B", RAGGED)
-def test_ragged_shapes(V, K, dtype, B):
+def test_ragged_shapes(V, K, dtype, B, path):
     wl = synth.workload("batch1", V=V, K=K, dtype=dtype, B=B, T=0.7, name=f"ragged{V}")
-    rep = run_case(wl, seed=V + K)
+    rep = run_case(wl, seed=V + K, path=path)
     parity.assert_parity(rep, f"V={V} K={K} {dtype}")
 
 
@@ -110,3 +116,46 @@ def test_repeatable_and_stream_independent():
         b = parity.gpu_verify(inp, stream=s)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_fused_equals_three_call_and_reuses_workspace():
+    """The fused call draws the same tokens as the three calls, and leaves
+    its workspace's counters at zero so the next call can reuse it."""
+    from speculative_sampling_verification_softmax_amd import binding
+    inp = synth.make_inputs("headline", seed=11, device="cuda")
+    torch.cuda.synchronize()
+    a = parity.gpu_verify(inp, path="three_call")
+    ws = binding.new_workspace(256, 8, 128256, torch.bfloat16, "cuda")
+    for rep in range(3):
+        b = parity.gpu_verify(inp, path="fused", workspace=ws)
+        for k in ("num_accepted", "out_tokens", "num_emitted"):
+            np.testing.assert_array_equal(a[k], b[k], err_msg=f"{k} call {rep}")
+        for k in ("target_stats", "draft_stats", "probs"):
+            np.testing.assert_allclose(a[k], b[k], rtol=1e-5, atol=0, err_msg=f"{k} call {rep}")
+        if rep == 0:
+            first = b
+        else:
+            for k in first:
+                np.testing.assert_array_equal(first[k], b[k], err_msg=f"fused repeat {k}")
+        # control words, ready words, stat words and counters are back to zero:
+        # ctl (256 B), stat words (8 B per row), ready (4 B per sequence),
+        # records (32 B per sequence), slice counters (4 B per sequence)
+        r256 = lambda x: (x + 255) // 256 * 256
+        ctl = 256
+        words = r256(8 * 256 * 17)
+        ready = r256(4 * 256)
+        recs = r256(32 * 256)
+        dump = ws.view(torch.int32).cpu().numpy()
+        assert np.all(dump[: (ctl + words + ready) // 4] == 0)
+        sdone = (ctl + words + ready + recs) // 4
+        assert np.all(dump[sdone: sdone + 256] == 0)
+
+
+def test_fused_smaller_batch_after_larger_on_same_workspace():
+    from speculative_sampling_verification_softmax_amd import binding
+    ws = binding.new_workspace(64, 4, 32000, torch.bfloat16, "cuda")
+    for B in (64, 5, 1):
+        inp = synth.make_inputs("small", seed=B, device="cuda", B=B)
+        g = parity.gpu_verify(inp, path="fused", workspace=ws)
+        o = parity.oracle_verify(synth.to_host_arrays(inp))
+        parity.assert_parity(parity.compare(g, o, inp["T"]), f"fused B={B}")
