@@ -86,7 +86,20 @@ def main() -> int:
                          "spec_verify, spec_residual_sample")
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times "
+                         "(a known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes three times")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the verify shards by sequence and needs "
