@@ -5,9 +5,9 @@
 
 One step = the whole verify of one batch: row statistics of every target and
 draft row, the accept scan and the residual or bonus draw, inputs resident in
-HBM.  --path fused (default) runs it as one spec_verify_fused launch;
---path three_call as spec_softmax_stats, spec_verify, spec_residual_sample back
-to back on one stream.  W untimed steps, then K timed steps bracketed by device
+HBM.  --path three_call (default, the faster path on MI355X) runs it as
+spec_softmax_stats, spec_verify, spec_residual_sample back to back on one
+stream; --path fused as one spec_verify_fused launch.  W untimed steps, then K timed steps bracketed by device
 synchronisation.  Prints one JSON line on stdout; progress goes to stderr.
 
 Reported:
@@ -81,7 +81,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--path", default="fused", choices=["fused", "three_call"],
+    ap.add_argument("--path", default="three_call", choices=["three_call", "fused"],
                     help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
                          "spec_verify, spec_residual_sample")
     ap.add_argument("--cpu-seqs", type=int, default=256,

@@ -154,12 +154,16 @@ size_t spec_verify_workspace_size(int B, int K, int V, int dtype);
  *   probs, num_emitted   optional outputs as above (NULL to skip)
  *   workspace      device memory of at least spec_verify_workspace_size(...)
  *                  bytes, 256-byte aligned, owned by the caller.  It must be
- *                  all zero before its first use; every completed call leaves
- *                  it zero again, so it can be reused call after call.  Two
- *                  calls that are in flight at the same time need two
+ *                  all zero before its first use; every completed call puts
+ *                  its counters and flags back to zero, so it can be reused
+ *                  call after call by any call with B and K no larger than
+ *                  those of the calls before it (a larger B or K needs a
+ *                  zeroed workspace).
+ *                  Two calls that are in flight at the same time need two
  *                  workspaces.  A non-zero third 32-bit word after a call
- *                  means a wait inside the kernel gave up (never expected);
- *                  the workspace must then be cleared.
+ *                  means a bounded wait inside the kernel gave up (never
+ *                  expected; the sequence concerned then has no final token)
+ *                  and the workspace must be cleared before it is used again.
  * Returns SPEC_OK, SPEC_ERR_INVALID_ARG (also for a workspace that is too
  * small or misaligned) or SPEC_ERR_LAUNCH.
  */

@@ -74,6 +74,15 @@ __device__ __forceinline__ bool row_ok(float m, float s) {
 // ---------------------------------------------------------------- wave64 ops
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// A value known to be the same in every lane (read from LDS or from one
+// address), moved to a scalar register so that the compiler treats it, and
+// everything derived from it, as uniform.
+__device__ __forceinline__ unsigned uniform(unsigned v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
@@ -134,14 +143,18 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 // with 2^(j/256) from a 256-entry table (tab, filled by fill_exp2_table) and
 // 2^(r/256) = exp(r ln2/256) by its degree-3 Taylor polynomial
 // (|r ln2/256| <= 0.00136, truncation error <= 1.5e-13).  Callers pass y, the
-// argument already multiplied by 256/ln2.  Results below ~2^-1062 flush to 0.
+// argument already multiplied by 256/ln2.
 struct Exp64 {
   static constexpr int kTab = 256;
   static constexpr double kLn2 = 0.693147180559945309417232121458176568;
   static constexpr double kScale = 256.0 / kLn2;
   static constexpr double c1 = kLn2 / 256.0;
-  static constexpr double c2 = c1 * c1 / 2.0;
-  static constexpr double c3 = c1 * c1 * c1 / 6.0;
+  // Adding 1.5*2^52 rounds a double of magnitude below 2^51 to an integer k
+  // (to nearest, ties to even) and leaves k in the low 32 bits of the sum.
+  static constexpr double kRound = 6755399441055744.0;
+  // y is clamped here: 2^(-300000/256) = 2^-1172 underflows to exactly 0, so
+  // -inf (and NaN, which fmax drops) give 0 without a select.
+  static constexpr double kFloor = -300000.0;
 };
 
 __device__ __forceinline__ void fill_exp2_table(double* tab) {
@@ -149,18 +162,16 @@ __device__ __forceinline__ void fill_exp2_table(double* tab) {
     tab[j] = exp2(static_cast<double>(j) / Exp64::kTab);
 }
 
-// Branch-free: y below the range (or -inf, NaN) evaluates a clamped argument
-// and selects 0.
 __device__ __forceinline__ double exp64_scaled(double y, const double* tab) {
-  const double yc = fmax(y, -272000.0);
-  const double k = rint(yc);
-  const double r = yc - k;
-  const int ki = static_cast<int>(k);
-  double p = fma(r, Exp64::c3, Exp64::c2);
-  p = fma(r, p, Exp64::c1);
-  p = fma(r, p, 1.0);
-  const double v = ldexp(tab[ki & 255] * p, ki >> 8);
-  return (y > -272000.0) ? v : 0.0;
+  const double yc = fmax(y, Exp64::kFloor);
+  const double kb = yc + Exp64::kRound;
+  const int ki = __double2loint(kb);
+  const double x = (yc - (kb - Exp64::kRound)) * Exp64::c1;  // r ln2/256
+  // 1 + x + x^2/2 + x^3/6; only the 1/6 is not an inline constant
+  double p = fma(x, 1.0 / 6.0, 0.5);
+  p = fma(x, p, 1.0);
+  p = fma(x, p, 1.0);
+  return ldexp(tab[ki & 255] * p, ki >> 8);
 }
 
 // ------------------------------------------------- cross-workgroup handoff
@@ -183,6 +194,47 @@ __device__ __forceinline__ unsigned atomic_load_dev(const unsigned* p) {
 __device__ __forceinline__ void atomic_store_dev(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Reads of an array written by other workgroups of the same launch, as
+// buffer loads with the sc1 bit: unlike the atomic loads above they carry no
+// ordering, so the compiler issues a thread's loads together.  `base` must be
+// uniform across the wave (it goes into a scalar buffer resource) and the
+// array no longer than 2^31 bytes.  Src<false, T> is the plain-pointer view
+// with the same interface.
+constexpr int kBufWord3Dev = 0x00020000;  // untyped dword access (gfx9 family)
+constexpr int kAuxSc1 = 16;               // cache-policy bit sc1
+
+template <bool XB, typename T>
+struct Src;
+
+template <typename T>
+struct Src<false, T> {
+  const T* p;
+  __device__ __forceinline__ Src(const T* base, int64_t) : p(base) {}
+  __device__ __forceinline__ T operator[](int64_t i) const { return p[i]; }
+};
+
+template <typename T>
+struct Src<true, T> {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte elements");
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Src(const T* base, int64_t n)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0),
+                                            static_cast<int>(n * static_cast<int64_t>(sizeof(T))),
+                                            kBufWord3Dev)) {}
+  __device__ __forceinline__ T operator[](int64_t i) const {
+    const int off = static_cast<int>(i * static_cast<int64_t>(sizeof(T)));
+    if constexpr (sizeof(T) == 4) {
+      const unsigned w = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kAuxSc1);
+      return __builtin_bit_cast(T, w);
+    } else {
+      const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAuxSc1);
+      const unsigned long long v =
+          static_cast<unsigned long long>(w[0]) | (static_cast<unsigned long long>(w[1]) << 32);
+      return __builtin_bit_cast(T, v);
+    }
+  }
+};
 
 // Wait until this wave's outstanding memory operations have completed.
 __device__ __forceinline__ void store_complete() {

@@ -22,26 +22,74 @@ namespace spec {
 //
 // HBM-bound streaming reduction of one row.  The row is split into an
 // unaligned head, a body of 16-byte vectors (8 bf16 or 4 fp32 per load, fully
-// coalesced across the wave) and a tail.  Each thread keeps a running max m
-// and sum s: a group of VPG vectors is loaded, its max taken, the group's
-// terms exp2((x - m) * log2(e)/T) summed in fp32 (x - m is exact for bf16
-// inputs; only the product by the constant rounds), and the group sum added
-// to s, carried in fp64 and rescaled only when the max grows.  Thread partials
-// are brought to the row max and summed in fp64.  Relative error of s: a few
-// 1e-7.
+// coalesced across the wave) and a tail.  Each thread takes groups of VPG
+// vectors; the next group's loads are issued before the current group is
+// reduced.
+//
+// Per thread the sum is kept against an integer shift k = rint(max * c2)
+// (c2 = log2(e)/T): every term is exp2(fma(x, c2, -k)), one fused multiply-add
+// (x*c2 is exact inside it, one rounding) and one exp2, and when the max grows
+// the running fp64 sum is rescaled by an exact power of two.  The group's
+// terms are summed in fp32, the running sum in fp64.  At the end the thread
+// sums are brought to the row's shift k_r by exact powers of two, summed in
+// fp64 and multiplied by 2^(k_r - m*c2) (|k_r - m*c2| <= 1/2, m*c2 exact in
+// fp64), giving s = sum exp2((x - m) * c2).  Relative error of s: a few 1e-7.
+//
+// Rows whose max has |m*c2| >= 2^22 (logits beyond ~2.9e6*T) cannot use an
+// fp32 integer shift; their s comes from a second pass that takes the
+// difference x - m first (row_stats_wide).
+
+constexpr float kShiftMax = 4194304.f;  // 2^22
 
 struct RowAcc {
+  float m = -__builtin_huge_valf();  // max of the values seen
+  float k = -kShiftMax;              // integer shift, rint(m*c2) clamped to +-2^22
+  double s = 0.0;                    // sum of exp2(x*c2 - k)
+};
+
+template <int N>
+__device__ __forceinline__ float group_max(const float (&x)[N]) {
+  float g = x[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) g = fmaxf(g, x[i]);
+  return g;
+}
+
+// Sum of exp2(fma(x, c2, -k)) over the group, pairwise.
+template <int N>
+__device__ __forceinline__ float group_exp_sum(const float (&x)[N], float c2, float k) {
+  float t[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) t[i] = __builtin_amdgcn_exp2f(fmaf(x[i], c2, -k));
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int i = 0; i + w < N; i += 2 * w) t[i] = t[i] + t[i + w];
+  return t[0];
+}
+
+template <int N>
+__device__ __forceinline__ void fold(RowAcc& a, const float (&x)[N], float c2) {
+  const float mn = fmaxf(a.m, group_max(x));
+  // -inf (nothing finite seen) and very negative maxima clamp to -2^22: the
+  // terms are then 0 or negligible against any row whose max is in range.
+  const float kn = rintf(__builtin_amdgcn_fmed3f(mn * c2, -kShiftMax, kShiftMax));
+  const float gs = group_exp_sum(x, c2, kn);
+  a.s = ldexp(a.s, static_cast<int>(a.k - kn)) + static_cast<double>(gs);
+  a.m = mn;
+  a.k = kn;
+}
+
+// The old-style accumulator for rows with huge logits: terms exp2((x - m)*c2)
+// with the difference taken first, the running sum rescaled when m grows.
+struct WideAcc {
   float m = -__builtin_huge_valf();
   double s = 0.0;
 };
 
 template <int N>
-__device__ __forceinline__ void fold(RowAcc& a, const float (&x)[N], float c2) {
-  float g = x[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) g = fmaxf(g, x[i]);
-  const float mn = fmaxf(a.m, g);
-  // While every value seen is -inf the shift is 0 and all terms are exp2(-inf)=0.
+__device__ __forceinline__ void fold_wide(WideAcc& a, const float (&x)[N], float c2) {
+  const float mn = fmaxf(a.m, group_max(x));
   const float ms = (mn == -__builtin_huge_valf()) ? 0.f : mn;
   float gs = 0.f;
 #pragma unroll
@@ -51,60 +99,147 @@ __device__ __forceinline__ void fold(RowAcc& a, const float (&x)[N], float c2) {
   a.m = mn;
 }
 
+// Geometry of one row: head elements before the first 16-byte boundary, nvec
+// whole vectors, then the tail.
+template <int DT>
+struct RowGeom {
+  int head, nvec, tail0;
+  __device__ __forceinline__ RowGeom(const char* row, int V) {
+    constexpr int EB = Elt<DT>::bytes;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+    head = static_cast<int>(((16 - (addr & 15)) & 15) / EB);
+    if (head > V) head = V;
+    nvec = (V - head) / (16 / EB);
+    tail0 = head + nvec * (16 / EB);
+  }
+};
+
+// Second pass for rows with |m*c2| >= 2^22 (block-uniform; rare).
+template <int BLOCK, int DT>
+__device__ __noinline__ double row_stats_wide(const char* row, int V, float c2, float m,
+                                              float* red_f, double* red_d) {
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+  const int tid = threadIdx.x;
+  const RowGeom<DT> G(row, V);
+  WideAcc acc;
+  for (int i = tid; i < G.head; i += BLOCK) {
+    float x[1] = {logit_f32<DT>(row, i)};
+    fold_wide(acc, x, c2);
+  }
+  for (int i = G.tail0 + tid; i < V; i += BLOCK) {
+    float x[1] = {logit_f32<DT>(row, i)};
+    fold_wide(acc, x, c2);
+  }
+  const uint4* vp = reinterpret_cast<const uint4*>(row + static_cast<int64_t>(G.head) *
+                                                             Elt<DT>::bytes);
+  for (int i = tid; i < G.nvec; i += BLOCK) {
+    float x[EPV];
+    unpack16<DT>(vp[i], x);
+    fold_wide(acc, x, c2);
+  }
+  const float scale = (acc.m == m) ? 1.f : __builtin_amdgcn_exp2f((acc.m - m) * c2);
+  return block_sum<BLOCK>(acc.s * static_cast<double>(scale), red_d);
+}
+
+// VPG vectors of a row body at vector indices i0 + u*BLOCK, u < VPG, as fp32.
+// The body is addressed through a buffer resource: the per-thread offset is
+// a fixed VGPR and the group offset a scalar, so the loads cost no vector
+// address arithmetic.
+template <int BLOCK, int DT, int VPG>
+__device__ __forceinline__ void body_load(__amdgpu_buffer_rsrc_t rs, int vo, int i0,
+                                          uint4 (&v)[VPG]) {
+#pragma unroll
+  for (int u = 0; u < VPG; ++u) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (i0 + u * BLOCK) * 16, 0);
+    v[u] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <int DT, int VPG>
+__device__ __forceinline__ void body_unpack(const uint4 (&v)[VPG],
+                                            float (&x)[VPG * (16 / Elt<DT>::bytes)]) {
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+#pragma unroll
+  for (int u = 0; u < VPG; ++u) {
+    float xu[EPV];
+    unpack16<DT>(v[u], xu);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
+  }
+}
+
+// Word 3 of a raw buffer resource on gfx9-family parts (untyped dword access).
+constexpr int kBufWord3 = 0x00020000;
+
 // {m, s} of one row, returned to every thread of the block.  A row with no
-// finite maximum gets s = NaN (NaN logits already make s NaN).
+// finite maximum gets s = NaN (NaN logits already make s NaN).  `row` must be
+// uniform across the block.
 template <int BLOCK, int DT, int VPG>
 __device__ __forceinline__ void row_stats(const char* row, int V, float c2, float* red_f,
                                           double* red_d, float& m_out, float& s_out) {
-  constexpr int EB = Elt<DT>::bytes;
-  constexpr int EPV = 16 / EB;
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+  constexpr int STEP = BLOCK * VPG;
   const int tid = threadIdx.x;
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-  int head = static_cast<int>(((16 - (addr & 15)) & 15) / EB);
-  if (head > V) head = V;
-  const int nvec = (V - head) / EPV;
-  const int tail0 = head + nvec * EPV;
+  const RowGeom<DT> G(row, V);
 
   RowAcc acc;
-  if (tid < head) {
+  if (tid < G.head) {
     float x[1] = {logit_f32<DT>(row, tid)};
     fold(acc, x, c2);
   }
-  if (tid < V - tail0) {
-    float x[1] = {logit_f32<DT>(row, tail0 + tid)};
+  if (tid < V - G.tail0) {
+    float x[1] = {logit_f32<DT>(row, G.tail0 + tid)};
     fold(acc, x, c2);
   }
-  const uint4* vp = reinterpret_cast<const uint4*>(row + static_cast<int64_t>(head) * EB);
-  constexpr int STEP = BLOCK * VPG;
-  const int nfull = nvec / STEP;
-  for (int it = 0; it < nfull; ++it) {
-    const int i0 = it * STEP + tid;
+  const char* body = row + static_cast<int64_t>(G.head) * Elt<DT>::bytes;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(body), static_cast<short>(0), G.nvec * 16, kBufWord3);
+  const int vo = tid * 16;
+  const int nfull = G.nvec / STEP;
+  if (nfull > 0) {
     uint4 v[VPG];
-#pragma unroll
-    for (int u = 0; u < VPG; ++u) v[u] = vp[i0 + u * BLOCK];
+    body_load<BLOCK, DT, VPG>(rs, vo, 0, v);
+    for (int it = 1; it < nfull; ++it) {
+      float x[VPG * EPV];
+      body_unpack<DT, VPG>(v, x);
+      body_load<BLOCK, DT, VPG>(rs, vo, it * STEP, v);  // next group in flight
+      fold(acc, x, c2);
+    }
+    float x[VPG * EPV];
+    body_unpack<DT, VPG>(v, x);
+    fold(acc, x, c2);
+  }
+  if (nfull * STEP < G.nvec) {  // one partial group: vectors past nvec read as -inf
+    const int i0 = nfull * STEP + tid;
     float x[VPG * EPV];
 #pragma unroll
     for (int u = 0; u < VPG; ++u) {
       float xu[EPV];
-      unpack16<DT>(v[u], xu);
+      if (i0 + u * BLOCK < G.nvec) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (nfull * STEP + u * BLOCK) * 16, 0);
+        unpack16<DT>(make_uint4(w[0], w[1], w[2], w[3]), xu);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xu[e] = -__builtin_huge_valf();
+      }
 #pragma unroll
       for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
     }
     fold(acc, x, c2);
   }
-  for (int i = nfull * STEP + tid; i < nvec; i += BLOCK) {
-    const uint4 v = vp[i];
-    float x[EPV];
-    unpack16<DT>(v, x);
-    fold(acc, x, c2);
-  }
+
   const float m = block_max<BLOCK>(acc.m, red_f);
-  const float ms = (m == -__builtin_huge_valf()) ? 0.f : m;
-  const float scale = (acc.m == m) ? 1.f : __builtin_amdgcn_exp2f((acc.m - ms) * c2);
-  const double part = acc.s * static_cast<double>(scale);
-  const double s = block_sum<BLOCK>(part, red_d);
-  float sf = static_cast<float>(s);
-  if (!__builtin_isfinite(m)) sf = __builtin_nanf("");
+  float sf;
+  if (!__builtin_isfinite(m)) {
+    sf = __builtin_nanf("");
+  } else if (fabsf(m * c2) < kShiftMax) {
+    const float kr = rintf(m * c2);
+    const double s = block_sum<BLOCK>(ldexp(acc.s, static_cast<int>(acc.k - kr)), red_d);
+    const double t = static_cast<double>(kr) - static_cast<double>(m) * static_cast<double>(c2);
+    sf = static_cast<float>(s * exp2(t));
+  } else {
+    sf = static_cast<float>(row_stats_wide<BLOCK, DT>(row, V, c2, m, red_f, red_d));
+  }
   m_out = m;
   s_out = sf;
 }
@@ -291,19 +426,19 @@ __device__ __forceinline__ bool chunk_full(const DrawRows& R, int c) {
 }
 
 // Issue the loads of a full chunk (both rows together).
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ void chunk_issue(const DrawRows& R, int c, RawChunk& raw) {
   constexpr int E = 16 / Elt<DT>::bytes;
   const int64_t x0 = static_cast<int64_t>(c) * (kWave * E) + static_cast<int64_t>(lane_id()) * E;
   const int64_t off = x0 * Elt<DT>::bytes;
   raw.q = *reinterpret_cast<const uint4*>(static_cast<const char*>(R.qrow) + off);
-  if (R.mode == kModeResidual)
+  if (MODE == kModeResidual)
     raw.p = *reinterpret_cast<const uint4*>(static_cast<const char*>(R.prow) + off);
 }
 
 // The lane's E values of both rows: from the issued loads for a full chunk,
 // element by element (-inf past V) otherwise.
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ void chunk_values(const DrawRows& R, int c, bool full,
                                              const RawChunk& raw,
                                              float (&zq)[16 / Elt<DT>::bytes],
@@ -311,30 +446,30 @@ __device__ __forceinline__ void chunk_values(const DrawRows& R, int c, bool full
   constexpr int E = 16 / Elt<DT>::bytes;
   if (full) {
     unpack16<DT>(raw.q, zq);
-    if (R.mode == kModeResidual) unpack16<DT>(raw.p, zp);
+    if (MODE == kModeResidual) unpack16<DT>(raw.p, zp);
   } else {
     const int64_t x0 =
         static_cast<int64_t>(c) * (kWave * E) + static_cast<int64_t>(lane_id()) * E;
     load_group<DT>(R.qrow, x0, R.V, false, zq);
-    if (R.mode == kModeResidual) load_group<DT>(R.prow, x0, R.V, false, zp);
+    if (MODE == kModeResidual) load_group<DT>(R.prow, x0, R.V, false, zp);
   }
 }
 
 // Exact weights of this lane's E tokens (used to re-derive the chosen chunk).
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq, double ip,
                                              const double* tab,
                                              double (&w)[16 / Elt<DT>::bytes]) {
   constexpr int E = 16 / Elt<DT>::bytes;
   RawChunk raw;
   const bool full = chunk_full<DT>(R, c);
-  if (full) chunk_issue<DT>(R, c, raw);
+  if (full) chunk_issue<DT, MODE>(R, c, raw);
   float zq[E], zp[E];
-  chunk_values<DT>(R, c, full, raw, zq, zp);
+  chunk_values<DT, MODE>(R, c, full, raw, zq, zp);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
-    if (R.mode == kModeResidual) {
+    if (MODE == kModeResidual) {
       const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
       const double d = eq * iq - ep * ip;
       w[e] = d > 0.0 ? d : 0.0;
@@ -353,7 +488,7 @@ struct ChunkSums {
 
 // Fast-path arithmetic of one chunk from its values.  Adds every token's e_q,
 // e_p to the lane's lsq, lsp.
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
                                            const float (&zq)[16 / Elt<DT>::bytes],
                                            const float (&zp)[16 / Elt<DT>::bytes],
@@ -366,27 +501,27 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
   for (int e = 0; e < E; ++e) {
     const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
     lsq = lsq + eq;
-    if (R.mode == kModeResidual) {
+    if (MODE == kModeResidual) {
       const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
       lsp = lsp + ep;
       const double r = ep * R.sq_t;
       const double d = fma(eq, R.sp_t, -r);  // e_q s~_p - e_p s~_q
       const bool certain = fabs(d) > r * kDelta || eq == 0.0;
-      if (certain && d > 0.0) {
-        a = a + eq;
-        bb = bb + ep;
-      }
+      // 1.0 or 0.0 (high word only): clearly positive tokens add e_q and e_p
+      const double take = __hiloint2double((certain && d > 0.0) ? 0x3ff00000 : 0, 0);
+      a = fma(take, eq, a);
+      bb = fma(take, ep, bb);
       if (!certain) unc_bits |= 1u << e;
     } else {
       a = a + eq;
     }
   }
   out.A = wave_sum(a);
-  out.Bv = wave_sum(bb);
+  out.Bv = MODE == kModeResidual ? wave_sum(bb) : 0.0;
   out.n_unc = 0;
 #pragma unroll
   for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
-  if (R.mode == kModeResidual) {
+  if (MODE == kModeResidual) {
     const int x0 = c * (kWave * E) + lane_id() * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -404,28 +539,37 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
   }
 }
 
-// One wave sweeps chunks c0, c0+stride, ... < c1, loading each next chunk
-// while computing the current one; emit(c, sums) stores a chunk's results.
-template <int DT, typename Emit>
+// One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
+// flight (a slot is refilled as soon as its chunk has been unpacked);
+// emit(c, sums) stores a chunk's results.
+template <int DT, int MODE, int PF, typename Emit>
 __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, int stride,
                                            const double* tab, double& lsq, double& lsp,
                                            Emit emit) {
   constexpr int E = 16 / Elt<DT>::bytes;
-  if (c0 >= c1) return;
-  RawChunk cur, nxt;
-  bool cur_full = chunk_full<DT>(R, c0);
-  if (cur_full) chunk_issue<DT>(R, c0, cur);
-  for (int c = c0; c < c1; c += stride) {
-    const int cn = c + stride;
-    const bool nxt_full = cn < c1 && chunk_full<DT>(R, cn);
-    if (nxt_full) chunk_issue<DT>(R, cn, nxt);
-    float zq[E], zp[E];
-    chunk_values<DT>(R, c, cur_full, cur, zq, zp);
-    ChunkSums cs;
-    chunk_sums<DT>(R, c, zq, zp, tab, lsq, lsp, cs);
-    emit(c, cs);
-    cur = nxt;
-    cur_full = nxt_full;
+  RawChunk buf[PF];
+  bool full[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int c = c0 + j * stride;
+    full[j] = c < c1 && chunk_full<DT>(R, c);
+    if (full[j]) chunk_issue<DT, MODE>(R, c, buf[j]);
+  }
+  for (int base = c0; base < c1; base += PF * stride) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int c = base + j * stride;
+      if (c < c1) {
+        float zq[E], zp[E];
+        chunk_values<DT, MODE>(R, c, full[j], buf[j], zq, zp);
+        const int cn = c + PF * stride;
+        full[j] = cn < c1 && chunk_full<DT>(R, cn);
+        if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
+        ChunkSums cs;
+        chunk_sums<DT, MODE>(R, c, zq, zp, tab, lsq, lsp, cs);
+        emit(c, cs);
+      }
+    }
   }
 }
 
@@ -488,14 +632,14 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
 }
 
 // Token inside chunk c (wave 0): returns the token id in every lane, or -1.
-template <int DT>
+template <int DT, int MODE>
 __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool crossing, double excl,
                                              double target, double iq, double ip,
                                              const double* tab) {
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
   double w[E];
-  lane_weights<DT>(R, c, iq, ip, tab, w);
+  lane_weights<DT, MODE>(R, c, iq, ip, tab, w);
   double ls = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ls = ls + w[e];
@@ -550,9 +694,9 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
     for (int c = wv; c < nch; c += NW) {
       RawChunk raw;
       const bool full = chunk_full<DT>(R, c);
-      if (full) chunk_issue<DT>(R, c, raw);
+      if (full) chunk_issue<DT, kModeResidual>(R, c, raw);
       float zq[E], zp[E];
-      chunk_values<DT>(R, c, full, raw, zq, zp);
+      chunk_values<DT, kModeResidual>(R, c, full, raw, zq, zp);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         aq = aq + tok_exp(zq[e], R.yscale, R.mq, sh.tab);
@@ -567,7 +711,10 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
   for (int attempt = 0; attempt < 2; ++attempt) {
     for (int c = wv; c < nch; c += NW) {
       double w[E];
-      lane_weights<DT>(R, c, iq, ip, sh.tab, w);
+      if (R.mode == kModeResidual)
+        lane_weights<DT, kModeResidual>(R, c, iq, ip, sh.tab, w);
+      else
+        lane_weights<DT, kModeBonus>(R, c, iq, ip, sh.tab, w);
       double ls = 0.0;
 #pragma unroll
       for (int e = 0; e < E; ++e) ls = ls + w[e];
@@ -587,7 +734,11 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
   }
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
-    tok = draw_in_chunk<DT>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0], sh.seld[1], iq, ip, sh.tab);
+    tok = R.mode == kModeResidual
+              ? draw_in_chunk<DT, kModeResidual>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                 sh.seld[1], iq, ip, sh.tab)
+              : draw_in_chunk<DT, kModeBonus>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                              sh.seld[1], iq, ip, sh.tab);
   if (tid == 0) sh.sel[2] = tok;
   __syncthreads();
   tok = sh.sel[2];
@@ -595,30 +746,43 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
   return tok;
 }
 
-// Fast-path finish (whole block) from the sweep's results: chunk sums A, Bv,
-// uncertain lists, normaliser parts (XB: written by other workgroups).
-// Overwrites A with the chunk totals W_c.  Returns the token, -1 (nothing to
-// draw) or -2 (take the slow path).
+// Fast-path finish (whole block) from a sweep's results: the exact
+// normalisers Sq, Sp and, per chunk, the sums A, Bv and the uncertain lists
+// (XB: written by other workgroups of this launch).  W (nch doubles of this
+// workgroup's own memory; it may be A itself when XB is false) receives the
+// chunk totals W_c.  Returns the token, -1 (nothing to draw) or -2 (take the
+// slow path).
 template <int BLOCK, int DT, bool XB>
-__device__ int fast_finish(const DrawRows& R, int nch, double* A, const double* Bv,
-                           const int* unc_n, const int* unc_idx, const double* sq_part,
-                           const double* sp_part, int nparts, double u,
-                           DrawShared<BLOCK>& sh) {
+__device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
+                           Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
+                           double* W, double u, DrawShared<BLOCK>& sh) {
   const int tid = threadIdx.x, wv = tid / kWave;
-  double Sq = 0.0, Sp = 0.0;
-  for (int i = 0; i < nparts; ++i) {
-    Sq = Sq + ld<XB>(&sq_part[i]);
-    Sp = Sp + ld<XB>(&sp_part[i]);
-  }
   double iq = 1.0, ip = 1.0;
   if (R.mode == kModeResidual) {
     iq = 1.0 / Sq;
     ip = 1.0 / Sp;
-    bool ok = true;
     const double ratio = (Sq / Sp) / (R.sq_t / R.sp_t);
-    if (!(fabs(ratio - 1.0) <= kDelta / 4)) ok = false;
-    for (int c = tid; c < nch && ok; c += BLOCK)
-      if (ld<XB>(&unc_n[c]) > kUncMax) ok = false;
+    bool ok = fabs(ratio - 1.0) <= kDelta / 4;
+    for (int c = tid; c < nch; c += BLOCK) {
+      const double a = A[c], bv = Bv[c];
+      const int nu = unc_n[c];
+      int x[kUncMax];
+#pragma unroll
+      for (int j = 0; j < kUncMax; ++j) x[j] = unc_idx[static_cast<int64_t>(c) * kUncMax + j];
+      double w = a * iq - bv * ip;
+      w = w > 0.0 ? w : 0.0;
+      if (nu > kUncMax) ok = false;
+#pragma unroll
+      for (int j = 0; j < kUncMax; ++j) {
+        if (j < nu) {
+          const double eq = tok_exp(logit_f32<DT>(R.qrow, x[j]), R.yscale, R.mq, sh.tab);
+          const double ep = tok_exp(logit_f32<DT>(R.prow, x[j]), R.yscale, R.mp, sh.tab);
+          const double d = eq * iq - ep * ip;
+          w = w + (d > 0.0 ? d : 0.0);
+        }
+      }
+      W[c] = w;
+    }
     if (tid == 0) sh.sel[3] = 0;
     __syncthreads();
     if (!ok) sh.sel[3] = 1;
@@ -626,27 +790,11 @@ __device__ int fast_finish(const DrawRows& R, int nch, double* A, const double* 
     const bool slow = sh.sel[3] != 0;
     __syncthreads();
     if (slow) return -2;
-    for (int c = tid; c < nch; c += BLOCK) {
-      double W = ld<XB>(&A[c]) * iq - ld<XB>(&Bv[c]) * ip;
-      W = W > 0.0 ? W : 0.0;
-      const int nu = ld<XB>(&unc_n[c]);
-      for (int j = 0; j < nu; ++j) {
-        const int64_t x = ld<XB>(&unc_idx[c * kUncMax + j]);
-        const double eq = tok_exp(logit_f32<DT>(R.qrow, x), R.yscale, R.mq, sh.tab);
-        const double ep = tok_exp(logit_f32<DT>(R.prow, x), R.yscale, R.mp, sh.tab);
-        const double d = eq * iq - ep * ip;
-        W = W + (d > 0.0 ? d : 0.0);
-      }
-      A[c] = W;
-    }
-    __syncthreads();
-  } else if (XB) {
-    // bonus: the chunk sums come from other workgroups; copy them to this
-    // workgroup's plain view before the prefix reads them
-    for (int c = tid; c < nch; c += BLOCK) A[c] = ld<XB>(&A[c]);
+  } else {
+    for (int c = tid; c < nch; c += BLOCK) W[c] = A[c];
     __syncthreads();
   }
-  if (wv == 0) locate_chunk(A, nch, u, sh.sel, sh.seld);
+  if (wv == 0) locate_chunk(W, nch, u, sh.sel, sh.seld);
   __syncthreads();
   if (R.mode == kModeResidual && !(sh.seld[2] > 0.0)) {
     __syncthreads();
@@ -654,7 +802,11 @@ __device__ int fast_finish(const DrawRows& R, int nch, double* A, const double* 
   }
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
-    tok = draw_in_chunk<DT>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0], sh.seld[1], iq, ip, sh.tab);
+    tok = R.mode == kModeResidual
+              ? draw_in_chunk<DT, kModeResidual>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                 sh.seld[1], iq, ip, sh.tab)
+              : draw_in_chunk<DT, kModeBonus>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                              sh.seld[1], iq, ip, sh.tab);
   if (tid == 0) sh.sel[2] = tok;
   __syncthreads();
   tok = sh.sel[2];
@@ -705,7 +857,7 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
     int* unc_n = reinterpret_cast<int*>(Bv + nch);
     int* unc_idx = unc_n + nch;
     double lsq = 0.0, lsp = 0.0;
-    wave_sweep<DT>(R, wv, nch, NW, sh.tab, lsq, lsp, [&](int c, const ChunkSums& cs) {
+    auto emit = [&](int c, const ChunkSums& cs) {
       if (lane == 0) {
         A[c] = cs.A;
         Bv[c] = cs.Bv;
@@ -713,10 +865,16 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
 #pragma unroll
         for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
       }
-    });
+    };
+    if (R.mode == kModeResidual)
+      wave_sweep<DT, kModeResidual, 2>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+    else
+      wave_sweep<DT, kModeBonus, 2>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     const double Sq = block_sum<BLOCK>(lsq, sh.red);
     const double Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false>(R, nch, A, Bv, unc_n, unc_idx, &Sq, &Sp, 1, u, sh);
+    tok = fast_finish<BLOCK, DT, false>(
+        R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
+        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
   }
   if (tok == -2) tok = slow_draw<BLOCK, DT>(R, nch, dyn, u, sh);
   if (tid == 0) {
@@ -738,23 +896,28 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
 // on the same CUs as later rows' streaming (HBM work).  The workgroup that
 // finishes the last SLICE of a sequence draws its final token.
 //
-// Hand-offs (see device_common.hpp): a ROW publishes {m, s} as one 64-bit
-// word in the workspace whose non-zero value is also its ready flag (s is
-// never +0 and NaN is canonical); SCAN polls its sequence's words, clears
-// them, runs the scan and publishes {n, stats at n} then a ready word; SLICE
-// polls that word; slices count themselves on a per-sequence counter whose
-// last increment elects the finisher, which clears the counters.  Every poll
-// waits on items already taken by running workgroups that never wait on
-// later items, so the launch always drains; a poll that exceeds kSpinLimit
-// sets ctl[2] and gives up (not expected; that sequence then has no token).
+// Hand-offs between workgroups (possibly on different XCDs) use the sc1
+// loads and stores of device_common.hpp.  A ROW publishes {m, s} as one
+// 64-bit atomic word whose non-zero value is also its ready flag (s is never
+// +0 and NaN is canonical), so a row needs no wait of its own; SCAN polls its
+// sequence's words, clears them, runs the scan and publishes {n, stats at n}
+// then a ready word; SLICE polls that word, and its stores complete before it
+// counts itself on a per-sequence counter whose last increment elects the
+// finisher, which clears the counters.  Every poll waits on items already
+// taken by running workgroups that never wait on later items, so the launch
+// always drains; a poll that exceeds kSpinLimit sets the error word and gives
+// up (not expected; that sequence then has no final token).
 //
-// Workspace (zero before the first launch; each completed launch leaves it
-// zero again except the error word ctl[2]):
-//   ctl[0] item counter, ctl[1] exit counter, ctl[2] error word
-//   stat_word[B*(2K+1)]   (target rows b*(K+1)+t, then draft rows)
-//   ready[B], rec[B][8] = {n, mq, sq, mp, sp}, slices_done[B]
-//   sq_part[B][S], sp_part[B][S], A[B][nch], Bv[B][nch], unc_n[B][nch],
-//   unc_idx[B][nch][kUncMax]
+// Workspace, flags first (zero before the first launch and again after each
+// completed launch, except the error word):
+//   ctl[kCtlItem] item counter, ctl[kCtlExit] exit counter, ctl[kCtlErr]
+//   error word; stat_word[B*(2K+1)] (target rows b*(K+1)+t, then draft
+//   rows); ready[B]; slices_done[B]
+// then data written before it is read within each launch:
+//   rec[B][8] = {n, mq, sq, mp, sp}, sq_part[B][S], sp_part[B][S],
+//   A[B][nch], Bv[B][nch], unc_n[B][nch], unc_idx[B][nch][kUncMax]
+
+enum : int { kCtlItem = 0, kCtlExit = 1, kCtlErr = 2, kCtlWords = 64 };
 
 struct FusedArgs {
   const void* tgt;
@@ -770,8 +933,8 @@ struct FusedArgs {
   unsigned* ctl;
   unsigned long long* stat_word;
   unsigned* ready;
-  int* rec;
   unsigned* slices_done;
+  int* rec;
   double* sq_part;
   double* sp_part;
   double* A;
@@ -780,12 +943,11 @@ struct FusedArgs {
   int* unc_idx;
   int B, K, V;
   int S;    // slices per sequence
-  int CPW;  // chunks per wave in a slice
   int nch;  // chunks per row
   int D1, D2;
-  int nseg;          // item-order segments
-  int seg_g0[8];     // first group of each segment
-  int seg_size[8];   // items per group in each segment
+  int nseg;               // item-order segments
+  int seg_g0[8];          // first group of each segment
+  int seg_size[8];        // items per group in each segment
   unsigned seg_item0[8];  // first item of each segment
   unsigned total_items;
   float c2;
@@ -794,11 +956,19 @@ struct FusedArgs {
 
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kFusedMaxRows = 2 * 64 + 1;
+// Chunks in one slice: kFusedCPW for each wave of the workgroup, all of
+// their loads issued when the slice starts.
+constexpr int kFusedCPW = 4;
 
 template <int BLOCK>
 struct FusedShared {
   DrawShared<BLOCK> d;
   float scan_stats[kFusedMaxRows][2];
+  // a slice's per-chunk results, written out together when the slice ends
+  // (on this architecture stores count against the same wait counter as
+  // loads, so stores issued chunk by chunk would hold up the next loads)
+  double sA[(BLOCK / kWave) * kFusedCPW], sB[(BLOCK / kWave) * kFusedCPW];
+  int sUn[(BLOCK / kWave) * kFusedCPW], sUi[(BLOCK / kWave) * kFusedCPW][kUncMax];
   unsigned item, flag;
 };
 
@@ -814,21 +984,22 @@ template <int BLOCK, int DT, int VPG>
 __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a) {
   constexpr int NW = BLOCK / kWave;
   __shared__ FusedShared<BLOCK> sh;
+  extern __shared__ double wbuf[];  // nch doubles: chunk totals of a final draw
   const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
   const int K = a.K, V = a.V;
   const int64_t K1 = K + 1;
   const int rows_per = 2 * K + 1;
   fill_exp2_table(sh.d.tab);
   unsigned next_item = 0;
-  if (tid == 0) next_item = atomic_add_dev(&a.ctl[0], 1u);
+  if (tid == 0) next_item = atomic_add_dev(&a.ctl[kCtlItem], 1u);
 
   for (;;) {
     __syncthreads();
     if (tid == 0) sh.item = next_item;
     __syncthreads();
-    const unsigned item = sh.item;
+    const unsigned item = uniform(sh.item);
     if (item >= a.total_items) break;
-    if (tid == 0) next_item = atomic_add_dev(&a.ctl[0], 1u);  // used next iteration
+    if (tid == 0) next_item = atomic_add_dev(&a.ctl[kCtlItem], 1u);  // used next iteration
 
     // decode: segment, group, offset within the group
     int seg = 0;
@@ -844,25 +1015,22 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
       const int b = g, r = off;
       const char* row;
       float* out;
-      int64_t widx;
       if (r < K1) {
         const int64_t rr = static_cast<int64_t>(b) * K1 + r;
         row = static_cast<const char*>(a.tgt) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
         out = a.tstats + 2 * rr;
-        widx = static_cast<int64_t>(b) * rows_per + r;
       } else {
         const int64_t rr = static_cast<int64_t>(b) * K + (r - K1);
         row = static_cast<const char*>(a.dft) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
         out = a.dstats + 2 * rr;
-        widx = static_cast<int64_t>(b) * rows_per + r;
       }
       float m, s;
       row_stats<BLOCK, DT, VPG>(row, V, a.c2, sh.d.redf, sh.d.red, m, s);
       if (tid == 0) {
         out[0] = m;
         out[1] = s;
-        __hip_atomic_store(&a.stat_word[widx], pack_stats(m, s), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.stat_word[static_cast<int64_t>(b) * rows_per + r], pack_stats(m, s),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       continue;
     }
@@ -894,7 +1062,7 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
           }
         }
         if (!ok) {
-          if (lane == 0) atomic_store_dev(&a.ctl[2], 1u);
+          if (lane == 0) atomic_store_dev(&a.ctl[kCtlErr], 1u);
           for (int r = lane; r < rows_per; r += kWave) sh.scan_stats[r][1] = __builtin_nanf("");
         }
         // target rows are scan_stats[0..K], draft rows scan_stats[K+1..2K]
@@ -907,10 +1075,8 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
           if (n >= 0) {
             st<true>(reinterpret_cast<float*>(&rc[1]), sh.scan_stats[n][0]);
             st<true>(reinterpret_cast<float*>(&rc[2]), sh.scan_stats[n][1]);
-            if (n < K) {
-              st<true>(reinterpret_cast<float*>(&rc[3]), sh.scan_stats[K1 + n][0]);
-              st<true>(reinterpret_cast<float*>(&rc[4]), sh.scan_stats[K1 + n][1]);
-            }
+            st<true>(reinterpret_cast<float*>(&rc[3]), n < K ? sh.scan_stats[K1 + n][0] : 0.f);
+            st<true>(reinterpret_cast<float*>(&rc[4]), n < K ? sh.scan_stats[K1 + n][1] : 1.f);
           }
           store_complete();
           atomic_store_dev(&a.ready[b], 1u);
@@ -929,38 +1095,50 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
         ++spins;
       }
       sh.flag = spins < kSpinLimit ? 1u : 0u;
-      if (!sh.flag) atomic_store_dev(&a.ctl[2], 1u);
+      if (!sh.flag) atomic_store_dev(&a.ctl[kCtlErr], 1u);
     }
     __syncthreads();
-    const bool ready = sh.flag != 0;
-    const int* rc = a.rec + 8 * static_cast<int64_t>(b);
-    const int n = ready ? ld<true>(&rc[0]) : -1;
+    const bool ready = uniform(sh.flag) != 0;
+    const Src<true, int> rc(a.rec + 8 * static_cast<int64_t>(b), 8);
+    const int n = ready ? uniform(rc[0]) : -1;
+    const float mq = uniform(__int_as_float(rc[1])), sq = uniform(__int_as_float(rc[2]));
+    const float mp = uniform(__int_as_float(rc[3])), sp = uniform(__int_as_float(rc[4]));
     DrawRows R;
     bool rows_valid = false;
-    if (n >= 0 && n <= K) {
-      const float mq = ld<true>(reinterpret_cast<const float*>(&rc[1]));
-      const float sq = ld<true>(reinterpret_cast<const float*>(&rc[2]));
-      const float mp = n < K ? ld<true>(reinterpret_cast<const float*>(&rc[3])) : 0.f;
-      const float sp = n < K ? ld<true>(reinterpret_cast<const float*>(&rc[4])) : 1.f;
-      rows_valid = make_draw_rows<DT>(b, n, K, V, a.tgt, a.dft, mq, sq, mp, sp, a.yscale, R);
-    }
+    if (n >= 0 && n <= K)
+      rows_valid = make_draw_rows<DT>(b, n, K, V, a.tgt, a.dft, mq, sq, n < K ? mp : 0.f,
+                                      n < K ? sp : 1.f, a.yscale, R);
     const int64_t base = static_cast<int64_t>(b) * a.nch;
     if (rows_valid) {
       double lsq = 0.0, lsp = 0.0;
-      const int cps = NW * a.CPW;
-      const int c0 = sl * cps + wv;
-      const int c1 = min(a.nch, (sl + 1) * cps);
-      wave_sweep<DT>(R, c0, c1, NW, sh.d.tab, lsq, lsp, [&](int c, const ChunkSums& cs) {
+      constexpr int cps = NW * kFusedCPW;
+      const int cb = sl * cps;  // first chunk of the slice
+      const int c0 = cb + wv;
+      const int c1 = min(a.nch, cb + cps);
+      auto emit = [&](int c, const ChunkSums& cs) {
         if (lane == 0) {
-          st<true>(&a.A[base + c], cs.A);
-          st<true>(&a.Bv[base + c], cs.Bv);
-          st<true>(&a.unc_n[base + c], cs.n_unc);
+          const int i = c - cb;
+          sh.sA[i] = cs.A;
+          sh.sB[i] = cs.Bv;
+          sh.sUn[i] = cs.n_unc;
 #pragma unroll
-          for (int j = 0; j < kUncMax; ++j) st<true>(&a.unc_idx[(base + c) * kUncMax + j], cs.unc[j]);
+          for (int j = 0; j < kUncMax; ++j) sh.sUi[i][j] = cs.unc[j];
         }
-      });
-      const double Sq = block_sum<BLOCK>(lsq, sh.d.red);
+      };
+      if (R.mode == kModeResidual)
+        wave_sweep<DT, kModeResidual, kFusedCPW>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+      else
+        wave_sweep<DT, kModeBonus, kFusedCPW>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+      const double Sq = block_sum<BLOCK>(lsq, sh.d.red);  // its barriers also order the LDS above
       const double Sp = block_sum<BLOCK>(lsp, sh.d.red);
+      if (tid < c1 - cb) {
+        const int64_t c = base + cb + tid;
+        st<true>(&a.A[c], sh.sA[tid]);
+        st<true>(&a.Bv[c], sh.sB[tid]);
+        st<true>(&a.unc_n[c], sh.sUn[tid]);
+#pragma unroll
+        for (int j = 0; j < kUncMax; ++j) st<true>(&a.unc_idx[c * kUncMax + j], sh.sUi[tid][j]);
+      }
       if (tid == 0) {
         st<true>(&a.sq_part[static_cast<int64_t>(b) * a.S + sl], Sq);
         st<true>(&a.sp_part[static_cast<int64_t>(b) * a.S + sl], Sp);
@@ -970,18 +1148,28 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
     __syncthreads();
     if (tid == 0) sh.flag = atomic_add_dev(&a.slices_done[b], 1u);
     __syncthreads();
-    if (sh.flag != static_cast<unsigned>(a.S - 1)) continue;
+    if (uniform(sh.flag) != static_cast<unsigned>(a.S - 1)) continue;
 
     // ------------------------------------------- last slice of b: final draw
     int tok = -1;
     if (rows_valid) {
       const double u = a.uni[static_cast<int64_t>(b) * K1 + K];
-      tok = fast_finish<BLOCK, DT, true>(R, a.nch, a.A + base, a.Bv + base, a.unc_n + base,
-                                         a.unc_idx + base * kUncMax,
-                                         a.sq_part + static_cast<int64_t>(b) * a.S,
-                                         a.sp_part + static_cast<int64_t>(b) * a.S, a.S, u,
-                                         sh.d);
-      if (tok == -2) tok = slow_draw<BLOCK, DT>(R, a.nch, a.A + base, u, sh.d);
+      // exact normalisers: the slices' parts, summed by the whole block
+      const Src<true, double> sqp(a.sq_part + static_cast<int64_t>(b) * a.S, a.S);
+      const Src<true, double> spp(a.sp_part + static_cast<int64_t>(b) * a.S, a.S);
+      double lq = 0.0, lp = 0.0;
+      for (int i = tid; i < a.S; i += BLOCK) {
+        lq = lq + sqp[i];
+        lp = lp + spp[i];
+      }
+      const double Sq = block_sum<BLOCK>(lq, sh.d.red);
+      const double Sp = block_sum<BLOCK>(lp, sh.d.red);
+      tok = fast_finish<BLOCK, DT, true>(
+          R, a.nch, Sq, Sp, Src<true, double>(a.A + base, a.nch),
+          Src<true, double>(a.Bv + base, a.nch), Src<true, int>(a.unc_n + base, a.nch),
+          Src<true, int>(a.unc_idx + base * kUncMax, static_cast<int64_t>(a.nch) * kUncMax), wbuf,
+          u, sh.d);
+      if (tok == -2) tok = slow_draw<BLOCK, DT>(R, a.nch, wbuf, u, sh.d);
     }
     if (tid == 0) {
       if (n >= 0 && n <= K) a.out_tokens[static_cast<int64_t>(b) * K1 + n] = tok;
@@ -993,10 +1181,10 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
 
   // Last workgroup out resets the item counters for the next launch.
   if (tid == 0) {
-    const unsigned done = atomic_add_dev(&a.ctl[1], 1u);
+    const unsigned done = atomic_add_dev(&a.ctl[kCtlExit], 1u);
     if (done == gridDim.x - 1) {
-      atomic_store_dev(&a.ctl[0], 0u);
-      atomic_store_dev(&a.ctl[1], 0u);
+      atomic_store_dev(&a.ctl[kCtlItem], 0u);
+      atomic_store_dev(&a.ctl[kCtlExit], 0u);
     }
   }
 }

@@ -34,7 +34,8 @@ constexpr int kStatsBlock = SPEC_STATS_BLOCK;
 constexpr int kResidBlock = 1024;
 constexpr int kFusedBlock = 256;
 constexpr int kFusedNW = kFusedBlock / spec::kWave;
-constexpr int kFusedCPW = 4;  // chunks per wave in one residual slice
+// Dynamic LDS of the fused kernel: one double per chunk of a row.
+constexpr size_t kFusedMaxDynLds = static_cast<size_t>(SPEC_MAX_V / 64 / 4) * sizeof(double);
 // LDS the one-workgroup residual kernel may take for its fast-path arrays.
 constexpr size_t kResidFastLds = 48 * 1024;
 
@@ -63,23 +64,26 @@ size_t round256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layout of spec_verify_fused (offsets in bytes from the base).
 struct FusedLayout {
-  size_t ctl, stat_word, ready, rec, slices_done, sq_part, sp_part, A, Bv, unc_n, unc_idx, total;
+  size_t ctl, stat_word, ready, slices_done, rec, sq_part, sp_part, A, Bv, unc_n, unc_idx, total;
   int nch, S;
 };
 
 FusedLayout fused_layout(int B, int K, int V, int dtype) {
   FusedLayout L{};
   L.nch = num_chunks(V, dtype);
-  const int cps = kFusedNW * kFusedCPW;
+  const int cps = kFusedNW * spec::kFusedCPW;
   L.S = (L.nch + cps - 1) / cps;
   const size_t b = static_cast<size_t>(B);
   const size_t rows = b * (2 * static_cast<size_t>(K) + 1);
   size_t off = 0;
-  L.ctl = off;         off = round256(off + 16 * sizeof(unsigned));
+  // flags first: zero after every completed call, and a later call with
+  // B' <= B and K' <= K finds all of its own flags inside that region
+  L.ctl = off;         off = round256(off + spec::kCtlWords * sizeof(unsigned));
   L.stat_word = off;   off = round256(off + rows * sizeof(unsigned long long));
   L.ready = off;       off = round256(off + b * sizeof(unsigned));
-  L.rec = off;         off = round256(off + b * 8 * sizeof(int));
   L.slices_done = off; off = round256(off + b * sizeof(unsigned));
+  // written before they are read within each call
+  L.rec = off;         off = round256(off + b * 8 * sizeof(int));
   L.sq_part = off;     off = round256(off + b * L.S * sizeof(double));
   L.sp_part = off;     off = round256(off + b * L.S * sizeof(double));
   L.A = off;           off = round256(off + b * L.nch * sizeof(double));
@@ -134,8 +138,10 @@ int fused_grid() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     constexpr int VPG = DT == kBF16 ? SPEC_FUSED_VPG_BF16 : SPEC_FUSED_VPG_F32;
+    // dynamic LDS: nch doubles; sized here for the largest row (SPEC_MAX_V fp32)
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, spec::fused_kernel<kFusedBlock, DT, VPG>, kFusedBlock, 0) != hipSuccess)
+            &per_cu, spec::fused_kernel<kFusedBlock, DT, VPG>, kFusedBlock,
+            kFusedMaxDynLds) != hipSuccess)
       return 0;
     g = cus * (per_cu > 0 ? per_cu : 1);
   }
@@ -286,8 +292,8 @@ int spec_verify_fused(const void* target_logits, const void* draft_logits, int d
   a.ctl = reinterpret_cast<unsigned*>(ws + L.ctl);
   a.stat_word = reinterpret_cast<unsigned long long*>(ws + L.stat_word);
   a.ready = reinterpret_cast<unsigned*>(ws + L.ready);
-  a.rec = reinterpret_cast<int*>(ws + L.rec);
   a.slices_done = reinterpret_cast<unsigned*>(ws + L.slices_done);
+  a.rec = reinterpret_cast<int*>(ws + L.rec);
   a.sq_part = reinterpret_cast<double*>(ws + L.sq_part);
   a.sp_part = reinterpret_cast<double*>(ws + L.sp_part);
   a.A = reinterpret_cast<double*>(ws + L.A);
@@ -298,7 +304,6 @@ int spec_verify_fused(const void* target_logits, const void* draft_logits, int d
   a.K = K;
   a.V = V;
   a.S = L.S;
-  a.CPW = kFusedCPW;
   a.nch = L.nch;
   // A sequence's scan follows its rows by about one grid's worth of rows, so
   // that the rows are done when the scan is taken; its slices follow the scan.
@@ -312,14 +317,15 @@ int spec_verify_fused(const void* target_logits, const void* draft_logits, int d
   a.c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
   a.invT = 1.0 / static_cast<double>(temperature);
   a.yscale = a.invT * spec::Exp64::kScale;
+  const size_t lds = static_cast<size_t>(L.nch) * sizeof(double);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (dtype == SPEC_DTYPE_BF16) {
     hipLaunchKernelGGL((spec::fused_kernel<kFusedBlock, kBF16, SPEC_FUSED_VPG_BF16>),
-                       dim3(grid), dim3(kFusedBlock), 0, s, a);
+                       dim3(grid), dim3(kFusedBlock), lds, s, a);
   } else {
     hipLaunchKernelGGL((spec::fused_kernel<kFusedBlock, kF32, SPEC_FUSED_VPG_F32>),
-                       dim3(grid), dim3(kFusedBlock), 0, s, a);
+                       dim3(grid), dim3(kFusedBlock), lds, s, a);
   }
   return launched();
 }

@@ -137,18 +137,13 @@ def test_fused_equals_three_call_and_reuses_workspace():
         else:
             for k in first:
                 np.testing.assert_array_equal(first[k], b[k], err_msg=f"fused repeat {k}")
-        # control words, ready words, stat words and counters are back to zero:
-        # ctl (256 B), stat words (8 B per row), ready (4 B per sequence),
-        # records (32 B per sequence), slice counters (4 B per sequence)
+        # the flags lead the workspace and are back to zero: control words
+        # (64), row stat words (8 B per row), ready words and slice counters
+        # (4 B per sequence each), each section on a 256-byte boundary
         r256 = lambda x: (x + 255) // 256 * 256
-        ctl = 256
-        words = r256(8 * 256 * 17)
-        ready = r256(4 * 256)
-        recs = r256(32 * 256)
+        flags = r256(64 * 4) + r256(8 * 256 * 17) + 2 * r256(4 * 256)
         dump = ws.view(torch.int32).cpu().numpy()
-        assert np.all(dump[: (ctl + words + ready) // 4] == 0)
-        sdone = (ctl + words + ready + recs) // 4
-        assert np.all(dump[sdone: sdone + 256] == 0)
+        assert np.all(dump[: flags // 4] == 0)
 
 
 def test_fused_smaller_batch_after_larger_on_same_workspace():
