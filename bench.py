@@ -12,16 +12,31 @@ synchronisation.  Prints one JSON line on stdout; progress goes to stderr.
 
 Reported:
   value          verified sequences per second (B / seconds per step)
-  roofline       the dominant kernel (fused: the fused kernel, algorithmic
-                 bytes = the whole step's compulsory bytes; three_call: the
-                 stats kernel, every logit once + stats written) / its mean
-                 duration, timed with events on its stream in the timed region
-  cpu_baseline   the fp64 CPU oracle on the same input bytes (whole batch,
-                 all host threads), sequences per second
+  roofline       the dominant kernel (three_call: the stats kernel, every
+                 logit once + stats written; fused: the fused kernel, the
+                 whole step's compulsory bytes) / its mean duration, timed
+                 with events on its stream in the timed region.  traffic is
+                 the HBM bytes per launch that rocprofv3's FETCH_SIZE and
+                 WRITE_SIZE counters measured for that kernel and workload,
+                 scaled by a plain copy of known size, read from a
+                 "traffic-record" line under profiles/; null when no record
+                 matches the current kernel sources
+  cpu_baseline   the fp64 CPU oracle on a bounded sample of the same input
+                 bytes (host threads), sequences per second
+
+    python bench.py --pmc-summary DIR [--path P] [--workload W] [--command CMD]
+
+turns rocprofv3 --pmc CSV output (DIR/fetch, DIR/write, DIR/fetch_copy,
+DIR/write_copy: FETCH_SIZE and WRITE_SIZE of the bench, then of
+--copy-calibration 1024) into the markdown summary kept under profiles/,
+including the traffic-record line.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +48,9 @@ import torch
 from speculative_sampling_verification_softmax_amd import binding, synth
 
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "speculative_sampling_verification_softmax_amd", "csrc")
+COPY_MIB = 1024
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of peak), B=256 K=8 V=128256 bf16"
 
 
@@ -56,7 +74,104 @@ def step_bytes(wl: synth.Workload) -> int:
             + B * 4 + B * (K + 1) * 4 + B * K * 8 + B * 4)
 
 
-def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int) -> dict:
+def kernel_sources_hash() -> str:
+    """sha256 over the kernel sources: a traffic record is valid only for the
+    sources it was measured with."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hpp", ".hip", ".h")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def find_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a matching traffic-record line in profiles/."""
+    want = {"kernel": kernel, "workload": workload, "sources": kernel_sources_hash()}
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("traffic-record:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+                if all(kv.get(k) == v for k, v in want.items()):
+                    return float(kv["bytes"])
+    return None
+
+
+def _pmc_kernels(path: str) -> dict:
+    """{kernel short name: [counter values per dispatch]} from one rocprofv3 --pmc CSV."""
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"].replace("void ", "").split("(")[0]
+            out.setdefault(name, []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
+    f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
+    fetch, write = f("fetch"), f("write")
+    copy_bytes = COPY_MIB << 20
+    def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)
+        v = [x for k, xs in f(sub).items() if "copyBuffer" in k for x in xs]
+        big = [x for x in v if x > 0.9 * max(v)]
+        return sum(big) / len(big)
+    cf, cw = calib("fetch_copy"), calib("write_copy")
+    kf = copy_bytes / (cf * 1024)
+    kw = copy_bytes / (cw * 1024)
+    wl = synth.WORKLOADS[workload]
+    dom = "stats_kernel" if path == "three_call" else "fused_kernel"
+    alg = stats_bytes(wl) if path == "three_call" else step_bytes(wl)
+    lines = [f"# HBM traffic per launch: {path} path, {workload} workload "
+             f"(B={wl.B}, K={wl.K}, V={wl.V}, {wl.dtype}, T={wl.T})", "",
+             "Commands (one MI355X, from the repository root; each pass is a run of its own):", "",
+             "```", command, "```", "",
+             f"Calibration: a plain device copy of {COPY_MIB} MiB reads and writes "
+             f"{copy_bytes} bytes; FETCH_SIZE reads {cf:.1f} KiB and "
+             f"WRITE_SIZE {cw:.1f} KiB per dispatch, so bytes = "
+             f"FETCH_SIZE x {kf:.4f} x 1024 and WRITE_SIZE x {kw:.4f} x 1024.", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read bytes | HBM write bytes |",
+             "|---|---|---|---|---|---|"]
+    rec = None
+    for k in sorted(fetch):
+        if "spec::" not in k:
+            continue
+        fa = sum(fetch[k]) / len(fetch[k])
+        wa = sum(write.get(k, [0.0])) / max(len(write.get(k, [0.0])), 1)
+        rb, wb = fa * 1024 * kf, wa * 1024 * kw
+        lines.append(f"| `{k}` | {len(fetch[k])} | {fa:.1f} | {wa:.1f} | {rb:.4g} | {wb:.4g} |")
+        if dom in k:
+            rec = rb + wb
+    lines += ["", f"Algorithmic bytes of one `{dom}` launch: {alg}."]
+    if rec is not None:
+        lines += [f"Measured HBM bytes per launch: {rec:.6g} ({rec / alg:.4f} of algorithmic).", "",
+                  f"traffic-record: kernel={dom} workload={workload} sources={kernel_sources_hash()} "
+                  f"bytes={rec:.0f}"]
+    return "\n".join(lines) + "\n"
+
+
+def trace_summary(d: str, command: str) -> str:
+    """Markdown table of this library's kernels from rocprofv3 --kernel-trace --stats output."""
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    with open(f[0]) as fh:
+        for r in csv.DictReader(fh):
+            if "spec::" in r["Name"]:
+                rows.append((r["Name"].replace("void ", "").split("(")[0], int(r["Calls"]),
+                             float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
+    lines = ["Command (one MI355X, from the repository root):", "", "```", command, "```", "",
+             "| kernel | calls | average (ns) | min (ns) | max (ns) |", "|---|---|---|---|---|"]
+    lines += [f"| `{n}` | {c} | {a:.0f} | {lo:.0f} | {hi:.0f} |" for n, c, a, lo, hi in rows]
+    lines += ["", "Calls include the warm-up steps; torch's input generation kernels are left out.",
+              f"Kernel sources: {kernel_sources_hash()}."]
+    return "\n".join(lines) + "\n"
+
+
+def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, min_cpu_s: float = 12.0) -> dict:
+    """The oracle on the first max_seqs sequences of the batch, repeated until
+    about min_cpu_s CPU-seconds (wall time x threads) have been spent."""
     import oracle
     n = min(wl.B, max_seqs)
     idx = torch.arange(n, device=inp["target"].device)
@@ -65,13 +180,17 @@ def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int) -> dict:
     host = synth.to_host_arrays(sub)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     T = float(np.float32(wl.T))
-    t0 = time.perf_counter()
-    oracle.verify(host["target"], host["draft"], host["tokens"], host["uniforms"], T,
-                  nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "seqs/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {wl.B} sequences of the same {wl.name} batch "
-                      f"(fp64, {threads} OpenMP threads, {dt:.2f} s wall)"}
+    reps, wall = 0, 0.0
+    while reps == 0 or (wall * threads < min_cpu_s and reps < 200):
+        t0 = time.perf_counter()
+        oracle.verify(host["target"], host["draft"], host["tokens"], host["uniforms"], T,
+                      nthreads=threads)
+        wall += time.perf_counter() - t0
+        reps += 1
+    return {"value": n * reps / wall, "unit": "seqs/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {n} of {wl.B} sequences of the same {wl.name} batch, verified "
+                      f"{reps} times (fp64; {threads} OpenMP threads; {wall:.2f} s wall, "
+                      f"{wall * threads:.1f} CPU-s)"}
 
 
 def main() -> int:
@@ -89,7 +208,21 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(a known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--pmc-summary", default=None, metavar="DIR",
+                    help="print the markdown summary of rocprofv3 --pmc output under DIR and exit")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="print the markdown table of rocprofv3 --kernel-trace --stats output "
+                         "under DIR and exit")
+    ap.add_argument("--command", default="", help="with --pmc-summary / --trace-summary: the "
+                                                  "commands that made DIR")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary, args.path, args.workload, args.command), end="")
+        return 0
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.command), end="")
+        return 0
 
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
@@ -201,7 +334,7 @@ def main() -> int:
         "accepted_hist": hist,
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_us": dom_ms * 1e3,
+                     "traffic": find_traffic(dom_kernel, wl.name), "launch_us": dom_ms * 1e3,
                      "bytes_per_launch": dom_bytes},
         "cpu_baseline": cpu,
     }

@@ -496,7 +496,7 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
                                            ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
   double a = 0.0, bb = 0.0;
-  unsigned unc_bits = 0;
+  unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
@@ -506,12 +506,14 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
       lsp = lsp + ep;
       const double r = ep * R.sq_t;
       const double d = fma(eq, R.sp_t, -r);  // e_q s~_p - e_p s~_q
-      const bool certain = fabs(d) > r * kDelta || eq == 0.0;
+      // |d| >= kDelta r: the sign is certain (a token with e_q = e_p = 0 is
+      // certain and carries no weight)
+      const bool certain = fabs(d) >= r * kDelta;
       // 1.0 or 0.0 (high word only): clearly positive tokens add e_q and e_p
       const double take = __hiloint2double((certain && d > 0.0) ? 0x3ff00000 : 0, 0);
       a = fma(take, eq, a);
       bb = fma(take, ep, bb);
-      if (!certain) unc_bits |= 1u << e;
+      unc_m[e] = __ballot(!certain);
     } else {
       a = a + eq;
     }
@@ -525,7 +527,7 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
     const int x0 = c * (kWave * E) + lane_id() * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      unsigned long long m = __ballot((unc_bits >> e) & 1u);
+      unsigned long long m = unc_m[e];
       while (m) {  // wave-uniform; rare
         const int src = __ffsll(static_cast<long long>(m)) - 1;
         const int idx = __shfl(x0, src, kWave) + e;
@@ -867,9 +869,9 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
       }
     };
     if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, 2>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeResidual, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     else
-      wave_sweep<DT, kModeBonus, 2>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeBonus, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     const double Sq = block_sum<BLOCK>(lsq, sh.red);
     const double Sp = block_sum<BLOCK>(lsp, sh.red);
     tok = fast_finish<BLOCK, DT, false>(
@@ -956,8 +958,9 @@ struct FusedArgs {
 
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kFusedMaxRows = 2 * 64 + 1;
-// Chunks in one slice: kFusedCPW for each wave of the workgroup, all of
-// their loads issued when the slice starts.
+// Chunks in one slice: kFusedCPW for each wave of the workgroup.  Each wave
+// keeps one chunk's loads in flight ahead of the one it computes: deeper
+// prefetch costs registers this kernel does not have (measured slower).
 constexpr int kFusedCPW = 4;
 
 template <int BLOCK>
@@ -1126,9 +1129,9 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
         }
       };
       if (R.mode == kModeResidual)
-        wave_sweep<DT, kModeResidual, kFusedCPW>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+        wave_sweep<DT, kModeResidual, 1>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
       else
-        wave_sweep<DT, kModeBonus, kFusedCPW>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+        wave_sweep<DT, kModeBonus, 1>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
       const double Sq = block_sum<BLOCK>(lsq, sh.d.red);  // its barriers also order the LDS above
       const double Sp = block_sum<BLOCK>(lsp, sh.d.red);
       if (tid < c1 - cb) {
