@@ -65,6 +65,12 @@ def lib():
     L.oracle_verify.restype = i32
     L.oracle_final_draw.argtypes = [vp, vp, i32, i32, i32, i32, f64, vp, vp, vp, vp, vp, i32]
     L.oracle_final_draw.restype = i32
+    L.oracle_argmax_row.argtypes = [vp, i32, i32, vp]
+    L.oracle_argmax_row.restype = i32
+    L.oracle_greedy_verify.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
+    L.oracle_greedy_verify.restype = i32
+    L.oracle_sample_rows.argtypes = [vp, i32, i64, i32, f64, vp, vp, vp, i32]
+    L.oracle_sample_rows.restype = i32
     _lib = L
     return L
 
@@ -198,3 +204,46 @@ def final_draw(target: np.ndarray, draft: np.ndarray, uniforms: np.ndarray,
     if rc != 0:
         raise ValueError(f"oracle_final_draw failed ({rc})")
     return out
+
+
+def argmax_row(row: np.ndarray) -> int | None:
+    """First index of the row's maximum, or None when the row defines no
+    distribution (a NaN, or a maximum that is not finite)."""
+    row, dt = _logits(np.ascontiguousarray(row))
+    idx = np.zeros(1, np.int32)
+    rc = lib().oracle_argmax_row(_ptr(row), dt, int(row.shape[-1]), _ptr(idx))
+    return None if rc != 0 else int(idx[0])
+
+
+def greedy_verify(target: np.ndarray, tokens: np.ndarray, nthreads: int = 0) -> dict:
+    """Greedy verify: target [B][K+1][V] (float32 or bf16 bits), tokens [B][K]."""
+    target, dt = _logits(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    assert tokens.shape == (B, K)
+    out = dict(argmax=np.empty((B, K1), np.int32), num_accepted=np.empty(B, np.int32),
+               out_tokens=np.empty((B, K1), np.int32), num_emitted=np.empty(B, np.int32))
+    rc = lib().oracle_greedy_verify(_ptr(target), dt, B, K, V, _ptr(tokens), _ptr(out["argmax"]),
+                                    _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+                                    _ptr(out["num_emitted"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_greedy_verify failed ({rc})")
+    return out
+
+
+def sample_rows(logits: np.ndarray, uniforms: np.ndarray, T: float, nthreads: int = 0) -> dict:
+    """Draw one token from softmax(row / T) for every row of logits [..., V]
+    with the matching uniform (inverse CDF in ascending token id)."""
+    logits, dt = _logits(logits)
+    V = logits.shape[-1]
+    R = int(np.prod(logits.shape[:-1]))
+    u = np.ascontiguousarray(uniforms, np.float32).reshape(-1)
+    assert u.size == R
+    out = dict(tokens=np.empty(R, np.int32), dist=np.empty(R, np.float64))
+    rc = lib().oracle_sample_rows(_ptr(logits), dt, R, V, float(T), _ptr(u), _ptr(out["tokens"]),
+                                  _ptr(out["dist"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_sample_rows failed ({rc})")
+    shape = logits.shape[:-1]
+    return dict(tokens=out["tokens"].reshape(shape), dist=out["dist"].reshape(shape))

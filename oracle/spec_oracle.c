@@ -367,3 +367,122 @@ int oracle_final_draw(const void* target, const void* draft, int dtype,
     }
     return failed ? -2 : 0;
 }
+
+/* ---------------------------------------------------------------- greedy */
+
+int oracle_argmax_row(const void* row, int dtype, int V, int32_t* idx)
+{
+    double best = 0.0;
+    int32_t at = -1;
+    for (int x = 0; x < V; ++x) {
+        const double z = logit_at(row, dtype, x);
+        if (isnan(z))
+            return -1;
+        if (at < 0 || z > best) {
+            best = z;
+            at = x;
+        }
+    }
+    if (at < 0 || !isfinite(best))
+        return -1;
+    *idx = at;
+    return 0;
+}
+
+int oracle_greedy_verify(const void* target, int dtype, int B, int K, int V,
+                         const int32_t* tokens, int32_t* argmax,
+                         int32_t* num_accepted, int32_t* out_tokens,
+                         int32_t* num_emitted, int nthreads)
+{
+    if (!target || !tokens || !num_accepted || !out_tokens || B < 0 || K < 1 || V < 1)
+        return -1;
+    if ((dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16) || K > 64)
+        return -1;
+    const int eb = dtype == ORACLE_DTYPE_F32 ? 4 : 2;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    int nt = 1;
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int b = 0; b < B; ++b) {
+        int valid = 1;
+        int32_t a[65];
+        for (int t = 0; t <= K; ++t) {
+            const char* row = (const char*)target + ((int64_t)b * (K + 1) + t) * (int64_t)V * eb;
+            if (oracle_argmax_row(row, dtype, V, &a[t]) != 0) {
+                a[t] = -1;
+                valid = 0;
+            }
+            if (argmax)
+                argmax[(int64_t)b * (K + 1) + t] = a[t];
+        }
+        for (int t = 0; t < K; ++t) {
+            const int32_t x = tokens[(int64_t)b * K + t];
+            if (x < 0 || x >= V)
+                valid = 0;
+        }
+        int32_t* out = out_tokens + (int64_t)b * (K + 1);
+        for (int t = 0; t <= K; ++t)
+            out[t] = -1;
+        if (!valid) {
+            num_accepted[b] = -1;
+            if (num_emitted)
+                num_emitted[b] = 0;
+            continue;
+        }
+        int n = 0;
+        while (n < K && tokens[(int64_t)b * K + n] == a[n]) {
+            out[n] = tokens[(int64_t)b * K + n];
+            ++n;
+        }
+        out[n] = a[n];
+        num_accepted[b] = n;
+        if (num_emitted)
+            num_emitted[b] = n + 1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------- draft sampling */
+
+int oracle_sample_rows(const void* logits, int dtype, int64_t R, int V, double T,
+                       const float* uniforms, int32_t* tokens, double* dist, int nthreads)
+{
+    if (!logits || !uniforms || !tokens || R < 0 || V < 1 || !(T > 0.0) || !isfinite(T))
+        return -1;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return -1;
+    const int eb = dtype == ORACLE_DTYPE_F32 ? 4 : 2;
+#ifdef _OPENMP
+    int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    int nt = 1;
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel num_threads(nt)
+    {
+        double* prob = (double*)malloc(sizeof(double) * (size_t)V);
+        if (!prob) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < R; ++r) {
+            if (!prob)
+                continue;
+            const char* row = (const char*)logits + r * (int64_t)V * eb;
+            double M, S, d = 0.0;
+            int32_t x = -1;
+            if (oracle_softmax_row(row, dtype, V, T, prob, &M, &S) == 0)
+                x = oracle_inverse_cdf(prob, V, (double)uniforms[r], &d);
+            tokens[r] = x;
+            if (dist)
+                dist[r] = x >= 0 ? d : INFINITY;
+        }
+        free(prob);
+    }
+    return failed ? -2 : 0;
+}

@@ -19,6 +19,12 @@
  *           at the drafted token; a separate accepted count; residual denominator
  *           0 falls back to q.
  *   [THM1]  Method: Theorem 1, P(X=x) = min(p(x),q(x)) + max(0, q(x)-p(x)) = q(x).
+ *   [GREEDY] Pitfalls: greedy mode.  The card infers the rule from the general
+ *           one applied to one-hot distributions: accept while the drafted
+ *           token is the target argmax, else emit the target argmax.
+ *   [DRAFT] "Algorithm: Speculative Sampling (SpS)" (alg. 2) step 1 and
+ *           Pitfalls: draft tokens are sampled from the (transformed) draft
+ *           distributions p.
  *
  * Every floating-point step is IEEE binary64, evaluated in the order written.
  * Logits are read exactly: fp32 widens to fp64, bf16 is the upper half of a
@@ -121,6 +127,36 @@ int oracle_final_draw(const void* target, const void* draft, int dtype,
                       const float* uniforms, const int32_t* num_accepted,
                       int32_t* token, double* draw_dist, int32_t* draw_kind,
                       int nthreads);
+
+/* Argmax of one logit row [GREEDY]: the first index holding the maximum
+ * stored value (ties go to the smaller index, as numpy's argmax).
+ * Returns 0 and writes *idx, or -1 when the row holds a NaN or its maximum is
+ * not finite (the row defines no distribution). */
+int oracle_argmax_row(const void* row, int dtype, int V, int32_t* idx);
+
+/* Greedy verify [GREEDY]: for each sequence b,
+ *   a_t = argmax of target row t (t = 0..K),
+ *   n = the first t < K with tokens[b][t] != a_t, else K,
+ *   out_tokens[b] = tokens[b][0..n-1], then a_n, then -1; num_emitted = n+1.
+ * This is the general accept rule on one-hot p and q: q/p is 1 at the target
+ * argmax and 0 elsewhere, and the residual (q-p)_+ is one-hot at a_n.
+ * A sequence with a row that defines no distribution, or a draft token
+ * outside [0,V), is invalid: num_accepted -1, out_tokens all -1,
+ * num_emitted 0.  argmax [B][K+1] (nullable) receives a_t (-1 for an invalid
+ * row); num_emitted is nullable.  Returns 0, or -1 on a bad argument. */
+int oracle_greedy_verify(const void* target, int dtype, int B, int K, int V,
+                         const int32_t* tokens, int32_t* argmax,
+                         int32_t* num_accepted, int32_t* out_tokens,
+                         int32_t* num_emitted, int nthreads);
+
+/* Draft-side sampling [DRAFT], [TRANS]: for each of R independent rows r,
+ * the token drawn from softmax(z_r / T) by oracle_inverse_cdf with uniform
+ * u_r in [0,1): x = min { x : sum_{y<=x} prob_y > u_r * sum_y prob_y }.
+ * tokens [R] gets x, or -1 for a row that defines no distribution; dist [R]
+ * (nullable) the draw's boundary distance.  Returns 0, or -1 on a bad
+ * argument. */
+int oracle_sample_rows(const void* logits, int dtype, int64_t R, int V, double T,
+                       const float* uniforms, int32_t* tokens, double* dist, int nthreads);
 
 #ifdef __cplusplus
 }
