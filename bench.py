@@ -24,6 +24,14 @@ Reported:
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same input
                  bytes (host threads), sequences per second
 
+    python bench.py --mode greedy|sample [--steps K] [--warmup W]
+
+times the other two entry points on the same workload instead, with their own
+JSON line: spec_greedy_verify (greedy mode; value = verified sequences/s) or
+spec_sample on the workload's B*K draft rows (draft-side sampling; value =
+tokens/s); roofline = the call's algorithmic bytes (every logit row it needs
+read once) / its mean duration.
+
     python bench.py --pmc-summary DIR [--path P] [--workload W] [--command CMD]
 
 turns rocprofv3 --pmc CSV output (DIR/fetch, DIR/write, DIR/fetch_copy,
@@ -193,6 +201,113 @@ def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, min_cpu_s: float 
                       f"{wall * threads:.1f} CPU-s)"}
 
 
+def timed(step, steps: int, warmup: int, stream) -> tuple[float, float]:
+    """(ms per step over the timed region, mean ms of the event pairs each
+    step records around its main call)."""
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def repeat_cpu(fn, units: int, unit: str, threads: int, what: str, min_cpu_s: float = 12.0):
+    reps, wall = 0, 0.0
+    while reps == 0 or (wall * threads < min_cpu_s and reps < 200):
+        t0 = time.perf_counter()
+        fn()
+        wall += time.perf_counter() - t0
+        reps += 1
+    return {"value": units * reps / wall, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {reps} times (fp64; {threads} OpenMP threads; {wall:.2f} s wall, "
+                      f"{wall * threads:.1f} CPU-s)"}
+
+
+def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
+    """--mode greedy / --mode sample: one JSON record for that entry point."""
+    import oracle
+    B, K, V = wl.B, wl.K, wl.V
+    dev = inp["target"].device
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    if args.mode == "greedy":
+        tgt, tok = inp["target"], inp["tokens"]
+        am = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        nacc = torch.empty(B, dtype=torch.int32, device=dev)
+        out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        ne = torch.empty(B, dtype=torch.int32, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            binding.greedy_verify(tgt, tok, am, nacc, out, ne, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        ms, call_ms = timed(step, args.steps, args.warmup, stream)
+        rows = B * (K + 1)
+        alg = rows * V * wl.elt + rows * 4 + B * K * 4 + B * (K + 1) * 4 + 2 * B * 4
+        units, unit, metric = B, "seqs/s", f"greedy verified seqs/sec, B={B} K={K} V={V} {wl.dtype}"
+        kernel = "argmax_kernel + greedy_scan_kernel"
+        host = synth.to_host_arrays(inp)
+        cpu = None
+        if args.cpu_seqs > 0:
+            cpu = repeat_cpu(lambda: oracle.greedy_verify(host["target"], host["tokens"],
+                                                          nthreads=threads),
+                             B, "seqs/s", threads, f"the whole {wl.name} batch ({B} sequences)")
+    else:
+        logits = inp["draft"]
+        R = B * K
+        g = torch.Generator(device=dev).manual_seed(args.seed + 1)
+        u = (torch.randint(0, 1 << 24, (R,), generator=g, device=dev).to(torch.float64)
+             * 2.0 ** -24).to(torch.float32)
+        st = torch.empty((R, 2), dtype=torch.float32, device=dev)
+        tk = torch.empty(R, dtype=torch.int32, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            binding.sample(logits, u, wl.T, st, tk, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        ms, call_ms = timed(step, args.steps, args.warmup, stream)
+        alg = R * V * wl.elt + R * 4 + R * 8 + R * 4
+        units, unit = R, "tokens/s"
+        metric = f"draft tokens sampled/sec, {R} rows of V={V} {wl.dtype}, T={wl.T}"
+        kernel = "stats_kernel + sample_kernel"
+        cpu = None
+        if args.cpu_seqs > 0:
+            n = min(R, 256)
+            rows = logits.reshape(R, V)[:n].contiguous().cpu()
+            lh = (rows.view(torch.int16).numpy().view(np.uint16) if rows.dtype == torch.bfloat16
+                  else rows.numpy())
+            uh = u[:n].cpu().numpy()
+            T32 = float(np.float32(wl.T))
+            cpu = repeat_cpu(lambda: oracle.sample_rows(lh, uh, T32, nthreads=threads), n,
+                             "tokens/s", threads, f"the first {n} of the {R} draft rows")
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    log(f"[bench] {args.mode}: {ms * 1e3:.1f} us/step, call {call_ms * 1e3:.1f} us")
+    return {
+        "metric": metric, "value": units / (ms * 1e-3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32" if args.mode == "greedy" else "f64",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": args.mode, "B": B, "K": K, "V": V,
+                   "logits": wl.dtype, "T": wl.T, "seed": args.seed},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "launch_us": call_ms * 1e3, "bytes_per_launch": alg},
+        "cpu_baseline": cpu,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +315,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--mode", default="verify", choices=["verify", "greedy", "sample"],
+                    help="verify (the headline step), or time spec_greedy_verify / spec_sample")
     ap.add_argument("--path", default="three_call", choices=["three_call", "fused"],
                     help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
                          "spec_verify, spec_residual_sample")
@@ -256,6 +373,10 @@ def main() -> int:
     probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
     nemit = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.mode != "verify":
+        print(json.dumps(extra_mode(args, wl, inp, stream)), flush=True)
+        return 0
 
     ws = binding.new_workspace(B, K, wl.V, tgt.dtype, dev)
 

@@ -136,6 +136,43 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
                          int32_t* out_tokens, int32_t* num_emitted, void* stream);
 
 /*
+ * spec_greedy_verify -- greedy mode.  The card's Pitfalls (greedy mode) infer
+ * the rule from the general one applied to one-hot distributions: q_t is
+ * one-hot at a_t = argmax_x z^q_t[x], so x_t is accepted iff x_t == a_t, and
+ * the residual at the first mismatch (or the bonus row) is one-hot at a_n.
+ * The draft logits are not needed and T plays no part.
+ *   target_logits  [B][K+1][V], dtype as above
+ *   draft_tokens   [B][K] int32
+ *   target_argmax  out [B][K+1] int32: a_t, the first index of the row's
+ *                  maximum (ties go to the smaller index); -1 for a row that
+ *                  holds a NaN or whose maximum is not finite
+ *   num_accepted   out [B]: n in [0,K], or -1 (such a row, or a draft token
+ *                  outside [0,V), in the sequence)
+ *   out_tokens     out [B][K+1]: x_0..x_{n-1}, then a_n, then -1 (all -1 for
+ *                  an invalid sequence)
+ *   num_emitted    optional out [B]: n+1, or 0 for an invalid sequence
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_tokens,
+                       int B, int K, int V, int32_t* target_argmax, int32_t* num_accepted,
+                       int32_t* out_tokens, int32_t* num_emitted, void* stream);
+
+/*
+ * spec_sample -- draft-side sampling ("Algorithm: Speculative Sampling (SpS)",
+ * alg. 2 step 1, and "Decoding transforms": draft tokens are drawn from the
+ * temperature-transformed p).  For each of R independent rows r:
+ *   x_r = min { x : sum_{y<=x} e(y) > u_r * sum_y e(y) },  e(y) = exp((z_r[y] - m_r)/T),
+ * the same exact inverse CDF in ascending token id as the bonus draw.
+ *   logits      [R][V], dtype as above
+ *   uniforms    [R] in [0, 1)
+ *   row_stats   out [R][2] {m, s} as for spec_softmax_stats (computed here)
+ *   tokens      out [R]: x_r, or -1 for a row that defines no distribution
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
+                const float* uniforms, float* row_stats, int32_t* tokens, void* stream);
+
+/*
  * spec_verify_workspace_size -- bytes of device workspace spec_verify_fused
  * needs for this shape (0 for an invalid shape).  Independent of T.
  */

@@ -24,7 +24,7 @@ SPEC_MAX_K = 64
 SPEC_MAX_V = 1 << 20
 
 EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
-           "spec_verify_workspace_size", "spec_verify_fused")
+           "spec_verify_workspace_size", "spec_verify_fused", "spec_greedy_verify", "spec_sample")
 
 _lib = None
 
@@ -55,6 +55,10 @@ def load(path: str = LIB_PATH):
     L.spec_verify_fused.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                     vp, vp, ctypes.c_size_t, vp]
     L.spec_verify_fused.restype = i32
+    L.spec_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.spec_greedy_verify.restype = i32
+    L.spec_sample.argtypes = [vp, i32, i32, i32, f32, vp, vp, vp, vp]
+    L.spec_sample.restype = i32
     L.spec_status_string.argtypes = [i32]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -241,3 +245,53 @@ def verify_fused(target, draft, tokens, uniforms, T: float, workspace: torch.Ten
     _check(rc, "spec_verify_fused")
     return dict(target_stats=target_stats, draft_stats=draft_stats, num_accepted=num_accepted,
                 out_tokens=out_tokens, probs=probs, num_emitted=num_emitted)
+
+
+def greedy_verify(target, tokens, target_argmax=None, num_accepted=None, out_tokens=None,
+                  num_emitted=True, stream=None) -> dict:
+    """spec_greedy_verify: target [B][K+1][V] logits, tokens [B][K] int32."""
+    if target.dim() != 3:
+        raise ValueError("target must be [B][K+1][V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    if target_argmax is None:
+        target_argmax = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if num_emitted is True:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=dev)
+    elif num_emitted is False:
+        num_emitted = None
+    rc = load().spec_greedy_verify(
+        _dev(target, "target"), _dtype_code(target), _dev(tokens, "tokens", torch.int32, (B, K)),
+        B, K, V, _dev(target_argmax, "target_argmax", torch.int32, (B, K1)),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, K1)),
+        None if num_emitted is None else _dev(num_emitted, "num_emitted", torch.int32, (B,)),
+        _stream(stream))
+    _check(rc, "spec_greedy_verify")
+    return dict(argmax=target_argmax, num_accepted=num_accepted, out_tokens=out_tokens,
+                num_emitted=num_emitted)
+
+
+def sample(logits, uniforms, T: float, row_stats=None, tokens=None, stream=None) -> dict:
+    """spec_sample: one token per row of logits [..., V] from softmax(row / T)."""
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    dev = logits.device
+    if row_stats is None:
+        row_stats = torch.empty((R, 2), dtype=torch.float32, device=dev)
+    if tokens is None:
+        tokens = torch.empty(R, dtype=torch.int32, device=dev)
+    if uniforms.numel() != R:
+        raise ValueError(f"uniforms must hold {R} values")
+    rc = load().spec_sample(_dev(logits, "logits"), _dtype_code(logits), R, V, float(T),
+                            _dev(uniforms, "uniforms", torch.float32),
+                            _dev(row_stats, "row_stats", torch.float32, (R, 2)),
+                            _dev(tokens, "tokens", torch.int32, (R,)), _stream(stream))
+    _check(rc, "spec_sample")
+    shape = tuple(logits.shape[:-1])
+    return dict(tokens=tokens.view(shape), row_stats=row_stats.view(shape + (2,)))

@@ -171,6 +171,55 @@ __device__ __forceinline__ void body_unpack(const uint4 (&v)[VPG],
 // Word 3 of a raw buffer resource on gfx9-family parts (untyped dword access).
 constexpr int kBufWord3 = 0x00020000;
 
+// Streams a row body of nvec 16-byte vectors (body 16-byte aligned) through
+// the block in groups: thread tid's group `it` holds vectors
+// it*BLOCK*VPG + tid + u*BLOCK, u < VPG, unpacked to fp32 in x[u*EPV + e].
+// The next group's loads are issued before f(x, i0) reduces the current one
+// (i0 = the group's first vector index for this thread); the last, partial
+// group reads vectors past nvec as -inf.  `body` must be uniform.
+template <int BLOCK, int DT, int VPG, typename F>
+__device__ __forceinline__ void stream_body(const char* body, int nvec, F f) {
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+  constexpr int STEP = BLOCK * VPG;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(body), static_cast<short>(0), nvec * 16, kBufWord3);
+  const int vo = tid * 16;
+  const int nfull = nvec / STEP;
+  if (nfull > 0) {
+    uint4 v[VPG];
+    body_load<BLOCK, DT, VPG>(rs, vo, 0, v);
+    for (int it = 1; it < nfull; ++it) {
+      float x[VPG * EPV];
+      body_unpack<DT, VPG>(v, x);
+      body_load<BLOCK, DT, VPG>(rs, vo, it * STEP, v);  // next group in flight
+      f(x, (it - 1) * STEP + tid);
+    }
+    float x[VPG * EPV];
+    body_unpack<DT, VPG>(v, x);
+    f(x, (nfull - 1) * STEP + tid);
+  }
+  if (nfull * STEP < nvec) {  // one partial group: vectors past nvec read as -inf
+    const int i0 = nfull * STEP + tid;
+    float x[VPG * EPV];
+#pragma unroll
+    for (int u = 0; u < VPG; ++u) {
+      float xu[EPV];
+      if (i0 + u * BLOCK < nvec) {
+        const auto w =
+            __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (nfull * STEP + u * BLOCK) * 16, 0);
+        unpack16<DT>(make_uint4(w[0], w[1], w[2], w[3]), xu);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xu[e] = -__builtin_huge_valf();
+      }
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
+    }
+    f(x, i0);
+  }
+}
+
 // {m, s} of one row, returned to every thread of the block.  A row with no
 // finite maximum gets s = NaN (NaN logits already make s NaN).  `row` must be
 // uniform across the block.
@@ -192,41 +241,8 @@ __device__ __forceinline__ void row_stats(const char* row, int V, float c2, floa
     fold(acc, x, c2);
   }
   const char* body = row + static_cast<int64_t>(G.head) * Elt<DT>::bytes;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(body), static_cast<short>(0), G.nvec * 16, kBufWord3);
-  const int vo = tid * 16;
-  const int nfull = G.nvec / STEP;
-  if (nfull > 0) {
-    uint4 v[VPG];
-    body_load<BLOCK, DT, VPG>(rs, vo, 0, v);
-    for (int it = 1; it < nfull; ++it) {
-      float x[VPG * EPV];
-      body_unpack<DT, VPG>(v, x);
-      body_load<BLOCK, DT, VPG>(rs, vo, it * STEP, v);  // next group in flight
-      fold(acc, x, c2);
-    }
-    float x[VPG * EPV];
-    body_unpack<DT, VPG>(v, x);
-    fold(acc, x, c2);
-  }
-  if (nfull * STEP < G.nvec) {  // one partial group: vectors past nvec read as -inf
-    const int i0 = nfull * STEP + tid;
-    float x[VPG * EPV];
-#pragma unroll
-    for (int u = 0; u < VPG; ++u) {
-      float xu[EPV];
-      if (i0 + u * BLOCK < G.nvec) {
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (nfull * STEP + u * BLOCK) * 16, 0);
-        unpack16<DT>(make_uint4(w[0], w[1], w[2], w[3]), xu);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) xu[e] = -__builtin_huge_valf();
-      }
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
-    }
-    fold(acc, x, c2);
-  }
+  stream_body<BLOCK, DT, VPG>(body, G.nvec,
+                              [&](const float(&x)[VPG * EPV], int) { fold(acc, x, c2); });
 
   const float m = block_max<BLOCK>(acc.m, red_f);
   float sf;
@@ -816,6 +832,48 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   return tok;
 }
 
+// The whole draw for one row (pair) by one workgroup: the one-sweep fast path
+// when `fast` (dynamic LDS `dyn` then holds A, Bv: nch doubles each; unc_n:
+// nch ints; unc_idx: nch*kUncMax ints), else or on its failure the exact
+// two-sweep path (dyn: nch doubles).  sh.tab must hold the exp table.
+// Returns the token (every thread), or -1 when no token has positive weight.
+template <int BLOCK, int DT>
+__device__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
+                          DrawShared<BLOCK>& sh) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  constexpr int NW = BLOCK / kWave;
+  const int wv = threadIdx.x / kWave, lane = lane_id();
+  const int nch = (R.V + kWave * E - 1) / (kWave * E);
+  int tok = -2;
+  if (fast) {
+    double* A = dyn;
+    double* Bv = A + nch;
+    int* unc_n = reinterpret_cast<int*>(Bv + nch);
+    int* unc_idx = unc_n + nch;
+    double lsq = 0.0, lsp = 0.0;
+    auto emit = [&](int c, const ChunkSums& cs) {
+      if (lane == 0) {
+        A[c] = cs.A;
+        Bv[c] = cs.Bv;
+        unc_n[c] = cs.n_unc;
+#pragma unroll
+        for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
+      }
+    };
+    if (R.mode == kModeResidual)
+      wave_sweep<DT, kModeResidual, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+    else
+      wave_sweep<DT, kModeBonus, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+    const double Sq = block_sum<BLOCK>(lsq, sh.red);
+    const double Sp = block_sum<BLOCK>(lsp, sh.red);
+    tok = fast_finish<BLOCK, DT, false>(
+        R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
+        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
+  }
+  if (tok == -2) tok = slow_draw<BLOCK, DT>(R, nch, dyn, u, sh);
+  return tok;
+}
+
 // One workgroup per sequence (the spec_residual_sample path).  Dynamic LDS:
 // the fast layout (A, Bv: nch doubles each; unc_n: nch ints; unc_idx:
 // nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow path.
@@ -850,38 +908,173 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
   }
   fill_exp2_table(sh.tab);
   __syncthreads();
-  const int nch = (V + kWave * E - 1) / (kWave * E);
-  const double u = uni[b * K1 + K];
-  int tok = -2;
-  if (fast) {
-    double* A = dyn;
-    double* Bv = A + nch;
-    int* unc_n = reinterpret_cast<int*>(Bv + nch);
-    int* unc_idx = unc_n + nch;
-    double lsq = 0.0, lsp = 0.0;
-    auto emit = [&](int c, const ChunkSums& cs) {
-      if (lane == 0) {
-        A[c] = cs.A;
-        Bv[c] = cs.Bv;
-        unc_n[c] = cs.n_unc;
-#pragma unroll
-        for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
-      }
-    };
-    if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
-    else
-      wave_sweep<DT, kModeBonus, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
-    const double Sq = block_sum<BLOCK>(lsq, sh.red);
-    const double Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false>(
-        R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
-        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
-  }
-  if (tok == -2) tok = slow_draw<BLOCK, DT>(R, nch, dyn, u, sh);
+  const int tok = draw_block<BLOCK, DT>(R, uni[b * K1 + K], fast, dyn, sh);
   if (tid == 0) {
     out_tokens[b * K1 + n] = tok;
     if (num_emitted) num_emitted[b] = tok >= 0 ? n + 1 : 0;
+  }
+}
+
+// ============================================================ draft sampling
+//
+// Draft-side sampling ("Algorithm: Speculative Sampling (SpS)", alg. 2 step
+// 1; "Decoding transforms"): one token per row from softmax(z/T), by the
+// same exact inverse CDF as the bonus draw (weights exp((z-m)/T) in fp64,
+// ascending token id, strict >).  One workgroup per row; stats {m, s} of the
+// row come from stats_kernel.
+
+template <int BLOCK, int DT>
+__global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ logits,
+                                                       const float* __restrict__ stats,
+                                                       const float* __restrict__ uni, int V,
+                                                       double yscale, int fast,
+                                                       int32_t* __restrict__ tokens) {
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
+  const int64_t r = blockIdx.x;
+  const float m = stats[2 * r], s = stats[2 * r + 1];
+  if (!row_ok(m, s)) {
+    if (threadIdx.x == 0) tokens[r] = -1;
+    return;
+  }
+  DrawRows R;
+  R.qrow = static_cast<const char*>(logits) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+  R.prow = R.qrow;
+  R.V = V;
+  R.mode = kModeBonus;
+  R.aligned = (reinterpret_cast<uintptr_t>(R.qrow) & 15) == 0;
+  R.yscale = yscale;
+  R.mq = m;
+  R.mp = 0.0;
+  R.sq_t = s;
+  R.sp_t = 1.0;
+  fill_exp2_table(sh.tab);
+  __syncthreads();
+  const int tok = draw_block<BLOCK, DT>(R, uni[r], fast, dyn, sh);
+  if (threadIdx.x == 0) tokens[r] = tok;
+}
+
+// ================================================================== greedy
+//
+// Greedy verify (Pitfalls, greedy mode: the general rule applied to one-hot
+// distributions): a_t = argmax of target row t; accept drafted tokens while
+// they equal a_t; emit a_n at the first mismatch (or a_K after K matches).
+// argmax_kernel: one workgroup per target row, streaming like stats_kernel:
+// per group the max (v_max3), and the group's first maximal element only when
+// the group beats the thread's best so far; NaN anywhere invalidates the row.
+
+template <int BLOCK, int DT, int VPG>
+__global__ __launch_bounds__(BLOCK) void argmax_kernel(const void* __restrict__ rows, int V,
+                                                       int32_t* __restrict__ argmax) {
+  constexpr int EB = Elt<DT>::bytes;
+  constexpr int EPV = 16 / EB;
+  constexpr int STEP = BLOCK * VPG;
+  constexpr int NW = BLOCK / kWave;
+  __shared__ float red_v[NW];
+  __shared__ int red_i[NW];
+  __shared__ unsigned red_nan[NW];
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const char* row = static_cast<const char*>(rows) + static_cast<int64_t>(blockIdx.x) * V * EB;
+  const RowGeom<DT> G(row, V);
+  float best = -__builtin_huge_valf();
+  int best_i = 0x7fffffff;
+  unsigned long long nanm = 0;
+  // a candidate (value, index) that beats the best so far: larger, or equal
+  // with a smaller index
+  auto offer = [&](float v, int i) {
+    if (v > best || (v == best && i < best_i)) {
+      best = v;
+      best_i = i;
+    }
+  };
+  {  // head elements (indices below the body's)
+    const float v = tid < G.head ? logit_f32<DT>(row, tid) : -__builtin_huge_valf();
+    nanm |= __ballot(v != v);
+    if (tid < G.head) offer(v, tid);
+  }
+  const char* body = row + static_cast<int64_t>(G.head) * EB;
+  stream_body<BLOCK, DT, VPG>(body, G.nvec, [&](const float(&x)[VPG * EPV], int i0) {
+#pragma unroll
+    for (int k = 0; k < VPG * EPV; ++k) nanm |= __ballot(x[k] != x[k]);
+    const float g = group_max(x);
+    if (g > best) {  // rare after the first groups: find the group's first maximal element
+      int gi = 0x7fffffff;
+#pragma unroll
+      for (int u = VPG - 1; u >= 0; --u)
+#pragma unroll
+        for (int e = EPV - 1; e >= 0; --e)
+          if (x[u * EPV + e] == g) gi = G.head + (i0 + u * BLOCK) * EPV + e;
+      best = g;
+      best_i = gi;
+    }
+  });
+  {  // tail elements (indices above the body's), after it so that ties keep the body's
+    const bool has = tid < V - G.tail0;
+    const float v = has ? logit_f32<DT>(row, G.tail0 + tid) : -__builtin_huge_valf();
+    nanm |= __ballot(v != v);
+    if (has) offer(v, G.tail0 + tid);
+  }
+  // wave, then block: the largest value, and among equal values the smallest index
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, kWave);
+    const int oi = __shfl_xor(best_i, o, kWave);
+    if (ov > best || (ov == best && oi < best_i)) {
+      best = ov;
+      best_i = oi;
+    }
+  }
+  if (lane == 0) {
+    red_v[wv] = best;
+    red_i[wv] = best_i;
+    red_nan[wv] = nanm != 0ull ? 1u : 0u;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float bv = red_v[0];
+    int bi = red_i[0];
+    unsigned nan = red_nan[0];
+    for (int w = 1; w < NW; ++w) {
+      if (red_v[w] > bv || (red_v[w] == bv && red_i[w] < bi)) {
+        bv = red_v[w];
+        bi = red_i[w];
+      }
+      nan |= red_nan[w];
+    }
+    argmax[blockIdx.x] = (nan || !__builtin_isfinite(bv)) ? -1 : bi;
+  }
+}
+
+// One wave per sequence: the greedy accept scan over the target argmaxes.
+__global__ __launch_bounds__(kWave) void greedy_scan_kernel(const int32_t* __restrict__ argmax,
+                                                            const int32_t* __restrict__ tokens,
+                                                            int K, int V,
+                                                            int32_t* __restrict__ num_accepted,
+                                                            int32_t* __restrict__ out_tokens,
+                                                            int32_t* __restrict__ num_emitted) {
+  const int64_t b = blockIdx.x;
+  const int64_t K1 = K + 1;
+  const int t = lane_id();
+  bool valid = true, mismatch = false;
+  int x = -1;
+  if (t <= K) valid = argmax[b * K1 + t] >= 0;
+  if (t == 0) valid = valid && argmax[b * K1 + K] >= 0;  // the bonus row (lane K may not exist)
+  if (t < K) {
+    x = tokens[b * K + t];
+    valid = valid && x >= 0 && x < V;
+    mismatch = x != argmax[b * K1 + t];
+  }
+  const bool all_valid = __all(valid);
+  const unsigned long long mm = __ballot(mismatch);
+  const int n = !all_valid ? -1 : (mm ? __ffsll(static_cast<long long>(mm)) - 1 : K);
+  if (t == 0) {
+    num_accepted[b] = n;
+    if (num_emitted) num_emitted[b] = n + 1;
+  }
+  for (int pos = t; pos <= K; pos += kWave) {
+    int v = -1;
+    if (n >= 0) v = pos < n ? tokens[b * K + pos] : (pos == n ? argmax[b * K1 + n] : -1);
+    out_tokens[b * K1 + pos] = v;
   }
 }
 

@@ -251,6 +251,74 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
   return launched();
 }
 
+int spec_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
+                       int K, int V, int32_t* target_argmax, int32_t* num_accepted,
+                       int32_t* out_tokens, int32_t* num_emitted, void* stream) {
+  // the target rows alone are checked; T plays no part in an argmax
+  int rc = check_common(target_logits, target_logits, dtype, B, K, V, 1.0f);
+  if (rc != SPEC_OK) return rc;
+  if (!draft_tokens || !target_argmax || !num_accepted || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  if (!aligned(draft_tokens, 4) || !aligned(target_argmax, 4) || !aligned(num_accepted, 4) ||
+      !aligned(out_tokens, 4) || !aligned(num_emitted, 4))
+    return SPEC_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = static_cast<int64_t>(B) * (K + 1);
+  (void)hipGetLastError();
+  if (dtype == SPEC_DTYPE_BF16) {
+    hipLaunchKernelGGL((spec::argmax_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>),
+                       dim3(static_cast<unsigned>(rows)), dim3(kStatsBlock), 0, s, target_logits,
+                       V, target_argmax);
+  } else {
+    hipLaunchKernelGGL((spec::argmax_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>),
+                       dim3(static_cast<unsigned>(rows)), dim3(kStatsBlock), 0, s, target_logits,
+                       V, target_argmax);
+  }
+  rc = launched();
+  if (rc != SPEC_OK) return rc;
+  hipLaunchKernelGGL(spec::greedy_scan_kernel, dim3(static_cast<unsigned>(B)), dim3(spec::kWave), 0,
+                     s, target_argmax, draft_tokens, K, V, num_accepted, out_tokens, num_emitted);
+  return launched();
+}
+
+int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
+                const float* uniforms, float* row_stats, int32_t* tokens, void* stream) {
+  if (R < 1 || static_cast<int64_t>(R) * 2 > 0x7fffffffLL) return SPEC_ERR_INVALID_ARG;
+  // the row checks of the verify calls, with the R rows as a batch of target rows
+  int rc = check_common(logits, logits, dtype, R, 1, V, temperature);
+  if (rc != SPEC_OK) return rc;
+  if (!uniforms || !row_stats || !tokens) return SPEC_ERR_INVALID_ARG;
+  if (!aligned(uniforms, 4) || !aligned(row_stats, 4) || !aligned(tokens, 4))
+    return SPEC_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
+  const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
+  const int nch = num_chunks(V, dtype);
+  const size_t fast_lds = static_cast<size_t>(nch) *
+                          (2 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
+  const int fast = fast_lds <= kResidFastLds ? 1 : 0;
+  const size_t lds = fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
+  (void)hipGetLastError();
+  if (dtype == SPEC_DTYPE_BF16) {
+    hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, logits, static_cast<int64_t>(R), V, c2,
+                       row_stats, row_stats);
+  } else {
+    hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, logits, static_cast<int64_t>(R), V, c2,
+                       row_stats, row_stats);
+  }
+  rc = launched();
+  if (rc != SPEC_OK) return rc;
+  if (dtype == SPEC_DTYPE_BF16) {
+    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kBF16>), dim3(R), dim3(kResidBlock), lds,
+                       s, logits, row_stats, uniforms, V, yscale, fast, tokens);
+  } else {
+    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kF32>), dim3(R), dim3(kResidBlock), lds,
+                       s, logits, row_stats, uniforms, V, yscale, fast, tokens);
+  }
+  return launched();
+}
+
 size_t spec_verify_workspace_size(int B, int K, int V, int dtype) {
   if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
   if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return 0;

@@ -140,3 +140,38 @@ def test_fused_rejects_bad_arguments(case):
     rc = L.spec_verify_fused(P, P, 1, P, P, 2, 3, 100, T, P, P, P, out, None, None, ws,
                              ctypes.c_size_t(nbytes), None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("case", ["tgt", "tok", "am", "nacc", "out", "dtype", "K", "misaligned"])
+def test_greedy_rejects_bad_arguments(case):
+    L = _lib()
+    a = dict(tgt=P, dtype=1, tok=P, K=3, am=P, nacc=P, out=P, ne=None)
+    if case == "dtype":
+        a["dtype"] = 5
+    elif case == "K":
+        a["K"] = 0
+    elif case == "misaligned":
+        a["ne"] = P + 2
+    else:
+        a[case] = None
+    rc = L.spec_greedy_verify(a["tgt"], a["dtype"], a["tok"], 2, a["K"], 100, a["am"], a["nacc"],
+                              a["out"], a["ne"], None)
+    assert rc == 1
+
+
+@pytest.mark.parametrize("case", ["logits", "uni", "stats", "tok", "R", "V", "T", "misaligned"])
+def test_sample_rejects_bad_arguments(case):
+    L = _lib()
+    a = dict(logits=P, R=4, V=100, T=1.0, uni=P, stats=P, tok=P)
+    if case == "R":
+        a["R"] = 0
+    elif case == "V":
+        a["V"] = binding.SPEC_MAX_V + 1
+    elif case == "T":
+        a["T"] = 0.0
+    elif case == "misaligned":
+        a["tok"] = P + 1
+    else:
+        a[case] = None
+    rc = L.spec_sample(a["logits"], 1, a["R"], a["V"], a["T"], a["uni"], a["stats"], a["tok"], None)
+    assert rc == 1

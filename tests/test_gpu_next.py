@@ -1,0 +1,195 @@
+"""GPU parity of the greedy verify and the draft-side sampler (through the C
+ABI) against the fp64 oracle on the same seeded bytes.
+
+Greedy (Pitfalls, greedy mode): argmaxes, accepted counts and tokens must be
+identical (integer work: bit-exact).  Sampler ("Algorithm: Speculative
+Sampling (SpS)", alg. 2 step 1): tokens identical except draws whose uniform
+lies within 1e-6 of a breakpoint of the oracle's CDF (counted, under 1e-4 of
+draws), row normalisers within 1e-5 relative, row maxima exact."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_sampling_verification_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BOUNDARY = 1e-6
+MAX_FLAGGED_FRACTION = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    from speculative_sampling_verification_softmax_amd import binding
+    binding.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_logits(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+# ------------------------------------------------------------------ greedy
+
+def greedy_tokens(target_host: np.ndarray, rng, frac_match: float) -> np.ndarray:
+    """Draft tokens that equal the target argmax (by the oracle) with
+    probability frac_match and are random otherwise."""
+    B, K1, V = target_host.shape
+    K = K1 - 1
+    a = np.empty((B, K), np.int64)
+    for b in range(B):
+        for t in range(K):
+            i = oracle.argmax_row(target_host[b, t])
+            a[b, t] = 0 if i is None else i
+    rnd = rng.integers(0, V, size=(B, K))
+    return np.where(rng.random((B, K)) < frac_match, a, rnd).astype(np.int32)
+
+
+def check_greedy(target: torch.Tensor, tokens_np: np.ndarray, label: str):
+    from speculative_sampling_verification_softmax_amd import binding
+    say(f"[greedy] {label}: B={target.shape[0]} K={target.shape[1] - 1} V={target.shape[2]} "
+        f"{target.dtype} -> gpu")
+    tokens = torch.as_tensor(tokens_np, device="cuda")
+    g = binding.greedy_verify(target, tokens)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in g.items()}
+    o = oracle.greedy_verify(host_logits(target), tokens_np)
+    for k in ("argmax", "num_accepted", "out_tokens", "num_emitted"):
+        np.testing.assert_array_equal(g[k], o[k], err_msg=f"{label}: {k}")
+    hist = np.bincount(o["num_accepted"][o["num_accepted"] >= 0], minlength=target.shape[1])
+    say(f"[greedy] {label}: identical; accepted-count histogram {hist.tolist()}")
+
+
+@pytest.mark.parametrize("wl", ["tiny", "batch1", "small", "headline"])
+def test_greedy_workloads(wl):
+    rng = np.random.default_rng(1)
+    inp = synth.make_inputs(wl, seed=3, device="cuda", B=256 if wl == "tiny" else None)
+    th = host_logits(inp["target"])
+    check_greedy(inp["target"], greedy_tokens(th, rng, 0.8), wl)
+
+
+@pytest.mark.parametrize("V,K,dtype", [(1, 1, "bf16"), (7, 3, "f32"), (513, 2, "bf16"),
+                                       (40000, 5, "f32"), (129, 64, "bf16")])
+def test_greedy_ragged_and_ties(V, K, dtype):
+    rng = np.random.default_rng(V)
+    B = 9
+    # small integers: many exact ties, so the first-index rule is exercised
+    z = rng.integers(-3, 4, size=(B, K + 1, V)).astype(np.float32)
+    t = torch.as_tensor(z, device="cuda")
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t
+    # an odd offset so that rows do not start on 16-byte boundaries
+    big = torch.empty(B * (K + 1) * V + 1, dtype=t.dtype, device="cuda")
+    view = big[1:].view(B, K + 1, V)
+    view.copy_(t)
+    check_greedy(view, greedy_tokens(host_logits(view), rng, 0.7), f"V={V} K={K} {dtype}")
+
+
+def test_greedy_invalid_rows_and_tokens():
+    rng = np.random.default_rng(2)
+    B, K, V = 8, 4, 1000
+    z = torch.randn(B, K + 1, V, device="cuda") * 3
+    z[1, 2, 17] = float("nan")
+    z[2, K, :] = float("-inf")
+    z[3, 0, 5] = float("inf")
+    z[4, 1, :] = float("-inf")
+    z[4, 1, 999] = -1e30  # finite max at the last index
+    tokens = greedy_tokens(host_logits(z), rng, 0.9)
+    tokens[5, 3] = V
+    tokens[6, 0] = -1
+    check_greedy(z, tokens, "invalid rows/tokens")
+
+
+# ------------------------------------------------------------------ sampler
+
+def check_sample(logits: torch.Tensor, T: float, seed: int, label: str):
+    from speculative_sampling_verification_softmax_amd import binding
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    u = (torch.randint(0, 1 << 24, (R,), generator=g, device="cuda").to(torch.float64)
+         * 2.0 ** -24).to(torch.float32)
+    say(f"[sample] {label}: R={R} V={V} {logits.dtype} T={T} -> gpu")
+    out = binding.sample(logits, u, T)
+    torch.cuda.synchronize()
+    tok = out["tokens"].reshape(-1).cpu().numpy()
+    st = out["row_stats"].reshape(-1, 2).cpu().numpy().astype(np.float64)
+    lh = host_logits(logits).reshape(R, V)
+    T32 = float(np.float32(T))
+    o = oracle.sample_rows(lh, u.cpu().numpy(), T32)
+    flagged, failures = 0, []
+    for r in range(R):
+        if tok[r] != o["tokens"][r]:
+            if o["tokens"][r] >= 0 and o["dist"][r] < BOUNDARY:
+                flagged += 1
+            else:
+                failures.append((r, int(tok[r]), int(o["tokens"][r]), float(o["dist"][r])))
+    assert failures == [], f"{label}: {failures[:10]}"
+    assert flagged <= MAX_FLAGGED_FRACTION * R, f"{label}: {flagged} boundary draws of {R}"
+    # stats against the oracle's own row statistics
+    for r in range(0, R, max(1, R // 64)):
+        res = oracle.softmax_row(lh[r], T32)
+        if res is None:
+            assert np.isnan(st[r, 1])
+            continue
+        _, M, S = res
+        assert st[r, 0] / T32 == M, f"{label}: row {r} max"
+        assert abs(st[r, 1] - S) <= 1e-5 * S, f"{label}: row {r} s"
+    say(f"[sample] {label}: tokens identical except {flagged} boundary draws")
+
+
+@pytest.mark.parametrize("wl", ["batch1", "small", "headline"])
+def test_sample_draft_rows(wl):
+    inp = synth.make_inputs(wl, seed=4, device="cuda")
+    check_sample(inp["draft"], inp["T"], 10, wl)
+
+
+@pytest.mark.parametrize("V,dtype,T", [(1, "f32", 1.0), (63, "bf16", 0.3), (2049, "f32", 2.5),
+                                       (100003, "bf16", 1.0)])
+def test_sample_ragged(V, dtype, T):
+    R = 37
+    z = torch.randn(R, V, device="cuda", generator=torch.Generator(device="cuda").manual_seed(V)) * 3
+    z = z.to(torch.bfloat16) if dtype == "bf16" else z
+    big = torch.empty(R * V + 3, dtype=z.dtype, device="cuda")
+    view = big[3:].view(R, V)  # rows off 16-byte boundaries
+    view.copy_(z)
+    check_sample(view, T, V, f"V={V} {dtype}")
+
+
+def test_sample_masks_and_invalid_rows():
+    R, V = 6, 300
+    z = torch.randn(R, V, device="cuda")
+    z[0, :] = float("-inf")
+    z[0, 123] = 0.0          # a single allowed token
+    z[1, 7] = float("nan")   # invalid
+    z[2, :] = float("-inf")  # invalid
+    z[3, ::2] = float("-inf")
+    check_sample(z, 1.0, 5, "masks")
+    from speculative_sampling_verification_softmax_amd import binding
+    out = binding.sample(z, torch.full((R,), 0.5, device="cuda"), 1.0)["tokens"].cpu().numpy()
+    assert out[0] == 123 and out[1] == -1 and out[2] == -1 and out[3] % 2 == 1
+
+
+def test_sample_law_chi_square():
+    """The draws follow softmax(z/T): chi-square of 2e5 draws on one row."""
+    from scipy import special
+    from tests.stats_util import chisquare_pvalue
+    from speculative_sampling_verification_softmax_amd import binding
+    V, N, T = 64, 200_000, 0.8
+    g = torch.Generator(device="cuda").manual_seed(21)
+    z = torch.randn(V, device="cuda", generator=g) * 2
+    rows = z.expand(N, V).contiguous()
+    u = (torch.randint(0, 1 << 24, (N,), generator=g, device="cuda").to(torch.float64)
+         * 2.0 ** -24).to(torch.float32)
+    tok = binding.sample(rows, u, T)["tokens"].cpu().numpy()
+    p = special.softmax(z.cpu().numpy().astype(np.float64) / float(np.float32(T)))
+    assert chisquare_pvalue(np.bincount(tok, minlength=V), p) > 1e-4
