@@ -32,6 +32,13 @@ spec_sample on the workload's B*K draft rows (draft-side sampling; value =
 tokens/s); roofline = the call's algorithmic bytes (every logit row it needs
 read once) / its mean duration.
 
+    python bench.py --mode ksweep [--ks 1,2,4,8,16]
+
+the K trade-off of the pages' fig. 1 on synthetic rows: for each K, the
+three-call verify at the workload's B, V, T and draft noise (fresh inputs per
+K), its time per call and the mean tokens emitted per sequence; one JSON line
+with a "sweep" list.
+
     python bench.py --pmc-summary DIR [--path P] [--workload W] [--command CMD]
 
 turns rocprofv3 --pmc CSV output (DIR/fetch, DIR/write, DIR/fetch_copy,
@@ -308,6 +315,45 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
     }
 
 
+def ksweep(args, base: synth.Workload) -> dict:
+    """Verify time and emitted tokens per sequence as K varies (fig. 1 analogue)."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for K in [int(k) for k in args.ks.split(",")]:
+        wl = synth.workload(base.name, K=K)
+        inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
+        tgt, dft, tok, uni = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"]
+        B = wl.B
+        ts = torch.empty((B, K + 1, 2), dtype=torch.float32, device="cuda")
+        ds = torch.empty((B, K, 2), dtype=torch.float32, device="cuda")
+        nacc = torch.empty(B, dtype=torch.int32, device="cuda")
+        o = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+        pr = torch.empty((B, K, 2), dtype=torch.float32, device="cuda")
+        ne = torch.empty(B, dtype=torch.int32, device="cuda")
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            binding.softmax_stats(tgt, dft, wl.T, ts, ds, stream=stream)
+            binding.verify(tgt, dft, tok, uni, ts, ds, wl.T, nacc, o, pr, stream=stream)
+            binding.residual_sample(tgt, dft, uni, ts, ds, nacc, wl.T, o, ne, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        ms, _ = timed(step, args.steps, args.warmup, stream)
+        emitted = float(ne.double().mean().item())
+        out.append({"K": K, "us_per_call": ms * 1e3, "emitted_per_seq": emitted,
+                    "emitted_tokens_per_s": B * emitted / (ms * 1e-3),
+                    "GBps": step_bytes(wl) / (ms * 1e-3) / 1e9})
+        log(f"[bench] K={K}: {ms * 1e3:.1f} us, {emitted:.3f} tokens/seq")
+        del inp, tgt, dft
+        torch.cuda.empty_cache()
+    return {"metric": f"verify time and emitted tokens per sequence vs K, B={base.B} "
+                      f"V={base.V} {base.dtype} T={base.T}",
+            "unit": "per K", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic", "config": {"workload": base.name, "mode": "ksweep"},
+            "sweep": out}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,8 +361,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--mode", default="verify", choices=["verify", "greedy", "sample"],
-                    help="verify (the headline step), or time spec_greedy_verify / spec_sample")
+    ap.add_argument("--mode", default="verify", choices=["verify", "greedy", "sample", "ksweep"],
+                    help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
+                         "sweep K")
+    ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
     ap.add_argument("--path", default="three_call", choices=["three_call", "fused"],
                     help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
                          "spec_verify, spec_residual_sample")
@@ -361,6 +409,9 @@ def main() -> int:
 
     binding.load()
     wl = synth.WORKLOADS[args.workload]
+    if args.mode == "ksweep":
+        print(json.dumps(ksweep(args, wl)), flush=True)
+        return 0
     log(f"[bench] generating {wl.name}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype} T={wl.T}")
     inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
     tgt, dft, tok, uni, T = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], wl.T
