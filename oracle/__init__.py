@@ -71,6 +71,11 @@ def lib():
     L.oracle_greedy_verify.restype = i32
     L.oracle_sample_rows.argtypes = [vp, i32, i64, i32, f64, vp, vp, vp, i32]
     L.oracle_sample_rows.restype = i32
+    L.oracle_filter_threshold.argtypes = [vp, i32, i32, f64, i32, f64, vp]
+    L.oracle_filter_threshold.restype = i32
+    L.oracle_verify_filtered.argtypes = [vp, vp, i32, i32, i32, i32, f64, i32, f64, vp, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+    L.oracle_verify_filtered.restype = i32
     _lib = L
     return L
 
@@ -247,3 +252,42 @@ def sample_rows(logits: np.ndarray, uniforms: np.ndarray, T: float, nthreads: in
         raise ValueError(f"oracle_sample_rows failed ({rc})")
     shape = logits.shape[:-1]
     return dict(tokens=out["tokens"].reshape(shape), dist=out["dist"].reshape(shape))
+
+
+def filter_threshold(row: np.ndarray, T: float, top_k: int = 0, top_p: float = 1.0):
+    """Logit threshold of the decoding transforms on one row (-inf: nothing
+    removed), or None when the row defines no distribution."""
+    row, dt = _logits(np.ascontiguousarray(row))
+    t = np.zeros(1, np.float64)
+    rc = lib().oracle_filter_threshold(_ptr(row), dt, int(row.shape[-1]), float(T), int(top_k),
+                                       float(top_p), _ptr(t))
+    return None if rc != 0 else float(t[0])
+
+
+def verify_filtered(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
+                    uniforms: np.ndarray, T: float, top_k: int = 0, top_p: float = 1.0,
+                    nthreads: int = 0) -> dict:
+    """verify() on the rows after temperature, top-k and nucleus."""
+    target, dt = _logits(target)
+    draft, dt2 = _logits(draft)
+    assert dt == dt2
+    B, K1, V = target.shape
+    K = K1 - 1
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    uniforms = np.ascontiguousarray(uniforms, np.float32)
+    out = dict(
+        target_thr=np.empty((B, K + 1), np.float64), draft_thr=np.empty((B, K), np.float64),
+        target_stats=np.empty((B, K + 1, 2), np.float64), draft_stats=np.empty((B, K, 2), np.float64),
+        num_accepted=np.empty(B, np.int32), out_tokens=np.empty((B, K + 1), np.int32),
+        num_emitted=np.empty(B, np.int32), probs=np.empty((B, K, 2), np.float64),
+        accept_dist=np.empty((B, K), np.float64), draw_dist=np.empty(B, np.float64),
+        draw_kind=np.empty(B, np.int32))
+    rc = lib().oracle_verify_filtered(
+        _ptr(target), _ptr(draft), dt, B, K, V, float(T), int(top_k), float(top_p), _ptr(tokens),
+        _ptr(uniforms), _ptr(out["target_thr"]), _ptr(out["draft_thr"]), _ptr(out["target_stats"]),
+        _ptr(out["draft_stats"]), _ptr(out["num_accepted"]), _ptr(out["out_tokens"]),
+        _ptr(out["num_emitted"]), _ptr(out["probs"]), _ptr(out["accept_dist"]),
+        _ptr(out["draw_dist"]), _ptr(out["draw_kind"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_filtered failed ({rc})")
+    return out

@@ -486,3 +486,122 @@ int oracle_sample_rows(const void* logits, int dtype, int64_t R, int V, double T
     }
     return failed ? -2 : 0;
 }
+
+/* -------------------------------------------------- decoding transforms */
+
+static int cmp_desc(const void* a, const void* b)
+{
+    const double x = *(const double*)a, y = *(const double*)b;
+    return (x < y) - (x > y);
+}
+
+int oracle_filter_threshold(const void* row, int dtype, int V, double T, int top_k,
+                            double top_p, double* thr)
+{
+    if (!row || !thr || V < 1 || !(T > 0.0) || !isfinite(T) || !(top_p > 0.0))
+        return -1;
+    double* v = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!v)
+        return -1;
+    double mx = -INFINITY;
+    for (int x = 0; x < V; ++x) {
+        v[x] = logit_at(row, dtype, x);
+        if (isnan(v[x])) {
+            free(v);
+            return -1;
+        }
+        if (v[x] > mx)
+            mx = v[x];
+    }
+    if (!isfinite(mx)) {
+        free(v);
+        return -1;
+    }
+    qsort(v, (size_t)V, sizeof(double), cmp_desc);
+    double t = -INFINITY;
+    int n = V;  /* kept values are v[0..n) */
+    if (top_k > 0 && top_k < V) {
+        t = v[top_k - 1];
+        while (n > 0 && v[n - 1] < t)
+            --n;
+    }
+    if (top_p < 1.0) {
+        const double M = v[0] / T;
+        double S = 0.0;
+        for (int i = 0; i < n; ++i)
+            S += exp(v[i] / T - M);
+        double c = 0.0;
+        int i = 0;
+        while (i < n) {
+            const double val = v[i];
+            while (i < n && v[i] == val)
+                c += exp(v[i++] / T - M);
+            if (c >= top_p * S) {
+                if (val > t)
+                    t = val;
+                break;
+            }
+        }
+    }
+    /* a threshold at or below the smallest logit removes nothing */
+    if (t <= v[V - 1])
+        t = -INFINITY;
+    *thr = t;
+    free(v);
+    return 0;
+}
+
+int oracle_verify_filtered(const void* target, const void* draft, int dtype,
+                           int B, int K, int V, double T, int top_k, double top_p,
+                           const int32_t* tokens, const float* uniforms,
+                           double* target_thr, double* draft_thr,
+                           double* target_stats, double* draft_stats,
+                           int32_t* num_accepted, int32_t* out_tokens, int32_t* num_emitted,
+                           double* probs, double* accept_dist, double* draw_dist,
+                           int32_t* draw_kind, int nthreads)
+{
+    if (!target || !draft || B < 1 || K < 1 || V < 1 || !(top_p > 0.0))
+        return -1;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return -1;
+    const size_t eb = dtype == ORACLE_DTYPE_F32 ? 4 : 2;
+    const int64_t nt = (int64_t)B * (K + 1), nd = (int64_t)B * K;
+    char* tc = (char*)malloc((size_t)nt * (size_t)V * eb);
+    char* dc = (char*)malloc((size_t)nd * (size_t)V * eb);
+    if (!tc || !dc) {
+        free(tc);
+        free(dc);
+        return -2;
+    }
+    memcpy(tc, target, (size_t)nt * (size_t)V * eb);
+    memcpy(dc, draft, (size_t)nd * (size_t)V * eb);
+    for (int64_t r = 0; r < nt + nd; ++r) {
+        char* row = r < nt ? tc + r * (int64_t)V * (int64_t)eb : dc + (r - nt) * (int64_t)V * (int64_t)eb;
+        double t;
+        if (oracle_filter_threshold(row, dtype, V, T, top_k, top_p, &t) != 0)
+            t = NAN;
+        if (r < nt) {
+            if (target_thr)
+                target_thr[r] = t;
+        } else if (draft_thr) {
+            draft_thr[r - nt] = t;
+        }
+        if (!(t > -INFINITY))
+            continue;  /* nothing removed, or an invalid row (left as it is) */
+        for (int x = 0; x < V; ++x) {
+            if (logit_at(row, dtype, x) < t) {
+                if (dtype == ORACLE_DTYPE_F32) {
+                    ((float*)row)[x] = -INFINITY;
+                } else {
+                    ((uint16_t*)row)[x] = 0xFF80u;  /* bf16 -inf */
+                }
+            }
+        }
+    }
+    const int rc = oracle_verify(tc, dc, dtype, B, K, V, T, tokens, uniforms, target_stats,
+                                 draft_stats, num_accepted, out_tokens, num_emitted, probs,
+                                 accept_dist, draw_dist, draw_kind, nthreads);
+    free(tc);
+    free(dc);
+    return rc;
+}

@@ -158,6 +158,37 @@ int oracle_greedy_verify(const void* target, int dtype, int B, int K, int V,
 int oracle_sample_rows(const void* logits, int dtype, int64_t R, int V, double T,
                        const float* uniforms, int32_t* tokens, double* dist, int nthreads);
 
+/* Decoding transforms [TRANS], [PIT]: temperature, then top-k, then nucleus
+ * (top-p), applied alike to every target and draft row before anything else.
+ * The result is a logit threshold thr: tokens with z < thr get probability 0,
+ * the others keep their relative weights exp(z/T - M).
+ *   top-k (0 < top_k < V): thr_k = the top_k-th largest stored logit; every
+ *     token at or above it is kept (ties at thr_k included).
+ *   nucleus (top_p < 1), over the tokens top-k kept: with e_x = exp(z_x/T - M)
+ *     and the kept values taken in descending order, S = their sum and
+ *     C(v) = the sum over tokens with z >= v (the same additions, a prefix of
+ *     S), thr_p = the largest stored value v with C(v) >= top_p * S.
+ * thr = -inf when nothing is removed.  Returns 0, or -1 when the row defines
+ * no distribution (then thr is left alone) or the parameters are invalid
+ * (top_p <= 0 or NaN). */
+int oracle_filter_threshold(const void* row, int dtype, int V, double T, int top_k,
+                            double top_p, double* thr);
+
+/* oracle_verify on the transformed rows: every target and draft row is
+ * thresholded by oracle_filter_threshold (tokens below become -inf in a copy
+ * of the logits) and the copies are verified.  target_thr [B][K+1] and
+ * draft_thr [B][K] (nullable) receive the thresholds (NaN for a row that
+ * defines no distribution).  Other arguments and outputs as oracle_verify.
+ * Returns 0, -1 on a bad argument, -2 if memory could not be obtained. */
+int oracle_verify_filtered(const void* target, const void* draft, int dtype,
+                           int B, int K, int V, double T, int top_k, double top_p,
+                           const int32_t* tokens, const float* uniforms,
+                           double* target_thr, double* draft_thr,
+                           double* target_stats, double* draft_stats,
+                           int32_t* num_accepted, int32_t* out_tokens, int32_t* num_emitted,
+                           double* probs, double* accept_dist, double* draw_dist,
+                           int32_t* draw_kind, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
