@@ -240,7 +240,7 @@ def repeat_cpu(fn, units: int, unit: str, threads: int, what: str, min_cpu_s: fl
 
 
 def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
-    """--mode greedy / --mode sample: one JSON record for that entry point."""
+    """--mode greedy / sample / filter: one JSON record for that entry point."""
     import oracle
     B, K, V = wl.B, wl.K, wl.V
     dev = inp["target"].device
@@ -269,6 +269,42 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
             cpu = repeat_cpu(lambda: oracle.greedy_verify(host["target"], host["tokens"],
                                                           nthreads=threads),
                              B, "seqs/s", threads, f"the whole {wl.name} batch ({B} sequences)")
+    elif args.mode == "filter":
+        tgt, dft = inp["target"], inp["draft"]
+        ft, fd = torch.empty_like(tgt), torch.empty_like(dft)
+        tt = torch.empty(B * (K + 1), dtype=torch.float32, device=dev)
+        td = torch.empty(B * K, dtype=torch.float32, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            binding.filter_rows(tgt, wl.T, args.top_k, args.top_p, out=ft, thresholds=tt,
+                                stream=stream)
+            binding.filter_rows(dft, wl.T, args.top_k, args.top_p, out=fd, thresholds=td,
+                                stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        ms, call_ms = timed(step, args.steps, args.warmup, stream)
+        R = B * (2 * K + 1)
+        alg = 2 * R * V * wl.elt + R * 4  # each row read once and written once
+        units, unit = B, "seqs/s"
+        metric = (f"filtered seqs/sec (top-k {args.top_k}, top-p {args.top_p}, target and draft "
+                  f"rows), B={B} K={K} V={V} {wl.dtype}")
+        kernel = "filter_kernel x2"
+        cpu = None
+        if args.cpu_seqs > 0:
+            n = min(B * K, 64)
+            rows = dft.reshape(B * K, V)[:n].contiguous().cpu()
+            lh = (rows.view(torch.int16).numpy().view(np.uint16) if rows.dtype == torch.bfloat16
+                  else rows.numpy())
+            T32, p32 = float(np.float32(wl.T)), float(np.float32(args.top_p))
+
+            def cpu_rows():
+                for r in range(n):
+                    oracle.filter_threshold(lh[r], T32, top_k=args.top_k, top_p=p32)
+            cpu = repeat_cpu(cpu_rows, n / (2 * K + 1), "seqs/s", 1,
+                             f"thresholds of the first {n} draft rows (one thread), "
+                             f"scaled to {2 * K + 1} rows per sequence")
     else:
         logits = inp["draft"]
         R = B * K
@@ -361,10 +397,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--mode", default="verify", choices=["verify", "greedy", "sample", "ksweep"],
+    ap.add_argument("--mode", default="verify",
+                    choices=["verify", "greedy", "sample", "filter", "ksweep"],
                     help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
                          "sweep K")
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
+    ap.add_argument("--top-k", type=int, default=50, help="top-k for --mode filter (0: off)")
+    ap.add_argument("--top-p", type=float, default=0.9, help="nucleus top_p for --mode filter")
     ap.add_argument("--path", default="three_call", choices=["three_call", "fused"],
                     help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
                          "spec_verify, spec_residual_sample")

@@ -173,6 +173,34 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
                 const float* uniforms, float* row_stats, int32_t* tokens, void* stream);
 
 /*
+ * spec_filter -- the decoding transforms top-k and nucleus (the card's Method,
+ * "Decoding transforms", and Pitfalls: temperature, top-k and nucleus are
+ * applied alike to p and q, before the ratio, the residual and the draft
+ * draws).  Run it on the target rows and on the draft rows, then give the
+ * filtered rows to the calls above (and to spec_sample on the draft side).
+ * For each of R independent rows, with z the stored logits:
+ *   top-k (0 < top_k < V): t_k = the top_k-th largest stored value; tokens
+ *     with z >= t_k are kept (ties with it all kept).
+ *   nucleus (top_p < 1), over the top-k survivors: with e = exp((z - m)/T),
+ *     t_p = the largest stored value v with sum_{z >= v} e >= top_p * sum e.
+ *   thr = max(t_k, t_p); the kept set is {x : z[x] >= thr}.
+ *   logits       [R][V], dtype as above
+ *   temperature  T > 0 (used by the nucleus masses only)
+ *   top_k        0 or >= V: no top-k; negative: invalid
+ *   top_p        >= 1: no nucleus; <= 0 or NaN: invalid
+ *   thresholds   out [R] float: thr, -inf when nothing is removed, NaN for a
+ *                row that defines no distribution (a NaN, or no finite
+ *                maximum; its row is copied unchanged)
+ *   filtered     optional out [R][V], dtype as logits: z with removed tokens
+ *                set to -inf.  May equal logits (in place; then rows with
+ *                nothing removed are not written); may not overlap it
+ *                otherwise.  NULL: thresholds only.
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_filter(const void* logits, int dtype, int R, int V, float temperature, int top_k,
+                float top_p, float* thresholds, void* filtered, void* stream);
+
+/*
  * spec_verify_workspace_size -- bytes of device workspace spec_verify_fused
  * needs for this shape (0 for an invalid shape).  Independent of T.
  */

@@ -24,7 +24,8 @@ SPEC_MAX_K = 64
 SPEC_MAX_V = 1 << 20
 
 EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
-           "spec_verify_workspace_size", "spec_verify_fused", "spec_greedy_verify", "spec_sample")
+           "spec_verify_workspace_size", "spec_verify_fused", "spec_greedy_verify", "spec_sample",
+           "spec_filter")
 
 _lib = None
 
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH):
     L.spec_greedy_verify.restype = i32
     L.spec_sample.argtypes = [vp, i32, i32, i32, f32, vp, vp, vp, vp]
     L.spec_sample.restype = i32
+    L.spec_filter.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp]
+    L.spec_filter.restype = i32
     L.spec_status_string.argtypes = [i32]
     L.spec_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -295,3 +298,31 @@ def sample(logits, uniforms, T: float, row_stats=None, tokens=None, stream=None)
     _check(rc, "spec_sample")
     shape = tuple(logits.shape[:-1])
     return dict(tokens=tokens.view(shape), row_stats=row_stats.view(shape + (2,)))
+
+
+def filter_rows(logits, T: float, top_k: int = 0, top_p: float = 1.0, out=None,
+                thresholds=None, inplace: bool = False, write_rows: bool = True,
+                stream=None) -> dict:
+    """spec_filter: top-k / nucleus thresholds of each row of logits [..., V]
+    and the rows with the removed tokens set to -inf (written into `out`, a
+    new tensor by default, or into logits itself when inplace; not written
+    at all when write_rows is False)."""
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    dev = logits.device
+    if thresholds is None:
+        thresholds = torch.empty(R, dtype=torch.float32, device=dev)
+    if not write_rows:
+        out = None
+    elif inplace:
+        out = logits
+    elif out is None:
+        out = torch.empty_like(logits)
+    out_ptr = None if out is None else _dev(out, "out", logits.dtype, tuple(logits.shape))
+    rc = load().spec_filter(_dev(logits, "logits"), _dtype_code(logits), R, V, float(T),
+                            int(top_k), float(top_p),
+                            _dev(thresholds, "thresholds", torch.float32, (R,)), out_ptr,
+                            _stream(stream))
+    _check(rc, "spec_filter")
+    shape = tuple(logits.shape[:-1])
+    return dict(filtered=out, thresholds=thresholds.view(shape))

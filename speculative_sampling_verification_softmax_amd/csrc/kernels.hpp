@@ -14,6 +14,8 @@
 // Sampling (SpS)", alg. 2 steps 2-4; "Decoding transforms") and Pitfalls.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace spec {
@@ -1075,6 +1077,233 @@ __global__ __launch_bounds__(kWave) void greedy_scan_kernel(const int32_t* __res
     int v = -1;
     if (n >= 0) v = pos < n ? tokens[b * K + pos] : (pos == n ? argmax[b * K1 + n] : -1);
     out_tokens[b * K1 + pos] = v;
+  }
+}
+
+// ==================================================================== filter
+//
+// Decoding transforms ("Decoding transforms"; Pitfalls: temperature, top-k
+// and nucleus applied alike to p and q before anything else): per row a
+// logit threshold thr, tokens below it removed (written as -inf into the
+// output rows; the other calls then run unchanged on them).
+//   top-k (0 < k < V): thr_k = the k-th largest stored logit, ties kept.
+//   nucleus (top_p < 1), over the top-k survivors: with e = exp((z - m)/T) in
+//     fp64, thr_p = the largest stored value v whose mass sum_{z >= v} e
+//     reaches top_p * sum e.
+// Both are radix selects over an order-preserving integer key of the stored
+// value (16-bit for bf16, 32-bit for fp32), 8 bits per pass: each pass
+// re-reads the row, builds a 256-bin histogram in LDS (counts, or fp64
+// masses with ds_add_f64) of the tokens whose key matches the digits chosen
+// so far, and wave 0 walks the bins from the top to the one where the running
+// count (mass) reaches what is still needed.  Sort-free, exact, and slow: one
+// row read per pass (3 for bf16 top-k + nucleus, 9 for fp32), plus the fp64
+// exponentials of the nucleus passes.
+
+// Order-preserving key of a stored value; -0 is taken as +0 so that equal
+// values share a key.
+template <int DT>
+__device__ __forceinline__ unsigned order_key(float x) {
+  constexpr unsigned kSign = DT == kBF16 ? 0x8000u : 0x80000000u;
+  constexpr unsigned kAll = DT == kBF16 ? 0xFFFFu : 0xFFFFFFFFu;
+  unsigned b = __float_as_uint(x + 0.0f);
+  if constexpr (DT == kBF16) b >>= 16;
+  return (b & kSign) ? (~b & kAll) : (b | kSign);
+}
+
+template <int DT>
+__device__ __forceinline__ float key_value(unsigned k) {
+  constexpr unsigned kSign = DT == kBF16 ? 0x8000u : 0x80000000u;
+  constexpr unsigned kAll = DT == kBF16 ? 0xFFFFu : 0xFFFFFFFFu;
+  unsigned b = (k & kSign) ? (k & ~kSign) : (~k & kAll);
+  if constexpr (DT == kBF16) b <<= 16;
+  return __uint_as_float(b);
+}
+
+// f(x) for every stored value of a row (no padding), streaming the body with
+// stream_body.
+template <int BLOCK, int DT, int VPG, typename F>
+__device__ __forceinline__ void for_each_value(const char* row, int V, F f) {
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+  const int tid = threadIdx.x;
+  const RowGeom<DT> G(row, V);
+  if (tid < G.head) f(logit_f32<DT>(row, tid));
+  const int nvec = G.nvec;
+  stream_body<BLOCK, DT, VPG>(row + static_cast<int64_t>(G.head) * Elt<DT>::bytes, nvec,
+                              [&](const float(&x)[VPG * EPV], int i0) {
+#pragma unroll
+                                for (int u = 0; u < VPG; ++u)
+                                  if (i0 + u * BLOCK < nvec)
+#pragma unroll
+                                    for (int e = 0; e < EPV; ++e) f(x[u * EPV + e]);
+                              });
+  if (tid < V - G.tail0) f(logit_f32<DT>(row, G.tail0 + tid));
+}
+
+// Wave 0 walks hist[255..0] from the top: the first bin where the running
+// total reaches `need`.  Writes the bin to *bin_out and what is still needed
+// inside it (need minus the total above it) to *need_out.
+__device__ __forceinline__ void walk_bins(const double* hist, double need, int* bin_out,
+                                          double* need_out) {
+  const int lane = lane_id();
+  double v[4];
+  double ls = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // lane l holds bins 255-4l .. 252-4l, top first
+    v[j] = hist[255 - 4 * lane - j];
+    ls = ls + v[j];
+  }
+  const double incl = wave_incl_scan(ls);
+  const double excl = incl - ls;
+  const unsigned long long hit = __ballot(incl >= need);
+  // rounding can leave the total a hair under `need`: then the lowest bin
+  // holding anything is taken
+  const int src = hit ? static_cast<int>(__builtin_ctzll(hit)) : -1;
+  if (src < 0) {
+    if (lane == 0) {
+      int b = 0;
+      for (int i = 0; i < 256; ++i)
+        if (hist[i] > 0.0) {
+          b = i;
+          break;
+        }
+      *bin_out = b;
+      *need_out = 0.0;
+    }
+    return;
+  }
+  if (lane == src) {
+    double cum = excl;
+    int b = 255 - 4 * lane - 3;
+    double left = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (cum + v[j] >= need) {
+        b = 255 - 4 * lane - j;
+        left = need - cum;
+        break;
+      }
+      cum = cum + v[j];
+    }
+    *bin_out = b;
+    *need_out = left;
+  }
+}
+
+template <int BLOCK, int DT, int VPG>
+__global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out, int V,
+                                                       double yscale, int top_k, float top_p,
+                                                       float* __restrict__ thr_out) {
+  constexpr int KB = DT == kBF16 ? 16 : 32;  // key bits
+  constexpr int NW = BLOCK / kWave;
+  __shared__ double tab[Exp64::kTab];
+  __shared__ double hist[256];
+  __shared__ float redf[NW];
+  __shared__ unsigned redu[NW];
+  __shared__ int sel_bin;
+  __shared__ double sel_need;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  const int64_t r = blockIdx.x;
+  const char* row = static_cast<const char*>(in) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+  char* orow = static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+  fill_exp2_table(tab);
+
+  // pass 0: max, min and NaN
+  float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
+  unsigned long long nanm = 0;
+  for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
+    mx = fmaxf(mx, x);
+    mn = fminf(mn, x);
+    nanm |= __ballot(x != x);
+  });
+  const float m = block_max<BLOCK>(mx, redf);
+  const float lo = -block_max<BLOCK>(-mn, redf);
+  if (lane == 0) redu[wv] = nanm != 0ull ? 1u : 0u;
+  __syncthreads();
+  bool bad = !__builtin_isfinite(m);
+  for (int w = 0; w < NW; ++w) bad = bad || redu[w] != 0u;
+
+  unsigned thr_key = 0;  // keep keys >= thr_key
+  bool any = false;
+  if (!bad && top_k > 0 && top_k < V) {
+    double need = top_k;
+    unsigned prefix = 0;
+    for (int bits = 0; bits < KB; bits += 8) {
+      for (int i = tid; i < 256; i += BLOCK) hist[i] = 0.0;
+      __syncthreads();
+      const int sh = KB - bits - 8;
+      for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
+        const unsigned k = order_key<DT>(x);
+        if (bits == 0 || (k >> (sh + 8)) == prefix) atomicAdd(&hist[(k >> sh) & 255u], 1.0);
+      });
+      __syncthreads();
+      if (wv == 0) walk_bins(hist, need, &sel_bin, &sel_need);
+      __syncthreads();
+      prefix = (prefix << 8) | static_cast<unsigned>(sel_bin);
+      need = sel_need;
+      __syncthreads();
+    }
+    thr_key = prefix;
+    any = true;
+  }
+  if (!bad && top_p < 1.0f) {
+    const unsigned lower = thr_key;
+    double need = -1.0;  // top_p * S once the first pass has S
+    unsigned prefix = 0;
+    for (int bits = 0; bits < KB; bits += 8) {
+      for (int i = tid; i < 256; i += BLOCK) hist[i] = 0.0;
+      __syncthreads();
+      const int sh = KB - bits - 8;
+      for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
+        const unsigned k = order_key<DT>(x);
+        if (k >= lower && (bits == 0 || (k >> (sh + 8)) == prefix)) {
+          const double e = exp64_scaled((static_cast<double>(x) - m) * yscale, tab);
+          if (e > 0.0) atomicAdd(&hist[(k >> sh) & 255u], e);
+        }
+      });
+      __syncthreads();
+      if (bits == 0) {  // S: the whole mass of the kept tokens
+        double ls = 0.0;
+        if (wv == 0)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ls = ls + hist[4 * lane + j];
+        const double S = wave_sum(ls);
+        need = static_cast<double>(top_p) * S;
+      }
+      if (wv == 0) walk_bins(hist, need, &sel_bin, &sel_need);
+      __syncthreads();
+      prefix = (prefix << 8) | static_cast<unsigned>(sel_bin);
+      need = sel_need;
+      __syncthreads();
+    }
+    thr_key = thr_key > prefix ? thr_key : prefix;
+    any = true;
+  }
+  float thr = -__builtin_huge_valf();
+  if (bad) {
+    thr = __builtin_nanf("");
+  } else if (any && thr_key > order_key<DT>(lo)) {
+    thr = key_value<DT>(thr_key);
+  }
+  if (tid == 0) thr_out[r] = thr;
+
+  // the output row (none when out is null): removed tokens as -inf, the rest
+  // copied when out != in
+  const bool cut = thr > -__builtin_huge_valf();  // false for NaN too
+  if (out == nullptr || (!cut && out == in)) return;
+  using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
+  constexpr Bits kNegInf = DT == kBF16 ? Bits(0xFF80u) : Bits(0xFF800000u);
+  const Bits* src = reinterpret_cast<const Bits*>(row);
+  Bits* dst = reinterpret_cast<Bits*>(orow);
+  const bool copy = out != in;
+  for (int i = tid; i < V; i += BLOCK) {
+    const Bits b = src[i];
+    const float z = DT == kBF16 ? __uint_as_float(static_cast<uint32_t>(b) << 16)
+                                : __uint_as_float(static_cast<uint32_t>(b));
+    if (cut && z < thr) {
+      dst[i] = kNegInf;
+    } else if (copy) {
+      dst[i] = b;
+    }
   }
 }
 

@@ -319,6 +319,35 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
   return launched();
 }
 
+int spec_filter(const void* logits, int dtype, int R, int V, float temperature, int top_k,
+                float top_p, float* thresholds, void* filtered, void* stream) {
+  if (R < 1) return SPEC_ERR_INVALID_ARG;
+  int rc = check_common(logits, logits, dtype, R, 1, V, temperature);
+  if (rc != SPEC_OK) return rc;
+  if (!thresholds || !aligned(thresholds, 4)) return SPEC_ERR_INVALID_ARG;
+  if (top_k < 0 || !(top_p > 0.0f) || std::isnan(top_p)) return SPEC_ERR_INVALID_ARG;
+  const int eb = elt_bytes(dtype);
+  if (filtered != nullptr && filtered != logits) {
+    if (!aligned(filtered, eb)) return SPEC_ERR_INVALID_ARG;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(logits), b = reinterpret_cast<uintptr_t>(filtered);
+    const uintptr_t n = static_cast<uintptr_t>(R) * static_cast<uintptr_t>(V) * eb;
+    if (a < b + n && b < a + n) return SPEC_ERR_INVALID_ARG;  // partial overlap
+  }
+  const int k = top_k >= V ? 0 : top_k;
+  const float p = top_p >= 1.0f ? 1.0f : top_p;
+  const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dtype == SPEC_DTYPE_BF16) {
+    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, filtered, V, yscale, k, p, thresholds);
+  } else {
+    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, filtered, V, yscale, k, p, thresholds);
+  }
+  return launched();
+}
+
 size_t spec_verify_workspace_size(int B, int K, int V, int dtype) {
   if (B < 1 || K < 1 || K > SPEC_MAX_K || V < 1 || V > SPEC_MAX_V) return 0;
   if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return 0;

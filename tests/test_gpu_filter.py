@@ -1,0 +1,219 @@
+"""GPU parity of the decoding transforms (spec_filter, through the C ABI)
+against the fp64 oracle on the same seeded bytes.
+
+The card's Method, "Decoding transforms", and Pitfalls: top-k and nucleus
+are applied alike to the target and draft rows before the verify.
+
+Thresholds: top-k is a pure order statistic of the stored values, so it must
+be bit-identical.  The nucleus threshold compares a sum of fp64 masses with
+top_p times the total; the kernel and the oracle add in different orders, so
+a threshold may differ only where the oracle's mass at the deciding value lies
+within 1e-9 of the total of top_p * S (counted, under 1e-3 of rows).  The
+filtered rows must be the input with exactly the tokens below the kernel's
+threshold set to -inf (bit-exact).  End to end, verify on the filtered rows
+follows the parity rule of the plain verify against oracle.verify_filtered.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from speculative_sampling_verification_softmax_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MASS_TOL = 1e-9
+MAX_NUCLEUS_FLAGGED = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X (torch.cuda.is_available() is False)")
+    from speculative_sampling_verification_softmax_amd import binding
+    binding.load()
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_logits(t: torch.Tensor) -> np.ndarray:
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def as_f64(h: np.ndarray) -> np.ndarray:
+    if h.dtype == np.uint16:
+        return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return h.astype(np.float64)
+
+
+def neg_inf_bits(h: np.ndarray):
+    return np.uint16(0xFF80) if h.dtype == np.uint16 else np.float32(-np.inf)
+
+
+def nucleus_margin(z: np.ndarray, T: float, top_k: int, top_p: float, v: float) -> float:
+    """|mass(z >= v) - top_p * S| / S over the top-k survivors, in fp64."""
+    keep = np.ones_like(z, bool)
+    if 0 < top_k < z.size:
+        keep = z >= np.sort(z)[::-1][top_k - 1]
+    e = np.where(keep, np.exp((z - z.max()) / T), 0.0)
+    S = e.sum()
+    return abs(e[z >= v].sum() - top_p * S) / S
+
+
+def check_filter(logits: torch.Tensor, T: float, top_k: int, top_p: float, label: str,
+                 rows=None, inplace=False):
+    """Thresholds against the oracle (on `rows`, or all) and the filtered rows
+    against the input masked at the kernel's own thresholds."""
+    from speculative_sampling_verification_softmax_amd import binding
+    V = logits.shape[-1]
+    R = logits.numel() // V
+    T32 = float(np.float32(T))
+    p32 = float(np.float32(top_p))
+    say(f"[filter] {label}: R={R} V={V} {logits.dtype} T={T32} top_k={top_k} top_p={p32} "
+        f"inplace={inplace} -> gpu")
+    before = host_logits(logits).reshape(R, V).copy()
+    src = logits.clone() if inplace else logits
+    out = binding.filter_rows(src, T, top_k, top_p, inplace=inplace)
+    torch.cuda.synchronize()
+    thr = out["thresholds"].reshape(-1).cpu().numpy().astype(np.float64)
+    got = host_logits(out["filtered"]).reshape(R, V)
+    rows = list(range(R)) if rows is None else list(rows)
+    flagged, checked, kept = 0, 0, []
+    for r in rows:
+        o = oracle.filter_threshold(before[r], T32, top_k=top_k, top_p=p32)
+        zr = as_f64(before[r])
+        kept.append(int((zr >= thr[r]).sum()))
+        checked += 1
+        if o is None:
+            assert np.isnan(thr[r]), f"{label}: row {r} should be invalid, got {thr[r]}"
+            assert got[r].tobytes() == before[r].tobytes(), f"{label}: invalid row {r} changed"
+            continue
+        if thr[r] != o:
+            hi = max(thr[r], o)
+            assert p32 < 1.0, f"{label}: row {r} top-k threshold {thr[r]} != {o}"
+            m = nucleus_margin(zr, T32, top_k, p32, hi)
+            assert m <= MASS_TOL, f"{label}: row {r} threshold {thr[r]} != {o} (margin {m:.3e})"
+            flagged += 1
+        # the rows: the input with exactly z < thr set to -inf
+        exp = before[r].copy()
+        if thr[r] > -np.inf:
+            exp[zr < thr[r]] = neg_inf_bits(before)
+        assert got[r].tobytes() == exp.tobytes(), f"{label}: row {r} filtered row differs"
+    assert flagged <= MAX_NUCLEUS_FLAGGED * max(checked, 1), f"{label}: {flagged} near-tie rows"
+    kept = np.asarray(kept)
+    say(f"[filter] {label}: {checked} rows checked, {flagged} near-tie thresholds, "
+        f"kept tokens min/median/max {kept.min()}/{int(np.median(kept))}/{kept.max()}")
+    return out
+
+
+def zipf_rows(R, V, dtype, seed, grid=None):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    ranks = torch.randperm(V, generator=g, device="cuda").to(torch.float32) + 1.0
+    z = 2.0 * torch.randn(R, V, device="cuda", generator=g) - 1.1 * torch.log(ranks)
+    if grid:
+        z = torch.round(z * grid) / grid  # coarse values: many exact ties
+    return z.to(torch.bfloat16) if dtype == "bf16" else z
+
+
+@pytest.mark.parametrize("top_k,top_p", [(50, 1.0), (0, 0.9), (40, 0.8), (1, 1.0), (0, 1e-6),
+                                         (1000, 0.95)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_thresholds_and_rows(dtype, top_k, top_p):
+    z = zipf_rows(48, 32000, dtype, seed=top_k + int(top_p * 100))
+    check_filter(z, 0.8, top_k, top_p, f"{dtype} k={top_k} p={top_p}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ties_on_a_coarse_grid(dtype):
+    z = zipf_rows(40, 5000, dtype, seed=7, grid=2)
+    for k, p in [(10, 1.0), (100, 1.0), (0, 0.5), (30, 0.7)]:
+        check_filter(z, 1.0, k, p, f"grid {dtype} k={k} p={p}")
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "f32"), (7, "bf16"), (63, "f32"), (1025, "bf16"),
+                                     (100003, "f32")])
+def test_ragged_rows_off_alignment(V, dtype):
+    R = 13
+    z = zipf_rows(R, V, dtype, seed=V)
+    big = torch.empty(R * V + 3, dtype=z.dtype, device="cuda")
+    view = big[3:].view(R, V)  # rows off 16-byte boundaries
+    view.copy_(z)
+    for k, p in [(min(5, V), 1.0), (0, 0.9), (3, 0.5)]:
+        check_filter(view, 1.3, k, p, f"V={V} {dtype} k={k} p={p}")
+
+
+def test_headline_rows_in_place_sampled():
+    """The full target and draft batch of the bf16 V=128256 workload, filtered
+    in place; thresholds checked on a sample of rows (the oracle sorts each)."""
+    inp = synth.make_inputs("headline", seed=5, device="cuda")
+    rows = inp["target"].reshape(-1, inp["target"].shape[-1])
+    sample = list(range(0, rows.shape[0], 97))
+    check_filter(rows, inp["T"], 50, 0.9, "headline target", rows=sample, inplace=True)
+
+
+def test_invalid_rows_and_trivial_parameters():
+    from speculative_sampling_verification_softmax_amd import binding
+    R, V = 6, 300
+    z = torch.randn(R, V, device="cuda")
+    z[1, 7] = float("nan")
+    z[2, :] = float("-inf")
+    z[3, ::2] = float("-inf")   # masked half: a top-k inside the finite half
+    z[4, :] = 0.0               # all equal: nothing removed by either transform
+    z[5, 11] = float("inf")
+    check_filter(z, 1.0, 20, 0.9, "invalid/masked")
+    # k >= V and p >= 1: nothing removed anywhere, rows copied
+    out = binding.filter_rows(z, 1.0, V, 1.0)
+    thr = out["thresholds"].cpu().numpy()
+    assert np.all(thr[[0, 3, 4]] == -np.inf) and np.all(np.isnan(thr[[1, 2, 5]]))
+    assert torch.equal(out["filtered"].view(torch.int32), z.view(torch.int32))
+    # thresholds only: no rows written
+    only = binding.filter_rows(z, 1.0, 20, 0.9, write_rows=False)
+    full = binding.filter_rows(z, 1.0, 20, 0.9)
+    assert only["filtered"] is None
+    np.testing.assert_array_equal(only["thresholds"].cpu().numpy(),
+                                  full["thresholds"].cpu().numpy())
+
+
+@pytest.mark.parametrize("wl,top_k,top_p", [("small", 40, 0.9), ("batch1", 0, 0.8),
+                                            ("tiny", 10, 1.0)])
+def test_verify_on_filtered_rows(wl, top_k, top_p):
+    """filter -> three-call verify on the filtered rows against the oracle's
+    verify_filtered, with the drafted tokens drawn (by the oracle) from the
+    filtered draft rows as step 1 of the method does."""
+    from speculative_sampling_verification_softmax_amd import binding
+    inp = synth.make_inputs(wl, seed=11, device="cuda", B=256 if wl == "tiny" else None)
+    host = synth.to_host_arrays(inp)
+    T32 = float(np.float32(inp["T"]))
+    p32 = float(np.float32(top_p))
+    B, K1, V = inp["target"].shape
+    K = K1 - 1
+    # draft tokens from the oracle's filtered draft rows
+    dh = host["draft"].reshape(B * K, V).copy()
+    zf = as_f64(dh)
+    for r in range(B * K):
+        t = oracle.filter_threshold(dh[r], T32, top_k=top_k, top_p=p32)
+        if t is not None and t > -np.inf:
+            dh[r][zf[r] < t] = neg_inf_bits(dh)
+    rng = np.random.default_rng(3)
+    u = (rng.integers(0, 1 << 24, size=B * K) * 2.0 ** -24).astype(np.float32)
+    tok = oracle.sample_rows(dh, u, T32)["tokens"].reshape(B, K).astype(np.int32)
+    tok = np.where(tok < 0, 0, tok).astype(np.int32)
+    host["tokens"] = tok
+    say(f"[filtered verify] {wl} B={B} K={K} V={V} k={top_k} p={p32} -> gpu filter + verify")
+    ft = binding.filter_rows(inp["target"], inp["T"], top_k, top_p)["filtered"]
+    fd = binding.filter_rows(inp["draft"], inp["T"], top_k, top_p)["filtered"]
+    g = parity.gpu_verify(dict(target=ft, draft=fd, tokens=torch.as_tensor(tok, device="cuda"),
+                               uniforms=inp["uniforms"], T=inp["T"]))
+    o = oracle.verify_filtered(host["target"], host["draft"], tok, host["uniforms"], T32,
+                               top_k=top_k, top_p=p32)
+    rep = parity.compare(g, o, inp["T"])
+    say(f"[filtered verify] {wl}: draws={rep['draws']} flagged={len(rep['flagged'])} "
+        f"failures={len(rep['failures'])} accept_hist={rep['accept_hist']}")
+    parity.assert_parity(rep, f"filtered {wl}")
