@@ -1082,22 +1082,40 @@ __global__ __launch_bounds__(kWave) void greedy_scan_kernel(const int32_t* __res
 
 // ==================================================================== filter
 //
-// Decoding transforms ("Decoding transforms"; Pitfalls: temperature, top-k
-// and nucleus applied alike to p and q before anything else): per row a
-// logit threshold thr, tokens below it removed (written as -inf into the
-// output rows; the other calls then run unchanged on them).
+// Decoding transforms (the card's Method, "Decoding transforms", and
+// Pitfalls: temperature, top-k and nucleus applied alike to p and q before
+// anything else): per row a logit threshold thr; tokens below it are removed
+// (written as -inf into the output rows, and the other calls then run
+// unchanged on them).
 //   top-k (0 < k < V): thr_k = the k-th largest stored logit, ties kept.
-//   nucleus (top_p < 1), over the top-k survivors: with e = exp((z - m)/T) in
-//     fp64, thr_p = the largest stored value v whose mass sum_{z >= v} e
-//     reaches top_p * sum e.
+//   nucleus (top_p < 1), over the top-k survivors: with masses
+//     e = exp((z - m)/T), thr_p = the largest stored value v whose mass
+//     sum_{z >= v} e reaches top_p * sum e.
 // Both are radix selects over an order-preserving integer key of the stored
-// value (16-bit for bf16, 32-bit for fp32), 8 bits per pass: each pass
-// re-reads the row, builds a 256-bin histogram in LDS (counts, or fp64
-// masses with ds_add_f64) of the tokens whose key matches the digits chosen
-// so far, and wave 0 walks the bins from the top to the one where the running
-// count (mass) reaches what is still needed.  Sort-free, exact, and slow: one
-// row read per pass (3 for bf16 top-k + nucleus, 9 for fp32), plus the fp64
-// exponentials of the nucleus passes.
+// value (16 bits for bf16, 32 for fp32), 8 bits per pass: a 256-bin
+// histogram in LDS (counts, or masses) of the values whose key matches the
+// digits chosen so far, and a walk from the top bin to the one where the
+// running total reaches what is still needed.
+//
+// The thresholds of real rows lie close to the row maximum, so after a first
+// pass for the maximum a second pass collects into LDS the values of a window
+// at the top of the row, and the selects run over those few values.  The
+// window is [L, m] with L the k-th largest of the per-thread maxima for top-k
+// (k <= block size: at least k values lie at or above it), and otherwise the
+// values within kFilterWindow powers of two of probability below the
+// maximum.  A row whose nucleus threshold lies below that window (or whose
+// window holds more than kFilterCap values) runs the selects over the whole
+// row instead, one row read per digit.
+//
+// Masses are fixed-point integers (units of 2^-42 of the maximum's mass), so
+// every sum is exact in any order and the kernel gives the same thresholds
+// on every run.  Masses inside the window are fp64 exponentials; the mass
+// below the window (needed only for the nucleus total without top-k) is a sum
+// of fp32 exp2 terms each below 2^-16, rounded once to the same units.
+
+constexpr int kFilterCap = 12288;
+constexpr float kFilterWindow = 16.0f;
+constexpr double kMassScale = 4398046511104.0;  // 2^42: V * 2^42 < 2^63 for V <= 2^20
 
 // Order-preserving key of a stored value; -0 is taken as +0 so that equal
 // values share a key.
@@ -1117,6 +1135,13 @@ __device__ __forceinline__ float key_value(unsigned k) {
   unsigned b = (k & kSign) ? (k & ~kSign) : (~k & kAll);
   if constexpr (DT == kBF16) b <<= 16;
   return __uint_as_float(b);
+}
+
+// Mass of one token in fixed point: round(exp((z - m)/T) * 2^42).
+__device__ __forceinline__ unsigned long long mass_fixed(float z, float m, double yscale,
+                                                         const double* tab) {
+  const double e = exp64_scaled((static_cast<double>(z) - m) * yscale, tab);
+  return static_cast<unsigned long long>(e * kMassScale + 0.5);
 }
 
 // f(x) for every stored value of a row (no padding), streaming the body with
@@ -1139,30 +1164,61 @@ __device__ __forceinline__ void for_each_value(const char* row, int V, F f) {
   if (tid < V - G.tail0) f(logit_f32<DT>(row, G.tail0 + tid));
 }
 
+// g(x) over a row in groups: x is a float array (one value for the head and
+// tail elements, VPG vectors for the body); every thread makes the same calls
+// and entries past the row are -inf.
+template <int BLOCK, int DT, int VPG, typename G>
+__device__ __forceinline__ void for_each_group(const char* row, int V, G g) {
+  constexpr int EPV = 16 / Elt<DT>::bytes;
+  const int tid = threadIdx.x;
+  const RowGeom<DT> Gm(row, V);
+  {
+    const float x[1] = {tid < Gm.head ? logit_f32<DT>(row, tid) : -__builtin_huge_valf()};
+    g(x);
+  }
+  stream_body<BLOCK, DT, VPG>(row + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes, Gm.nvec,
+                              [&](const float(&x)[VPG * EPV], int) { g(x); });
+  {
+    const float x[1] = {tid < V - Gm.tail0 ? logit_f32<DT>(row, Gm.tail0 + tid)
+                                           : -__builtin_huge_valf()};
+    g(x);
+  }
+}
+
+__device__ __forceinline__ unsigned wave_incl_scan_u32(unsigned v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const unsigned o = static_cast<unsigned>(__shfl_up(static_cast<int>(v), d, kWave));
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
 // Wave 0 walks hist[255..0] from the top: the first bin where the running
 // total reaches `need`.  Writes the bin to *bin_out and what is still needed
 // inside it (need minus the total above it) to *need_out.
-__device__ __forceinline__ void walk_bins(const double* hist, double need, int* bin_out,
-                                          double* need_out) {
+__device__ __forceinline__ void walk_bins(const unsigned long long* hist, double need,
+                                          int* bin_out, double* need_out) {
   const int lane = lane_id();
   double v[4];
   double ls = 0.0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {  // lane l holds bins 255-4l .. 252-4l, top first
-    v[j] = hist[255 - 4 * lane - j];
+    v[j] = static_cast<double>(hist[255 - 4 * lane - j]);
     ls = ls + v[j];
   }
   const double incl = wave_incl_scan(ls);
   const double excl = incl - ls;
   const unsigned long long hit = __ballot(incl >= need);
-  // rounding can leave the total a hair under `need`: then the lowest bin
-  // holding anything is taken
+  // rounding of the running total can leave it a hair under `need`: then the
+  // lowest bin holding anything is taken
   const int src = hit ? static_cast<int>(__builtin_ctzll(hit)) : -1;
   if (src < 0) {
     if (lane == 0) {
       int b = 0;
       for (int i = 0; i < 256; ++i)
-        if (hist[i] > 0.0) {
+        if (hist[i] != 0ull) {
           b = i;
           break;
         }
@@ -1189,25 +1245,165 @@ __device__ __forceinline__ void walk_bins(const double* hist, double need, int* 
   }
 }
 
+template <int BLOCK>
+struct FilterShared {
+  double tab[Exp64::kTab];
+  unsigned long long hist[256];
+  float redf[BLOCK / kWave];
+  double redd[BLOCK / kWave];
+  unsigned long long redq[BLOCK / kWave];
+  unsigned redu[BLOCK / kWave];
+  int sel_bin;
+  double sel_need;
+  unsigned ncand;
+  float cand[kFilterCap];
+};
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int BLOCK>
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v,
+                                                            unsigned long long* red) {
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  unsigned long long r = 0ull;
+#pragma unroll
+  for (int i = 0; i < BLOCK / kWave; ++i) r += red[i];
+  return r;
+}
+
+template <int BLOCK>
+__device__ __forceinline__ unsigned block_min_u32(unsigned v, unsigned* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned t = static_cast<unsigned>(__shfl_xor(static_cast<int>(v), o, kWave));
+    v = t < v ? t : v;
+  }
+  __syncthreads();
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  unsigned r = red[0];
+#pragma unroll
+  for (int i = 1; i < BLOCK / kWave; ++i) r = red[i] < r ? red[i] : r;
+  return r;
+}
+
+// Key (order_key) of the value at which the running total, from the top of
+// the values `fe` visits (fe(f) calls f(x) once per value), first reaches the
+// target: the count `target` (MASS false) or target * S in mass units (MASS
+// true; S < 0: S is the mass of the visited values with key >= lower).  Only
+// values with key >= lower take part.  Every visited key lies in
+// [base, base + 2^span_bits); the digits are those of key - base, 8 bits a
+// pass from the top, so values packed into a narrow key range still spread
+// over the bins of the first pass.
+template <int BLOCK, int DT, bool MASS, typename FE>
+__device__ __forceinline__ unsigned radix_select(FE fe, unsigned lower, double target, double S,
+                                                 float m, double yscale, unsigned base,
+                                                 int span_bits, FilterShared<BLOCK>& sh) {
+  const int tid = threadIdx.x, lane = lane_id();
+  double need = MASS ? target * S : target;
+  unsigned long long prefix = 0ull;
+  bool first = true;
+#pragma unroll 1
+  for (int hi = span_bits; hi > 0; hi -= 8) {
+    const int s = hi > 8 ? hi - 8 : 0;
+    for (int i = tid; i < 256; i += BLOCK) sh.hist[i] = 0ull;
+    __syncthreads();
+    fe([&](float x) {
+      const unsigned k = order_key<DT>(x);
+      const unsigned long long d = static_cast<unsigned long long>(k - base);
+      if (k >= lower && (d >> hi) == prefix)
+        atomicAdd(&sh.hist[static_cast<unsigned>(d >> s) & 255u],
+                  MASS ? mass_fixed(x, m, yscale, sh.tab) : 1ull);
+    });
+    __syncthreads();
+    if (tid < kWave) {
+      if (MASS && first && S < 0.0) {
+        double ls = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ls = ls + static_cast<double>(sh.hist[4 * lane + j]);
+        need = target * wave_sum(ls);
+      }
+      walk_bins(sh.hist, need, &sh.sel_bin, &sh.sel_need);
+    }
+    __syncthreads();
+    prefix = (prefix << (hi - s)) | static_cast<unsigned long long>(sh.sel_bin);
+    need = sh.sel_need;
+    first = false;
+  }
+  return base + static_cast<unsigned>(prefix);
+}
+
+// Output row: the input with every token below thr set to -inf (cut false:
+// a plain copy).  16-byte accesses where input and output rows share their
+// offset within 16 bytes.
+template <int BLOCK, int DT>
+__device__ __forceinline__ void write_filtered(const char* row, char* orow, int V, bool cut,
+                                               float thr) {
+  using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
+  constexpr Bits kNegInf = DT == kBF16 ? Bits(0xFF80u) : Bits(0xFF800000u);
+  constexpr int EB = Elt<DT>::bytes;
+  const int tid = threadIdx.x;
+  const Bits* src = reinterpret_cast<const Bits*>(row);
+  Bits* dst = reinterpret_cast<Bits*>(orow);
+  auto one = [&](Bits b) -> Bits {
+    const float z = DT == kBF16 ? __uint_as_float(static_cast<uint32_t>(b) << 16)
+                                : __uint_as_float(static_cast<uint32_t>(b));
+    return (cut && z < thr) ? kNegInf : b;
+  };
+  auto word = [&](uint32_t w) -> uint32_t {
+    if constexpr (DT == kBF16) {
+      const uint32_t lo = one(static_cast<Bits>(w & 0xFFFFu));
+      const uint32_t hi = one(static_cast<Bits>(w >> 16));
+      return lo | (hi << 16);
+    } else {
+      return one(w);
+    }
+  };
+  if (((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) != 0) {
+    for (int i = tid; i < V; i += BLOCK) dst[i] = one(src[i]);
+    return;
+  }
+  const RowGeom<DT> G(row, V);
+  if (tid < G.head) dst[tid] = one(src[tid]);
+  if (tid < V - G.tail0) dst[G.tail0 + tid] = one(src[G.tail0 + tid]);
+  const uint4* vs = reinterpret_cast<const uint4*>(row + static_cast<int64_t>(G.head) * EB);
+  uint4* vd = reinterpret_cast<uint4*>(orow + static_cast<int64_t>(G.head) * EB);
+  constexpr int U = 4;
+  int i = tid;
+  for (; i + (U - 1) * BLOCK < G.nvec; i += U * BLOCK) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = vs[i + u * BLOCK];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      vd[i + u * BLOCK] = make_uint4(word(v[u].x), word(v[u].y), word(v[u].z), word(v[u].w));
+  }
+  for (; i < G.nvec; i += BLOCK) {
+    const uint4 v = vs[i];
+    vd[i] = make_uint4(word(v.x), word(v.y), word(v.z), word(v.w));
+  }
+}
+
 template <int BLOCK, int DT, int VPG>
 __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out, int V,
-                                                       double yscale, int top_k, float top_p,
-                                                       float* __restrict__ thr_out) {
-  constexpr int KB = DT == kBF16 ? 16 : 32;  // key bits
+                                                       float c2, double yscale, int top_k,
+                                                       float top_p, float* thr_out) {
   constexpr int NW = BLOCK / kWave;
-  __shared__ double tab[Exp64::kTab];
-  __shared__ double hist[256];
-  __shared__ float redf[NW];
-  __shared__ unsigned redu[NW];
-  __shared__ int sel_bin;
-  __shared__ double sel_need;
+  __shared__ FilterShared<BLOCK> sh;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
   const int64_t r = blockIdx.x;
   const char* row = static_cast<const char*>(in) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
-  char* orow = static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
-  fill_exp2_table(tab);
+  fill_exp2_table(sh.tab);
+  if (tid == 0) sh.ncand = 0u;
 
-  // pass 0: max, min and NaN
+  // max, min and NaN
   float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
   unsigned long long nanm = 0;
   for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
@@ -1215,73 +1411,108 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     mn = fminf(mn, x);
     nanm |= __ballot(x != x);
   });
-  const float m = block_max<BLOCK>(mx, redf);
-  const float lo = -block_max<BLOCK>(-mn, redf);
-  if (lane == 0) redu[wv] = nanm != 0ull ? 1u : 0u;
+  const float m = block_max<BLOCK>(mx, sh.redf);
+  const float lo = -block_max<BLOCK>(-mn, sh.redf);
+  if (lane == 0) sh.redu[wv] = nanm != 0ull ? 1u : 0u;
   __syncthreads();
   bool bad = !__builtin_isfinite(m);
-  for (int w = 0; w < NW; ++w) bad = bad || redu[w] != 0u;
+  for (int w = 0; w < NW; ++w) bad = bad || sh.redu[w] != 0u;
 
-  unsigned thr_key = 0;  // keep keys >= thr_key
-  bool any = false;
-  if (!bad && top_k > 0 && top_k < V) {
-    double need = top_k;
-    unsigned prefix = 0;
-    for (int bits = 0; bits < KB; bits += 8) {
-      for (int i = tid; i < 256; i += BLOCK) hist[i] = 0.0;
-      __syncthreads();
-      const int sh = KB - bits - 8;
-      for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
-        const unsigned k = order_key<DT>(x);
-        if (bits == 0 || (k >> (sh + 8)) == prefix) atomicAdd(&hist[(k >> sh) & 255u], 1.0);
-      });
-      __syncthreads();
-      if (wv == 0) walk_bins(hist, need, &sel_bin, &sel_need);
-      __syncthreads();
-      prefix = (prefix << 8) | static_cast<unsigned>(sel_bin);
-      need = sel_need;
-      __syncthreads();
-    }
-    thr_key = prefix;
-    any = true;
+  const bool use_k = top_k > 0, use_p = top_p < 1.0f;
+  float zlo = m - kFilterWindow / c2;
+  unsigned thr_key = 0;
+  if (!bad && use_k && top_k <= BLOCK) {
+    // top-k window: the k-th largest of the per-thread maxima.  Those k
+    // maxima are k distinct values at or above it, so the window holds the
+    // top-k set whatever its depth.
+    sh.cand[tid] = mx;
+    __syncthreads();
+    auto fm = [&](auto f) { f(sh.cand[tid]); };
+    constexpr int KB = DT == kBF16 ? 16 : 32;
+    zlo = key_value<DT>(radix_select<BLOCK, DT, false>(fm, 0u, top_k, -1.0, m, yscale, 0u, KB, sh));
   }
-  if (!bad && top_p < 1.0f) {
-    const unsigned lower = thr_key;
-    double need = -1.0;  // top_p * S once the first pass has S
-    unsigned prefix = 0;
-    for (int bits = 0; bits < KB; bits += 8) {
-      for (int i = tid; i < 256; i += BLOCK) hist[i] = 0.0;
-      __syncthreads();
-      const int sh = KB - bits - 8;
-      for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
-        const unsigned k = order_key<DT>(x);
-        if (k >= lower && (bits == 0 || (k >> (sh + 8)) == prefix)) {
-          const double e = exp64_scaled((static_cast<double>(x) - m) * yscale, tab);
-          if (e > 0.0) atomicAdd(&hist[(k >> sh) & 255u], e);
-        }
-      });
-      __syncthreads();
-      if (bits == 0) {  // S: the whole mass of the kept tokens
-        double ls = 0.0;
-        if (wv == 0)
+  if (!bad && (use_k || use_p)) {
+    // the window: values >= zlo go to LDS (one slot range per wave and
+    // group, taken with one LDS atomic); for the nucleus without top-k the
+    // fp32 mass below the window is summed on the way
+    const bool masses = use_p && !use_k;
+    float rest = 0.0f;
+    for_each_group<BLOCK, DT, VPG>(row, V, [&](const auto& x) {
+      constexpr int N = sizeof(x) / sizeof(float);
+      unsigned c = 0u;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ls = ls + hist[4 * lane + j];
-        const double S = wave_sum(ls);
-        need = static_cast<double>(top_p) * S;
+      for (int e = 0; e < N; ++e) c += x[e] >= zlo ? 1u : 0u;
+      if (masses) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float t = __builtin_amdgcn_exp2f((x[e] - m) * c2);
+          rest += x[e] >= zlo ? 0.0f : t;
+        }
       }
-      if (wv == 0) walk_bins(hist, need, &sel_bin, &sel_need);
-      __syncthreads();
-      prefix = (prefix << 8) | static_cast<unsigned>(sel_bin);
-      need = sel_need;
-      __syncthreads();
+      if (__ballot(c != 0u) != 0ull) {
+        const unsigned incl = wave_incl_scan_u32(c);
+        const unsigned total =
+            static_cast<unsigned>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
+        unsigned base = 0u;
+        if (lane == 0) base = atomicAdd(&sh.ncand, total);
+        unsigned pos = uniform(base) + incl - c;
+#pragma unroll
+        for (int e = 0; e < N; ++e)
+          if (x[e] >= zlo) {
+            if (pos < static_cast<unsigned>(kFilterCap)) sh.cand[pos] = x[e];
+            ++pos;
+          }
+      }
+    });
+    const double rest_all = masses ? block_sum<BLOCK>(static_cast<double>(rest), sh.redd) : 0.0;
+    __syncthreads();
+    const unsigned n = sh.ncand;
+    const int nc = static_cast<int>(n);
+    auto fe = [&](auto f) {
+      for (int i = tid; i < nc; i += BLOCK) f(sh.cand[i]);
+    };
+    // the window's own mass, from the values in LDS (nucleus without top-k)
+    unsigned long long win = 0ull;
+    if (masses && n <= static_cast<unsigned>(kFilterCap))
+      fe([&](float x) { win += mass_fixed(x, m, yscale, sh.tab); });
+    const unsigned long long win_all = masses ? block_sum_u64<BLOCK>(win, sh.redq) : 0ull;
+    const double S = static_cast<double>(win_all) + rint(rest_all * kMassScale);
+    const bool fast = n <= static_cast<unsigned>(kFilterCap) &&
+                      (use_k ? static_cast<unsigned>(top_k) <= n
+                             : static_cast<double>(win_all) >= static_cast<double>(top_p) * S);
+    if (fast) {
+      // key range of the values in LDS: [kmin, key(m)]
+      unsigned kmin = 0xFFFFFFFFu;
+      fe([&](float x) {
+        const unsigned k = order_key<DT>(x);
+        kmin = k < kmin ? k : kmin;
+      });
+      kmin = block_min_u32<BLOCK>(kmin, sh.redu);
+      const unsigned span = order_key<DT>(m) - kmin;
+      const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
+      if (use_k)
+        thr_key = radix_select<BLOCK, DT, false>(fe, 0u, top_k, -1.0, m, yscale, kmin, bits, sh);
+      if (use_p) {
+        const unsigned kp = radix_select<BLOCK, DT, true>(fe, thr_key, top_p, use_k ? -1.0 : S, m,
+                                                          yscale, kmin, bits, sh);
+        thr_key = thr_key > kp ? thr_key : kp;
+      }
+    } else {
+      constexpr int KB = DT == kBF16 ? 16 : 32;
+      auto fr = [&](auto f) { for_each_value<BLOCK, DT, VPG>(row, V, f); };
+      if (use_k)
+        thr_key = radix_select<BLOCK, DT, false>(fr, 0u, top_k, -1.0, m, yscale, 0u, KB, sh);
+      if (use_p) {
+        const unsigned kp =
+            radix_select<BLOCK, DT, true>(fr, thr_key, top_p, -1.0, m, yscale, 0u, KB, sh);
+        thr_key = thr_key > kp ? thr_key : kp;
+      }
     }
-    thr_key = thr_key > prefix ? thr_key : prefix;
-    any = true;
   }
   float thr = -__builtin_huge_valf();
   if (bad) {
     thr = __builtin_nanf("");
-  } else if (any && thr_key > order_key<DT>(lo)) {
+  } else if ((use_k || use_p) && thr_key > order_key<DT>(lo)) {
     thr = key_value<DT>(thr_key);
   }
   if (tid == 0) thr_out[r] = thr;
@@ -1290,21 +1521,9 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   // copied when out != in
   const bool cut = thr > -__builtin_huge_valf();  // false for NaN too
   if (out == nullptr || (!cut && out == in)) return;
-  using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
-  constexpr Bits kNegInf = DT == kBF16 ? Bits(0xFF80u) : Bits(0xFF800000u);
-  const Bits* src = reinterpret_cast<const Bits*>(row);
-  Bits* dst = reinterpret_cast<Bits*>(orow);
-  const bool copy = out != in;
-  for (int i = tid; i < V; i += BLOCK) {
-    const Bits b = src[i];
-    const float z = DT == kBF16 ? __uint_as_float(static_cast<uint32_t>(b) << 16)
-                                : __uint_as_float(static_cast<uint32_t>(b));
-    if (cut && z < thr) {
-      dst[i] = kNegInf;
-    } else if (copy) {
-      dst[i] = b;
-    }
-  }
+  write_filtered<BLOCK, DT>(row,
+                            static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes,
+                            V, cut, thr);
 }
 
 // ==================================================================== fused

@@ -24,6 +24,12 @@ using spec::kF32;
 #ifndef SPEC_STATS_VPG_F32
 #define SPEC_STATS_VPG_F32 8
 #endif
+#ifndef SPEC_FILTER_VPG_BF16
+#define SPEC_FILTER_VPG_BF16 4
+#endif
+#ifndef SPEC_FILTER_VPG_F32
+#define SPEC_FILTER_VPG_F32 4
+#endif
 #ifndef SPEC_FUSED_VPG_BF16
 #define SPEC_FUSED_VPG_BF16 4
 #endif
@@ -335,15 +341,18 @@ int spec_filter(const void* logits, int dtype, int R, int V, float temperature, 
   }
   const int k = top_k >= V ? 0 : top_k;
   const float p = top_p >= 1.0f ? 1.0f : top_p;
+  const float c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
   const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), dim3(R),
-                       dim3(kStatsBlock), 0, s, logits, filtered, V, yscale, k, p, thresholds);
+    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kBF16, SPEC_FILTER_VPG_BF16>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
+                       thresholds);
   } else {
-    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>), dim3(R),
-                       dim3(kStatsBlock), 0, s, logits, filtered, V, yscale, k, p, thresholds);
+    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kF32, SPEC_FILTER_VPG_F32>), dim3(R),
+                       dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
+                       thresholds);
   }
   return launched();
 }
