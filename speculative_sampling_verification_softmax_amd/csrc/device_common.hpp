@@ -96,6 +96,46 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Sum over the 64 lanes without the LDS crossbar: an inclusive scan inside
+// each row of 16 lanes with DPP row shifts (lanes shifted in from outside the
+// row read 0), then the four row totals (lanes 15, 31, 47, 63) added in
+// order.  Fixed order; every lane gets the same bits.
+__device__ __forceinline__ double dpp_row_shr(double v, int ctrl_n) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  int rlo, rhi;
+  switch (ctrl_n) {  // dpp_ctrl must be a constant: row_shr:n is 0x110 + n
+    case 1:
+      rlo = __builtin_amdgcn_update_dpp(0, lo, 0x111, 0xf, 0xf, true);
+      rhi = __builtin_amdgcn_update_dpp(0, hi, 0x111, 0xf, 0xf, true);
+      break;
+    case 2:
+      rlo = __builtin_amdgcn_update_dpp(0, lo, 0x112, 0xf, 0xf, true);
+      rhi = __builtin_amdgcn_update_dpp(0, hi, 0x112, 0xf, 0xf, true);
+      break;
+    case 4:
+      rlo = __builtin_amdgcn_update_dpp(0, lo, 0x114, 0xf, 0xf, true);
+      rhi = __builtin_amdgcn_update_dpp(0, hi, 0x114, 0xf, 0xf, true);
+      break;
+    default:
+      rlo = __builtin_amdgcn_update_dpp(0, lo, 0x118, 0xf, 0xf, true);
+      rhi = __builtin_amdgcn_update_dpp(0, hi, 0x118, 0xf, 0xf, true);
+      break;
+  }
+  return __hiloint2double(rhi, rlo);
+}
+
+__device__ __forceinline__ double wave_sum_rows(double v) {
+  v = v + dpp_row_shr(v, 1);
+  v = v + dpp_row_shr(v, 2);
+  v = v + dpp_row_shr(v, 4);
+  v = v + dpp_row_shr(v, 8);
+  auto lane_val = [&](int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+  };
+  return ((lane_val(15) + lane_val(31)) + lane_val(47)) + lane_val(63);
+}
+
 // Inclusive prefix sum across the 64 lanes (Hillis-Steele order, fixed).
 __device__ __forceinline__ double wave_incl_scan(double v) {
   const int lane = lane_id();

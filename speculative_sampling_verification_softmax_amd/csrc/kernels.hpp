@@ -400,6 +400,7 @@ struct DrawRows {
   double yscale;      // (1/T) * 256/ln2
   double mq, mp;      // row maxima (exact stored logits)
   double sq_t, sp_t;  // fp32 normalisers from the stats (approximate)
+  const double* et;   // bf16 exponential tables in LDS (q row, then p row), or null
 };
 
 // The rows at position n of sequence b and their stats.  Returns false when a
@@ -422,6 +423,7 @@ __device__ __forceinline__ bool make_draw_rows(int64_t b, int n, int K, int V, c
   R.mp = resid ? mp : 0.0;
   R.sq_t = sq;
   R.sp_t = resid ? sp : 1.0;
+  R.et = nullptr;
   return row_ok(mq, sq) && (!resid || row_ok(mp, sp));
 }
 
@@ -430,6 +432,81 @@ __device__ __forceinline__ bool make_draw_rows(int64_t b, int n, int K, int V, c
 // magnitude of the logits, so the maximum gets exactly exp(0) = 1.
 __device__ __forceinline__ double tok_exp(float z, double yscale, double m, const double* tab) {
   return exp64_scaled((static_cast<double>(z) - m) * yscale, tab);
+}
+
+// bf16 rows hold few distinct values: every z with 2^-7 <= |z| < 2^6 is one
+// of 2 * 13 * 128 codes.  A workgroup that draws from a row can fill a table
+// of tok_exp over those codes once (kETab doubles per row: positive codes,
+// negative codes, then a 0 for -inf) and look tokens up instead of evaluating
+// the exponential; other values are computed.  The table holds tok_exp's own
+// results, so both ways give the same bits.
+constexpr unsigned kETabLo = 120u << 7;  // bf16 bits of 2^-7, sign cleared
+constexpr unsigned kETabN = 13u << 7;    // codes per sign: exponents 2^-7 .. 2^5
+constexpr int kETabZero = 2 * static_cast<int>(kETabN);
+constexpr int kETab = kETabZero + 2;  // doubles per row (even)
+
+template <int BLOCK>
+__device__ __forceinline__ void fill_row_exp_table(double* et, double yscale, double m,
+                                                   const double* tab) {
+  for (int j = threadIdx.x; j < kETab; j += BLOCK) {
+    if (j >= kETabZero) {
+      et[j] = 0.0;
+      continue;
+    }
+    const unsigned code = (kETabLo + static_cast<unsigned>(j) % kETabN) |
+                          (static_cast<unsigned>(j) >= kETabN ? 0x8000u : 0u);
+    et[j] = tok_exp(__uint_as_float(code << 16), yscale, m, tab);
+  }
+}
+
+// e(x) of a token of the q row (P false) or the p row (P true) of R.  With
+// the tables (ET), every lane reads one entry (the zero slot for -inf and
+// for codes outside the table), and a wave computes the exponential only
+// when one of its lanes holds such a code.
+template <int DT, bool ET, bool P>
+__device__ __forceinline__ double row_exp(const DrawRows& R, float z, const double* tab) {
+  if constexpr (DT == kBF16 && ET) {
+    const unsigned b = __float_as_uint(z) >> 16;
+    const unsigned i = (b & 0x7FFFu) - kETabLo;
+    const bool in = i < kETabN;
+    const int idx = in ? static_cast<int>((b >> 15) * kETabN + i) : kETabZero;
+    double e = R.et[(P ? kETab : 0) + idx];
+    const bool other = !in && b != 0xFF80u;
+    if (__builtin_amdgcn_ballot_w64(other) != 0ull) {
+      if (other) e = tok_exp(z, R.yscale, P ? R.mp : R.mq, tab);
+    }
+    return e;
+  }
+  return tok_exp(z, R.yscale, P ? R.mp : R.mq, tab);
+}
+
+// row_exp for H tokens of one row at once: the table reads are issued
+// together, then one wave-level test covers all H for the computed codes.
+template <int DT, bool ET, bool P, int H>
+__device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, const double* tab,
+                                          double (&e)[H]) {
+  if constexpr (DT == kBF16 && ET) {
+    bool other[H];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const unsigned b = __float_as_uint(z[k]) >> 16;
+      const unsigned i = (b & 0x7FFFu) - kETabLo;
+      const bool in = i < kETabN;
+      const int idx = in ? static_cast<int>((b >> 15) * kETabN + i) : kETabZero;
+      e[k] = R.et[(P ? kETab : 0) + idx];
+      other[k] = !in && b != 0xFF80u;
+      any = any || other[k];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
+#pragma unroll
+      for (int k = 0; k < H; ++k)
+        if (other[k]) e[k] = tok_exp(z[k], R.yscale, P ? R.mp : R.mq, tab);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < H; ++k) e[k] = tok_exp(z[k], R.yscale, P ? R.mp : R.mq, tab);
+  }
 }
 
 // Raw 16-byte groups of one lane for one chunk (q row, and p row for a residual).
@@ -474,7 +551,7 @@ __device__ __forceinline__ void chunk_values(const DrawRows& R, int c, bool full
 }
 
 // Exact weights of this lane's E tokens (used to re-derive the chosen chunk).
-template <int DT, int MODE>
+template <int DT, int MODE, bool ET = false>
 __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq, double ip,
                                              const double* tab,
                                              double (&w)[16 / Elt<DT>::bytes]) {
@@ -486,9 +563,9 @@ __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq
   chunk_values<DT, MODE>(R, c, full, raw, zq, zp);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
+    const double eq = row_exp<DT, ET, false>(R, zq[e], tab);
     if (MODE == kModeResidual) {
-      const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
+      const double ep = row_exp<DT, ET, true>(R, zp[e], tab);
       const double d = eq * iq - ep * ip;
       w[e] = d > 0.0 ? d : 0.0;
     } else {
@@ -506,21 +583,27 @@ struct ChunkSums {
 
 // Fast-path arithmetic of one chunk from its values.  Adds every token's e_q,
 // e_p to the lane's lsq, lsp.
-template <int DT, int MODE>
+template <int DT, int MODE, bool ET = false>
 __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
                                            const float (&zq)[16 / Elt<DT>::bytes],
                                            const float (&zp)[16 / Elt<DT>::bytes],
                                            const double* tab, double& lsq, double& lsp,
                                            ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
+  constexpr int H = E < 4 ? E : 4;  // tokens whose exponentials are formed together
   double a = 0.0, bb = 0.0;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
+  double eqh[H], eph[H];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const double eq = tok_exp(zq[e], R.yscale, R.mq, tab);
+    if (e % H == 0) {
+      row_exp_n<DT, ET, false, H>(R, zq + e, tab, eqh);
+      if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, eph);
+    }
+    const double eq = eqh[e % H];
     lsq = lsq + eq;
     if (MODE == kModeResidual) {
-      const double ep = tok_exp(zp[e], R.yscale, R.mp, tab);
+      const double ep = eph[e % H];
       lsp = lsp + ep;
       const double r = ep * R.sq_t;
       const double d = fma(eq, R.sp_t, -r);  // e_q s~_p - e_p s~_q
@@ -536,8 +619,8 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
       a = a + eq;
     }
   }
-  out.A = wave_sum(a);
-  out.Bv = MODE == kModeResidual ? wave_sum(bb) : 0.0;
+  out.A = wave_sum_rows(a);
+  out.Bv = MODE == kModeResidual ? wave_sum_rows(bb) : 0.0;
   out.n_unc = 0;
 #pragma unroll
   for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
@@ -562,7 +645,7 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
 // One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
 // flight (a slot is refilled as soon as its chunk has been unpacked);
 // emit(c, sums) stores a chunk's results.
-template <int DT, int MODE, int PF, typename Emit>
+template <int DT, int MODE, int PF, bool ET = false, typename Emit>
 __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, int stride,
                                            const double* tab, double& lsq, double& lsp,
                                            Emit emit) {
@@ -586,7 +669,7 @@ __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, in
         full[j] = cn < c1 && chunk_full<DT>(R, cn);
         if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
         ChunkSums cs;
-        chunk_sums<DT, MODE>(R, c, zq, zp, tab, lsq, lsp, cs);
+        chunk_sums<DT, MODE, ET>(R, c, zq, zp, tab, lsq, lsp, cs);
         emit(c, cs);
       }
     }
@@ -652,14 +735,14 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
 }
 
 // Token inside chunk c (wave 0): returns the token id in every lane, or -1.
-template <int DT, int MODE>
+template <int DT, int MODE, bool ET = false>
 __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool crossing, double excl,
                                              double target, double iq, double ip,
                                              const double* tab) {
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
   double w[E];
-  lane_weights<DT, MODE>(R, c, iq, ip, tab, w);
+  lane_weights<DT, MODE, ET>(R, c, iq, ip, tab, w);
   double ls = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ls = ls + w[e];
@@ -703,7 +786,7 @@ struct DrawShared {
 
 // Exact two-sweep draw (whole block).  W: nch doubles of scratch.  Returns the
 // token (every thread), or -1 when no token carries positive weight.
-template <int BLOCK, int DT>
+template <int BLOCK, int DT, bool ET = false>
 __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh) {
   constexpr int NW = BLOCK / kWave;
   constexpr int E = 16 / Elt<DT>::bytes;
@@ -719,8 +802,8 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
       chunk_values<DT, kModeResidual>(R, c, full, raw, zq, zp);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        aq = aq + tok_exp(zq[e], R.yscale, R.mq, sh.tab);
-        ap = ap + tok_exp(zp[e], R.yscale, R.mp, sh.tab);
+        aq = aq + row_exp<DT, ET, false>(R, zq[e], sh.tab);
+        ap = ap + row_exp<DT, ET, true>(R, zp[e], sh.tab);
       }
     }
     const double Sq = block_sum<BLOCK>(aq, sh.red);
@@ -732,9 +815,9 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
     for (int c = wv; c < nch; c += NW) {
       double w[E];
       if (R.mode == kModeResidual)
-        lane_weights<DT, kModeResidual>(R, c, iq, ip, sh.tab, w);
+        lane_weights<DT, kModeResidual, ET>(R, c, iq, ip, sh.tab, w);
       else
-        lane_weights<DT, kModeBonus>(R, c, iq, ip, sh.tab, w);
+        lane_weights<DT, kModeBonus, ET>(R, c, iq, ip, sh.tab, w);
       double ls = 0.0;
 #pragma unroll
       for (int e = 0; e < E; ++e) ls = ls + w[e];
@@ -755,10 +838,10 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
     tok = R.mode == kModeResidual
-              ? draw_in_chunk<DT, kModeResidual>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                                 sh.seld[1], iq, ip, sh.tab)
-              : draw_in_chunk<DT, kModeBonus>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                              sh.seld[1], iq, ip, sh.tab);
+              ? draw_in_chunk<DT, kModeResidual, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                     sh.seld[1], iq, ip, sh.tab)
+              : draw_in_chunk<DT, kModeBonus, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                  sh.seld[1], iq, ip, sh.tab);
   if (tid == 0) sh.sel[2] = tok;
   __syncthreads();
   tok = sh.sel[2];
@@ -772,7 +855,7 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 // workgroup's own memory; it may be A itself when XB is false) receives the
 // chunk totals W_c.  Returns the token, -1 (nothing to draw) or -2 (take the
 // slow path).
-template <int BLOCK, int DT, bool XB>
+template <int BLOCK, int DT, bool XB, bool ET = false>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
                            double* W, double u, DrawShared<BLOCK>& sh) {
@@ -795,8 +878,8 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 #pragma unroll
       for (int j = 0; j < kUncMax; ++j) {
         if (j < nu) {
-          const double eq = tok_exp(logit_f32<DT>(R.qrow, x[j]), R.yscale, R.mq, sh.tab);
-          const double ep = tok_exp(logit_f32<DT>(R.prow, x[j]), R.yscale, R.mp, sh.tab);
+          const double eq = row_exp<DT, ET, false>(R, logit_f32<DT>(R.qrow, x[j]), sh.tab);
+          const double ep = row_exp<DT, ET, true>(R, logit_f32<DT>(R.prow, x[j]), sh.tab);
           const double d = eq * iq - ep * ip;
           w = w + (d > 0.0 ? d : 0.0);
         }
@@ -823,10 +906,10 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
     tok = R.mode == kModeResidual
-              ? draw_in_chunk<DT, kModeResidual>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                                 sh.seld[1], iq, ip, sh.tab)
-              : draw_in_chunk<DT, kModeBonus>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                              sh.seld[1], iq, ip, sh.tab);
+              ? draw_in_chunk<DT, kModeResidual, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                     sh.seld[1], iq, ip, sh.tab)
+              : draw_in_chunk<DT, kModeBonus, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                  sh.seld[1], iq, ip, sh.tab);
   if (tid == 0) sh.sel[2] = tok;
   __syncthreads();
   tok = sh.sel[2];
@@ -839,7 +922,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 // nch ints; unc_idx: nch*kUncMax ints), else or on its failure the exact
 // two-sweep path (dyn: nch doubles).  sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
-template <int BLOCK, int DT>
+template <int BLOCK, int DT, bool ET = false>
 __device__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
                           DrawShared<BLOCK>& sh) {
   constexpr int E = 16 / Elt<DT>::bytes;
@@ -863,16 +946,16 @@ __device__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
       }
     };
     if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeResidual, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     else
-      wave_sweep<DT, kModeBonus, 1>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeBonus, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     const double Sq = block_sum<BLOCK>(lsq, sh.red);
     const double Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false>(
+    tok = fast_finish<BLOCK, DT, false, ET>(
         R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
         Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
   }
-  if (tok == -2) tok = slow_draw<BLOCK, DT>(R, nch, dyn, u, sh);
+  if (tok == -2) tok = slow_draw<BLOCK, DT, ET>(R, nch, dyn, u, sh);
   return tok;
 }
 
@@ -884,7 +967,7 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
     const void* __restrict__ tgt, const void* __restrict__ dft,
     const float* __restrict__ uni, const float* __restrict__ tstats,
     const float* __restrict__ dstats, const int32_t* __restrict__ nacc, int K, int V,
-    double yscale, int fast, int32_t* __restrict__ out_tokens,
+    double yscale, int fast, int etab, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ num_emitted) {
   constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int NW = BLOCK / kWave;
@@ -910,7 +993,16 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
   }
   fill_exp2_table(sh.tab);
   __syncthreads();
-  const int tok = draw_block<BLOCK, DT>(R, uni[b * K1 + K], fast, dyn, sh);
+  double* work = dyn;
+  if (DT == kBF16 && etab) {  // dynamic LDS starts with the two rows' tables
+    fill_row_exp_table<BLOCK>(dyn, R.yscale, R.mq, sh.tab);
+    if (R.mode == kModeResidual) fill_row_exp_table<BLOCK>(dyn + kETab, R.yscale, R.mp, sh.tab);
+    __syncthreads();
+    R.et = dyn;
+    work = dyn + 2 * kETab;
+  }
+  const int tok = R.et != nullptr ? draw_block<BLOCK, DT, true>(R, uni[b * K1 + K], fast, work, sh)
+                                  : draw_block<BLOCK, DT, false>(R, uni[b * K1 + K], fast, work, sh);
   if (tid == 0) {
     out_tokens[b * K1 + n] = tok;
     if (num_emitted) num_emitted[b] = tok >= 0 ? n + 1 : 0;
@@ -929,7 +1021,7 @@ template <int BLOCK, int DT>
 __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ logits,
                                                        const float* __restrict__ stats,
                                                        const float* __restrict__ uni, int V,
-                                                       double yscale, int fast,
+                                                       double yscale, int fast, int etab,
                                                        int32_t* __restrict__ tokens) {
   extern __shared__ double dyn[];
   __shared__ DrawShared<BLOCK> sh;
@@ -950,9 +1042,18 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
   R.mp = 0.0;
   R.sq_t = s;
   R.sp_t = 1.0;
+  R.et = nullptr;
   fill_exp2_table(sh.tab);
   __syncthreads();
-  const int tok = draw_block<BLOCK, DT>(R, uni[r], fast, dyn, sh);
+  double* work = dyn;
+  if (DT == kBF16 && etab) {  // dynamic LDS starts with the row's table
+    fill_row_exp_table<BLOCK>(dyn, R.yscale, R.mq, sh.tab);
+    __syncthreads();
+    R.et = dyn;
+    work = dyn + kETab;
+  }
+  const int tok = R.et != nullptr ? draw_block<BLOCK, DT, true>(R, uni[r], fast, work, sh)
+                                  : draw_block<BLOCK, DT, false>(R, uni[r], fast, work, sh);
   if (threadIdx.x == 0) tokens[r] = tok;
 }
 

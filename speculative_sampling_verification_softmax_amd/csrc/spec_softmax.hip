@@ -44,6 +44,29 @@ constexpr int kFusedNW = kFusedBlock / spec::kWave;
 constexpr size_t kFusedMaxDynLds = static_cast<size_t>(SPEC_MAX_V / 64 / 4) * sizeof(double);
 // LDS the one-workgroup residual kernel may take for its fast-path arrays.
 constexpr size_t kResidFastLds = 48 * 1024;
+// Dynamic LDS of a draw workgroup in all (the static part is ~2.3 KB; the
+// total stays within 64 KB).
+constexpr size_t kDrawDynLds = 60 * 1024;
+
+// Dynamic LDS of the residual / sample kernels: the fast-path arrays (or the
+// slow path's nch doubles), preceded by `rows` bf16 exponential tables when
+// they fit.
+struct DrawLds {
+  int fast, etab;
+  size_t bytes;
+};
+
+DrawLds draw_lds(int nch, int dtype, int rows) {
+  DrawLds d{};
+  const size_t fast_lds = static_cast<size_t>(nch) *
+                          (2 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
+  d.fast = fast_lds <= kResidFastLds ? 1 : 0;
+  const size_t work = d.fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
+  const size_t tables = static_cast<size_t>(rows) * spec::kETab * sizeof(double);
+  d.etab = (dtype == SPEC_DTYPE_BF16 && work + tables <= kDrawDynLds) ? 1 : 0;
+  d.bytes = work + (d.etab ? tables : 0);
+  return d;
+}
 
 int elt_bytes(int dtype) { return dtype == SPEC_DTYPE_F32 ? 4 : 2; }
 
@@ -238,21 +261,17 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
     return SPEC_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
-  const int nch = num_chunks(V, dtype);
-  const size_t fast_lds = static_cast<size_t>(nch) *
-                          (2 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
-  const int fast = fast_lds <= kResidFastLds ? 1 : 0;
-  const size_t lds = fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
+  const DrawLds d = draw_lds(num_chunks(V, dtype), dtype, 2);
   (void)hipGetLastError();
   const dim3 grid(static_cast<unsigned>(B)), block(kResidBlock);
   if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::residual_kernel<kResidBlock, kBF16>), grid, block, lds, s,
+    hipLaunchKernelGGL((spec::residual_kernel<kResidBlock, kBF16>), grid, block, d.bytes, s,
                        target_logits, draft_logits, uniforms, target_stats, draft_stats,
-                       num_accepted, K, V, yscale, fast, out_tokens, num_emitted);
+                       num_accepted, K, V, yscale, d.fast, d.etab, out_tokens, num_emitted);
   } else {
-    hipLaunchKernelGGL((spec::residual_kernel<kResidBlock, kF32>), grid, block, lds, s,
+    hipLaunchKernelGGL((spec::residual_kernel<kResidBlock, kF32>), grid, block, d.bytes, s,
                        target_logits, draft_logits, uniforms, target_stats, draft_stats,
-                       num_accepted, K, V, yscale, fast, out_tokens, num_emitted);
+                       num_accepted, K, V, yscale, d.fast, d.etab, out_tokens, num_emitted);
   }
   return launched();
 }
@@ -298,11 +317,7 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
   const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
-  const int nch = num_chunks(V, dtype);
-  const size_t fast_lds = static_cast<size_t>(nch) *
-                          (2 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
-  const int fast = fast_lds <= kResidFastLds ? 1 : 0;
-  const size_t lds = fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
+  const DrawLds d = draw_lds(num_chunks(V, dtype), dtype, 1);
   (void)hipGetLastError();
   if (dtype == SPEC_DTYPE_BF16) {
     hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), dim3(R),
@@ -316,11 +331,11 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
   rc = launched();
   if (rc != SPEC_OK) return rc;
   if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kBF16>), dim3(R), dim3(kResidBlock), lds,
-                       s, logits, row_stats, uniforms, V, yscale, fast, tokens);
+    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kBF16>), dim3(R), dim3(kResidBlock),
+                       d.bytes, s, logits, row_stats, uniforms, V, yscale, d.fast, d.etab, tokens);
   } else {
-    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kF32>), dim3(R), dim3(kResidBlock), lds,
-                       s, logits, row_stats, uniforms, V, yscale, fast, tokens);
+    hipLaunchKernelGGL((spec::sample_kernel<kResidBlock, kF32>), dim3(R), dim3(kResidBlock),
+                       d.bytes, s, logits, row_stats, uniforms, V, yscale, d.fast, d.etab, tokens);
   }
   return launched();
 }
