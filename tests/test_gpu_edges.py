@@ -226,3 +226,49 @@ def test_binding_rejects_bad_tensors():
         binding.softmax_stats(inp["target"], inp["draft"], 0.0)
     with pytest.raises(TypeError):
         binding.softmax_stats(inp["target"].double(), inp["draft"].double(), 1.0)
+
+
+BOUNDARY_BF16 = [0x3C00, 0xBC00,   # +-2^-7: the first codes the residual kernel tabulates
+                 0x3BFF, 0xBBFF,   # just below 2^-7 in magnitude: computed
+                 0x427F, 0xC27F,   # +-63.75: the last tabulated codes
+                 0x4280, 0xC280,   # +-64: computed
+                 0x3B80, 0x0000, 0x8000, 0x0001, 0x8001,  # 2^-8, +-0, denormals
+                 0x42C8, 0xC2C8,   # +-100
+                 0xFF80]           # -inf
+
+
+@pytest.mark.parametrize("T", [1.0, 20.0])
+def test_bf16_table_boundary_codes(T):
+    """bf16 rows made of the codes at and around the edges of the draw
+    kernels' exponential table (2^-7 <= |z| < 2^6), -inf, zeros and
+    denormals: the three-call path (tabulated), the fused path (computed)
+    and the draft sampler all against the oracle."""
+    rng = np.random.default_rng(int(T))
+    B, K, V = 64, 3, 700
+    codes = np.array(BOUNDARY_BF16, np.uint32)
+
+    def rows(shape):
+        pick = codes[rng.integers(0, len(codes), shape)]
+        z = (pick << 16).view(np.float32).copy()
+        # a random third of the entries plain values, so rows differ
+        plain = rng.random(shape) < 0.3
+        z[plain] = rng.uniform(-8, 8, plain.sum()).astype(np.float32)
+        return z
+
+    tgt = rows((B, K + 1, V))
+    dft = rows((B, K, V))
+    tgt[:, :, 0] = 1.0  # every row has a finite maximum
+    dft[:, :, 0] = 1.0
+    tok = _tokens_from(rng, np.ascontiguousarray(
+        (np.asarray(torch.from_numpy(dft).to(torch.bfloat16).float()))), float(np.float32(T)))
+    inp = _to_dev(tgt, dft, tok, _uni(rng, B, K), T, dtype="bf16")
+    _check(inp, f"bf16 table edges T={T}")
+    # the sampler on the draft rows
+    rows_dev = inp["draft"].reshape(B * K, V)
+    u = torch.from_numpy((rng.integers(0, 1 << 24, B * K) * 2.0 ** -24).astype(np.float32)).cuda()
+    got = binding.sample(rows_dev, u, T)["tokens"].cpu().numpy()
+    lh = rows_dev.cpu().view(torch.int16).numpy().view(np.uint16)
+    o = oracle.sample_rows(lh, u.cpu().numpy(), float(np.float32(T)))
+    bad = [(r, int(got[r]), int(o["tokens"][r])) for r in range(B * K)
+           if got[r] != o["tokens"][r] and not (o["dist"][r] < parity.BOUNDARY)]
+    assert bad == [], bad[:5]
