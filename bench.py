@@ -127,7 +127,8 @@ def _pmc_kernels(path: str) -> dict:
 
 def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
-    fetch, write = f("fetch"), f("write")
+    suffix = "" if path == "three_call" else "_" + path  # pass directories: fetch, fetch_fused, ...
+    fetch, write = f("fetch" + suffix), f("write" + suffix)
     copy_bytes = COPY_MIB << 20
     def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)
         v = [x for k, xs in f(sub).items() if "copyBuffer" in k for x in xs]

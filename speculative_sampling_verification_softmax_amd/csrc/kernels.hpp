@@ -929,8 +929,8 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 // two-sweep path (dyn: nch doubles).  sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
 template <int BLOCK, int DT, bool ET = false>
-__device__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
-                          DrawShared<BLOCK>& sh) {
+__device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
+                                          DrawShared<BLOCK>& sh) {
   constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int NW = BLOCK / kWave;
   const int wv = threadIdx.x / kWave, lane = lane_id();
