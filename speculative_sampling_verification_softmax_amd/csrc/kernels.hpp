@@ -1480,22 +1480,28 @@ __device__ __forceinline__ void write_filtered(const char* row, char* orow, int 
   const RowGeom<DT> G(row, V);
   if (tid < G.head) dst[tid] = one(src[tid]);
   if (tid < V - G.tail0) dst[G.tail0 + tid] = one(src[G.tail0 + tid]);
-  const uint4* vs = reinterpret_cast<const uint4*>(row + static_cast<int64_t>(G.head) * EB);
-  uint4* vd = reinterpret_cast<uint4*>(orow + static_cast<int64_t>(G.head) * EB);
+  // the row's last read and the output's only write: non-temporal both
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u* vs = reinterpret_cast<const v4u*>(row + static_cast<int64_t>(G.head) * EB);
+  v4u* vd = reinterpret_cast<v4u*>(orow + static_cast<int64_t>(G.head) * EB);
+  auto conv = [&](v4u v) {
+    v4u o;
+    o.x = word(v.x);
+    o.y = word(v.y);
+    o.z = word(v.z);
+    o.w = word(v.w);
+    return o;
+  };
   constexpr int U = 4;
   int i = tid;
   for (; i + (U - 1) * BLOCK < G.nvec; i += U * BLOCK) {
-    uint4 v[U];
+    v4u v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = vs[i + u * BLOCK];
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&vs[i + u * BLOCK]);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      vd[i + u * BLOCK] = make_uint4(word(v[u].x), word(v[u].y), word(v[u].z), word(v[u].w));
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(conv(v[u]), &vd[i + u * BLOCK]);
   }
-  for (; i < G.nvec; i += BLOCK) {
-    const uint4 v = vs[i];
-    vd[i] = make_uint4(word(v.x), word(v.y), word(v.z), word(v.w));
-  }
+  for (; i < G.nvec; i += BLOCK) __builtin_nontemporal_store(conv(__builtin_nontemporal_load(&vs[i])), &vd[i]);
 }
 
 template <int BLOCK, int DT, int VPG>
