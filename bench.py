@@ -127,7 +127,7 @@ def _pmc_kernels(path: str) -> dict:
 
 def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
-    suffix = "" if path == "three_call" else "_" + path  # pass directories: fetch, fetch_fused, ...
+    suffix = "" if path == "three_call" else "_" + path  # pass directories: fetch, fetch_two_call, ...
     fetch, write = f("fetch" + suffix), f("write" + suffix)
     copy_bytes = COPY_MIB << 20
     def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)
@@ -138,8 +138,8 @@ def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     kf = copy_bytes / (cf * 1024)
     kw = copy_bytes / (cw * 1024)
     wl = synth.WORKLOADS[workload]
-    dom = "stats_kernel" if path == "three_call" else "fused_kernel"
-    alg = stats_bytes(wl) if path == "three_call" else step_bytes(wl)
+    dom = "fused_kernel" if path == "fused" else "stats_kernel"
+    alg = step_bytes(wl) if path == "fused" else stats_bytes(wl)
     lines = [f"# HBM traffic per launch: {path} path, {workload} workload "
              f"(B={wl.B}, K={wl.K}, V={wl.V}, {wl.dtype}, T={wl.T})", "",
              "Commands (one MI355X, from the repository root; each pass is a run of its own):", "",
@@ -405,9 +405,10 @@ def main() -> int:
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
     ap.add_argument("--top-k", type=int, default=50, help="top-k for --mode filter (0: off)")
     ap.add_argument("--top-p", type=float, default=0.9, help="nucleus top_p for --mode filter")
-    ap.add_argument("--path", default="three_call", choices=["three_call", "fused"],
-                    help="fused: spec_verify_fused (one launch); three_call: spec_softmax_stats, "
-                         "spec_verify, spec_residual_sample")
+    ap.add_argument("--path", default="two_call", choices=["three_call", "two_call", "fused"],
+                    help="three_call: spec_softmax_stats, spec_verify, spec_residual_sample; "
+                         "two_call: spec_softmax_stats, spec_verify_sample; "
+                         "fused: spec_verify_fused (one launch)")
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences in the CPU oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -488,7 +489,16 @@ def main() -> int:
         binding.verify(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, stream=stream)
         binding.residual_sample(tgt, dft, uni, ts, ds, nacc, T, out, nemit, stream=stream)
 
-    step = step_fused if args.path == "fused" else step_three
+    def step_two(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.softmax_stats(tgt, dft, T, ts, ds, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.verify_sample(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, nemit,
+                              stream=stream)
+
+    step = {"fused": step_fused, "two_call": step_two, "three_call": step_three}[args.path]
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):

@@ -136,6 +136,22 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
                          int32_t* out_tokens, int32_t* num_emitted, void* stream);
 
 /*
+ * spec_verify_sample -- spec_verify and spec_residual_sample in one launch
+ * (alg. 2 steps 2-4, sec. 4.2 and the Pitfalls readings cited above): one
+ * workgroup per sequence runs the accept tests and the first-rejection scan,
+ * then draws the final token.  Same inputs and outputs, and the same results,
+ * as spec_verify followed by spec_residual_sample on the stats of
+ * spec_softmax_stats; it saves one launch and the dependency between them.
+ *   probs, num_emitted   optional outputs (NULL to skip)
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
+ */
+int spec_verify_sample(const void* target_logits, const void* draft_logits, int dtype,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const float* target_stats, const float* draft_stats, int B, int K, int V,
+                       float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                       float* probs, int32_t* num_emitted, void* stream);
+
+/*
  * spec_greedy_verify -- greedy mode.  The card's Pitfalls (greedy mode) infer
  * the rule from the general one applied to one-hot distributions: q_t is
  * one-hot at a_t = argmax_x z^q_t[x], so x_t is accepted iff x_t == a_t, and

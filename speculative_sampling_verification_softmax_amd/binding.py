@@ -25,7 +25,7 @@ SPEC_MAX_V = 1 << 20
 
 EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
            "spec_verify_workspace_size", "spec_verify_fused", "spec_greedy_verify", "spec_sample",
-           "spec_filter")
+           "spec_filter", "spec_verify_sample")
 
 _lib = None
 
@@ -60,6 +60,9 @@ def load(path: str = LIB_PATH):
     L.spec_greedy_verify.restype = i32
     L.spec_sample.argtypes = [vp, i32, i32, i32, f32, vp, vp, vp, vp]
     L.spec_sample.restype = i32
+    L.spec_verify_sample.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp,
+                                     vp, vp]
+    L.spec_verify_sample.restype = i32
     L.spec_filter.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp]
     L.spec_filter.restype = i32
     L.spec_status_string.argtypes = [i32]
@@ -186,6 +189,48 @@ def verify_all(target, draft, tokens, uniforms, T: float, stream=None) -> dict:
     ts, ds = softmax_stats(target, draft, T, stream=stream)
     n, out, probs = verify(target, draft, tokens, uniforms, ts, ds, T, stream=stream)
     ne = residual_sample(target, draft, uniforms, ts, ds, n, T, out, stream=stream)
+    return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=probs,
+                num_emitted=ne)
+
+
+def verify_sample(target, draft, tokens, uniforms, target_stats, draft_stats, T: float,
+                  num_accepted=None, out_tokens=None, probs=True, num_emitted=True,
+                  stream=None):
+    """spec_verify_sample: the accept scan and the final draw in one launch.
+    Returns (num_accepted, out_tokens, probs or None, num_emitted or None)."""
+    B, K, V = _shapes(target, draft)
+    dev = target.device
+    if num_accepted is None:
+        num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if probs is True:
+        probs = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+    elif probs is False:
+        probs = None
+    if num_emitted is True:
+        num_emitted = torch.empty(B, dtype=torch.int32, device=dev)
+    elif num_emitted is False:
+        num_emitted = None
+    pp = None if probs is None else _dev(probs, "probs", torch.float32, (B, K, 2))
+    ne = None if num_emitted is None else _dev(num_emitted, "num_emitted", torch.int32, (B,))
+    rc = load().spec_verify_sample(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
+        _dev(tokens, "tokens", torch.int32, (B, K)),
+        _dev(uniforms, "uniforms", torch.float32, (B, K + 1)),
+        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)),
+        B, K, V, float(T),
+        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
+        _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1)), pp, ne, _stream(stream))
+    _check(rc, "spec_verify_sample")
+    return num_accepted, out_tokens, probs, num_emitted
+
+
+def verify_two_call(target, draft, tokens, uniforms, T: float, stream=None) -> dict:
+    """The whole verify as two calls: stats, then accept scan + final draw."""
+    ts, ds = softmax_stats(target, draft, T, stream=stream)
+    n, out, probs, ne = verify_sample(target, draft, tokens, uniforms, ts, ds, T, stream=stream)
     return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=probs,
                 num_emitted=ne)
 

@@ -965,24 +965,21 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
   return tok;
 }
 
-// One workgroup per sequence (the spec_residual_sample path).  Dynamic LDS:
+// The final draw of sequence b with accepted count n, by the whole
+// workgroup: writes out_tokens[b][n] and num_emitted[b].  Dynamic LDS `dyn`:
 // the fast layout (A, Bv: nch doubles each; unc_n: nch ints; unc_idx:
-// nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow path.
+// nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow
+// path; with `etab` (bf16) the two rows' exponential tables come first.
+// n must be uniform across the workgroup.
 template <int BLOCK, int DT>
-__global__ __launch_bounds__(BLOCK) void residual_kernel(
-    const void* __restrict__ tgt, const void* __restrict__ dft,
-    const float* __restrict__ uni, const float* __restrict__ tstats,
-    const float* __restrict__ dstats, const int32_t* __restrict__ nacc, int K, int V,
-    double yscale, int fast, int etab, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ num_emitted) {
-  constexpr int E = 16 / Elt<DT>::bytes;
-  constexpr int NW = BLOCK / kWave;
-  extern __shared__ double dyn[];
-  __shared__ DrawShared<BLOCK> sh;
-  const int64_t b = blockIdx.x;
+__device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt, const void* dft,
+                                              const float* uni, const float* tstats,
+                                              const float* dstats, int K, int V, double yscale,
+                                              int fast, int etab, int32_t* out_tokens,
+                                              int32_t* num_emitted, double* dyn,
+                                              DrawShared<BLOCK>& sh) {
   const int64_t K1 = K + 1;
-  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
-  const int n = nacc[b];
+  const int tid = threadIdx.x;
   if (n < 0 || n > K) {
     if (tid == 0 && num_emitted) num_emitted[b] = 0;
     return;
@@ -1013,6 +1010,50 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
     out_tokens[b * K1 + n] = tok;
     if (num_emitted) num_emitted[b] = tok >= 0 ? n + 1 : 0;
   }
+}
+
+// One workgroup per sequence (the spec_residual_sample path): the final draw
+// with the caller's accepted counts.
+template <int BLOCK, int DT>
+__global__ __launch_bounds__(BLOCK) void residual_kernel(
+    const void* __restrict__ tgt, const void* __restrict__ dft,
+    const float* __restrict__ uni, const float* __restrict__ tstats,
+    const float* __restrict__ dstats, const int32_t* __restrict__ nacc, int K, int V,
+    double yscale, int fast, int etab, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ num_emitted) {
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
+  const int64_t b = blockIdx.x;
+  draw_sequence<BLOCK, DT>(b, nacc[b], tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
+                           out_tokens, num_emitted, dyn, sh);
+}
+
+// One workgroup per sequence (the spec_verify_sample path): wave 0 runs the
+// accept tests and the first-rejection scan (verify_seq), then the whole
+// workgroup draws the final token.  The same results as spec_verify followed
+// by spec_residual_sample, in one launch.
+template <int BLOCK, int DT>
+__global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
+    const void* __restrict__ tgt, const void* __restrict__ dft,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uni,
+    const float* __restrict__ tstats, const float* __restrict__ dstats, int K, int V,
+    double invT, double yscale, int fast, int etab, int32_t* __restrict__ num_accepted,
+    int32_t* __restrict__ out_tokens, float* __restrict__ probs,
+    int32_t* __restrict__ num_emitted) {
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
+  const int64_t b = blockIdx.x;
+  if (threadIdx.x < kWave) {
+    const int n = verify_seq<DT, false>(b, tgt, dft, tokens, uni, tstats + 2 * b * (K + 1),
+                                        dstats + 2 * b * K, K, V, invT, num_accepted,
+                                        out_tokens, probs, true);
+    if (threadIdx.x == 0) sh.sel[0] = n;
+  }
+  __syncthreads();
+  const int n = uniform(sh.sel[0]);
+  __syncthreads();  // sel[] is reused by the draw
+  draw_sequence<BLOCK, DT>(b, n, tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
+                           out_tokens, num_emitted, dyn, sh);
 }
 
 // ============================================================ draft sampling

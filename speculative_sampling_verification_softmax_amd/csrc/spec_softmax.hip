@@ -276,6 +276,39 @@ int spec_residual_sample(const void* target_logits, const void* draft_logits, in
   return launched();
 }
 
+int spec_verify_sample(const void* target_logits, const void* draft_logits, int dtype,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const float* target_stats, const float* draft_stats, int B, int K, int V,
+                       float temperature, int32_t* num_accepted, int32_t* out_tokens,
+                       float* probs, int32_t* num_emitted, void* stream) {
+  int rc = check_common(target_logits, draft_logits, dtype, B, K, V, temperature);
+  if (rc != SPEC_OK) return rc;
+  if (!draft_tokens || !uniforms || !target_stats || !draft_stats || !num_accepted || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned(draft_tokens, 4) || !aligned(uniforms, 4) || !aligned(target_stats, 4) ||
+      !aligned(draft_stats, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
+      !aligned(probs, 4) || !aligned(num_emitted, 4))
+    return SPEC_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const double invT = 1.0 / static_cast<double>(temperature);
+  const double yscale = invT * spec::Exp64::kScale;
+  const DrawLds d = draw_lds(num_chunks(V, dtype), dtype, 2);
+  (void)hipGetLastError();
+  const dim3 grid(static_cast<unsigned>(B)), block(kResidBlock);
+  if (dtype == SPEC_DTYPE_BF16) {
+    hipLaunchKernelGGL((spec::verify_draw_kernel<kResidBlock, kBF16>), grid, block, d.bytes, s,
+                       target_logits, draft_logits, draft_tokens, uniforms, target_stats,
+                       draft_stats, K, V, invT, yscale, d.fast, d.etab, num_accepted, out_tokens,
+                       probs, num_emitted);
+  } else {
+    hipLaunchKernelGGL((spec::verify_draw_kernel<kResidBlock, kF32>), grid, block, d.bytes, s,
+                       target_logits, draft_logits, draft_tokens, uniforms, target_stats,
+                       draft_stats, K, V, invT, yscale, d.fast, d.etab, num_accepted, out_tokens,
+                       probs, num_emitted);
+  }
+  return launched();
+}
+
 int spec_greedy_verify(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
                        int K, int V, int32_t* target_argmax, int32_t* num_accepted,
                        int32_t* out_tokens, int32_t* num_emitted, void* stream) {

@@ -19,17 +19,21 @@ MAX_FLAGGED_FRACTION = 1e-4
 PROB_RTOL = 1e-5
 
 
-PATHS = ("three_call", "fused")
+PATHS = ("three_call", "two_call", "fused")
 
 
 def gpu_verify(inp: dict, stream=None, path: str = "three_call", workspace=None) -> dict:
-    """Run the HIP verify through the C ABI: the three calls, or the fused call
-    (with a fresh zeroed workspace unless one is given)."""
+    """Run the HIP verify through the C ABI: the three calls, the two calls
+    (stats, then spec_verify_sample), or the fused call (with a fresh zeroed
+    workspace unless one is given)."""
     import torch
     from speculative_sampling_verification_softmax_amd import binding
     if path == "three_call":
         out = binding.verify_all(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
                                  inp["T"], stream=stream)
+    elif path == "two_call":
+        out = binding.verify_two_call(inp["target"], inp["draft"], inp["tokens"],
+                                      inp["uniforms"], inp["T"], stream=stream)
     elif path == "fused":
         B, K1, V = inp["target"].shape
         if workspace is None:

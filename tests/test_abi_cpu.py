@@ -205,3 +205,21 @@ def test_filter_rejects_bad_arguments(case):
     rc = L.spec_filter(a["logits"], 1, a["R"], a["V"], a["T"], a["k"], a["p"], a["thr"], a["out"],
                        None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("case", ["tgt", "dft", "tok", "uni", "ts", "ds", "nacc", "out", "K", "T",
+                                  "misaligned"])
+def test_verify_sample_rejects_bad_arguments(case):
+    L = _lib()
+    a = dict(tgt=P, dft=P, tok=P, uni=P, ts=P, ds=P, nacc=P, out=P, K=3, T=1.0, probs=None, ne=None)
+    if case == "K":
+        a["K"] = binding.SPEC_MAX_K + 1
+    elif case == "T":
+        a["T"] = -1.0
+    elif case == "misaligned":
+        a["ne"] = P + 3
+    else:
+        a[case] = None
+    rc = L.spec_verify_sample(a["tgt"], a["dft"], 1, a["tok"], a["uni"], a["ts"], a["ds"], 2,
+                              a["K"], 100, a["T"], a["nacc"], a["out"], a["probs"], a["ne"], None)
+    assert rc == 1

@@ -154,3 +154,17 @@ def test_fused_smaller_batch_after_larger_on_same_workspace():
         g = parity.gpu_verify(inp, path="fused", workspace=ws)
         o = parity.oracle_verify(synth.to_host_arrays(inp))
         parity.assert_parity(parity.compare(g, o, inp["T"]), f"fused B={B}")
+
+
+@pytest.mark.parametrize("wl", ["small", "headline"])
+def test_two_call_equals_three_call_bit_for_bit(wl):
+    """spec_verify_sample runs the same accept and draw arithmetic as spec_verify
+    plus spec_residual_sample: every output must be identical, floats included."""
+    inp = synth.make_inputs(wl, seed=7, device="cuda")
+    say(f"[two_call] {wl}: three calls vs two calls")
+    a = parity.gpu_verify(inp, path="three_call")
+    b = parity.gpu_verify(inp, path="two_call")
+    for k in ("num_accepted", "out_tokens", "num_emitted"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    for k in ("target_stats", "draft_stats", "probs"):
+        assert a[k].tobytes() == b[k].tobytes(), k
