@@ -241,7 +241,7 @@ def repeat_cpu(fn, units: int, unit: str, threads: int, what: str, min_cpu_s: fl
 
 
 def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
-    """--mode greedy / sample / filter: one JSON record for that entry point."""
+    """--mode greedy / sample / filter / filtered: one JSON record for that entry point."""
     import oracle
     B, K, V = wl.B, wl.K, wl.V
     dev = inp["target"].device
@@ -306,6 +306,46 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
             cpu = repeat_cpu(cpu_rows, n / (2 * K + 1), "seqs/s", 1,
                              f"thresholds of the first {n} draft rows (one thread), "
                              f"scaled to {2 * K + 1} rows per sequence")
+    elif args.mode == "filtered":
+        tgt, dft, tok, uni = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"]
+        ft, fd = torch.empty_like(tgt), torch.empty_like(dft)
+        tt = torch.empty(B * (K + 1), dtype=torch.float32, device=dev)
+        td = torch.empty(B * K, dtype=torch.float32, device=dev)
+        st = torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev)
+        sd = torch.empty((B, K, 2), dtype=torch.float32, device=dev)
+        nacc = torch.empty(B, dtype=torch.int32, device=dev)
+        out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        ne = torch.empty(B, dtype=torch.int32, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            binding.filter_rows(tgt, wl.T, args.top_k, args.top_p, out=ft, thresholds=tt,
+                                stats=st, stream=stream)
+            binding.filter_rows(dft, wl.T, args.top_k, args.top_p, out=fd, thresholds=td,
+                                stats=sd, stream=stream)
+            binding.verify_sample(ft, fd, tok, uni, st, sd, wl.T, nacc, out, False, ne,
+                                  stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+        ms, call_ms = timed(step, args.steps, args.warmup, stream)
+        R = B * (2 * K + 1)
+        alg = 2 * R * V * wl.elt + R * 12  # rows read once and written once; thresholds, stats
+        units, unit = B, "seqs/s"
+        metric = (f"verified seqs/sec with top-k {args.top_k} and top-p {args.top_p} on both p "
+                  f"and q (filter with stats, then spec_verify_sample), B={B} K={K} V={V} "
+                  f"{wl.dtype}")
+        kernel = "filter_kernel x2 + verify_draw_kernel"
+        cpu = None
+        if args.cpu_seqs > 0:
+            n = min(B, 8)
+            host = synth.to_host_arrays(inp)
+            T32, p32 = float(np.float32(wl.T)), float(np.float32(args.top_p))
+            cpu = repeat_cpu(lambda: oracle.verify_filtered(
+                host["target"][:n], host["draft"][:n], host["tokens"][:n], host["uniforms"][:n],
+                T32, top_k=args.top_k, top_p=p32, nthreads=threads), n, "seqs/s", threads,
+                f"the first {n} of the {B} sequences (the thresholds on one thread, the verify "
+                f"on all)")
     else:
         logits = inp["draft"]
         R = B * K
@@ -399,7 +439,7 @@ def main() -> int:
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--mode", default="verify",
-                    choices=["verify", "greedy", "sample", "filter", "ksweep"],
+                    choices=["verify", "greedy", "sample", "filter", "filtered", "ksweep"],
                     help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
                          "sweep K")
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")

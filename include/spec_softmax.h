@@ -207,6 +207,12 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
  *   thresholds   out [R] float: thr, -inf when nothing is removed, NaN for a
  *                row that defines no distribution (a NaN, or no finite
  *                maximum; its row is copied unchanged)
+ *   row_stats    optional out [R][2] float: {m, s} of the filtered row, as
+ *                spec_softmax_stats defines them (the maximum is never
+ *                removed, so m is the input row's; s sums the kept tokens;
+ *                s is NaN for a row that defines no distribution).  With it
+ *                the verify calls take the filtered rows and these stats
+ *                directly, without a spec_softmax_stats pass over them.
  *   filtered     optional out [R][V], dtype as logits: z with removed tokens
  *                set to -inf.  May equal logits (in place; then rows with
  *                nothing removed are not written); may not overlap it
@@ -214,7 +220,7 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
  * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
  */
 int spec_filter(const void* logits, int dtype, int R, int V, float temperature, int top_k,
-                float top_p, float* thresholds, void* filtered, void* stream);
+                float top_p, float* thresholds, float* row_stats, void* filtered, void* stream);
 
 /*
  * spec_verify_workspace_size -- bytes of device workspace spec_verify_fused

@@ -63,7 +63,7 @@ def load(path: str = LIB_PATH):
     L.spec_verify_sample.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp,
                                      vp, vp]
     L.spec_verify_sample.restype = i32
-    L.spec_filter.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp]
+    L.spec_filter.argtypes = [vp, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp]
     L.spec_filter.restype = i32
     L.spec_status_string.argtypes = [i32]
     L.spec_status_string.restype = ctypes.c_char_p
@@ -347,16 +347,20 @@ def sample(logits, uniforms, T: float, row_stats=None, tokens=None, stream=None)
 
 def filter_rows(logits, T: float, top_k: int = 0, top_p: float = 1.0, out=None,
                 thresholds=None, inplace: bool = False, write_rows: bool = True,
-                stream=None) -> dict:
+                stats=None, stream=None) -> dict:
     """spec_filter: top-k / nucleus thresholds of each row of logits [..., V]
     and the rows with the removed tokens set to -inf (written into `out`, a
     new tensor by default, or into logits itself when inplace; not written
-    at all when write_rows is False)."""
+    at all when write_rows is False).  stats: True for a new [..., 2] tensor
+    of the filtered rows' {m, s}, or a float32 tensor to fill; None: none."""
     V = logits.shape[-1]
     R = logits.numel() // V
     dev = logits.device
+    shape = tuple(logits.shape[:-1])
     if thresholds is None:
         thresholds = torch.empty(R, dtype=torch.float32, device=dev)
+    if stats is True:
+        stats = torch.empty(shape + (2,), dtype=torch.float32, device=dev)
     if not write_rows:
         out = None
     elif inplace:
@@ -364,10 +368,10 @@ def filter_rows(logits, T: float, top_k: int = 0, top_p: float = 1.0, out=None,
     elif out is None:
         out = torch.empty_like(logits)
     out_ptr = None if out is None else _dev(out, "out", logits.dtype, tuple(logits.shape))
+    st_ptr = None if stats is None else _dev(stats, "stats", torch.float32, shape + (2,))
     rc = load().spec_filter(_dev(logits, "logits"), _dtype_code(logits), R, V, float(T),
                             int(top_k), float(top_p),
-                            _dev(thresholds, "thresholds", torch.float32, (R,)), out_ptr,
+                            _dev(thresholds, "thresholds", torch.float32, (R,)), st_ptr, out_ptr,
                             _stream(stream))
     _check(rc, "spec_filter")
-    shape = tuple(logits.shape[:-1])
-    return dict(filtered=out, thresholds=thresholds.view(shape))
+    return dict(filtered=out, thresholds=thresholds.view(shape), stats=stats)

@@ -1488,50 +1488,65 @@ __device__ __forceinline__ unsigned radix_select(FE fe, unsigned lower, double t
   return base + static_cast<unsigned>(prefix);
 }
 
-// Output row: the input with every token below thr set to -inf (cut false:
-// a plain copy).  16-byte accesses where input and output rows share their
-// offset within 16 bytes.
-template <int BLOCK, int DT>
-__device__ __forceinline__ void write_filtered(const char* row, char* orow, int V, bool cut,
-                                               float thr) {
+// The last pass over a row: with WRITE, the output row (the input with every
+// token below thr set to -inf; cut false: a plain copy); with STATS, this
+// thread's part of the filtered row's normaliser sum exp2((z - m) c2) over
+// the kept tokens (fp32 terms, fp64 sums; the same quantity as the stats
+// kernel's s).  16-byte accesses where input and output rows share their
+// offset within 16 bytes (or when only reading).
+template <int BLOCK, int DT, bool WRITE, bool STATS>
+__device__ __forceinline__ double finish_row(const char* row, char* orow, int V, bool cut,
+                                             float thr, float m, float c2) {
   using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
   constexpr Bits kNegInf = DT == kBF16 ? Bits(0xFF80u) : Bits(0xFF800000u);
   constexpr int EB = Elt<DT>::bytes;
   const int tid = threadIdx.x;
   const Bits* src = reinterpret_cast<const Bits*>(row);
   Bits* dst = reinterpret_cast<Bits*>(orow);
-  auto one = [&](Bits b) -> Bits {
+  double acc = 0.0;
+  // one stored value: its output bits, and its term added to t
+  auto one = [&](Bits b, float& t) -> Bits {
     const float z = DT == kBF16 ? __uint_as_float(static_cast<uint32_t>(b) << 16)
                                 : __uint_as_float(static_cast<uint32_t>(b));
-    return (cut && z < thr) ? kNegInf : b;
+    const bool drop = cut && z < thr;
+    if (STATS) t += drop ? 0.0f : __builtin_amdgcn_exp2f((z - m) * c2);
+    return drop ? kNegInf : b;
   };
-  auto word = [&](uint32_t w) -> uint32_t {
+  auto word = [&](uint32_t w, float& t) -> uint32_t {
     if constexpr (DT == kBF16) {
-      const uint32_t lo = one(static_cast<Bits>(w & 0xFFFFu));
-      const uint32_t hi = one(static_cast<Bits>(w >> 16));
+      const uint32_t lo = one(static_cast<Bits>(w & 0xFFFFu), t);
+      const uint32_t hi = one(static_cast<Bits>(w >> 16), t);
       return lo | (hi << 16);
     } else {
-      return one(w);
+      return one(w, t);
     }
   };
-  if (((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) != 0) {
-    for (int i = tid; i < V; i += BLOCK) dst[i] = one(src[i]);
-    return;
+  auto scalar = [&](int i) {
+    float t = 0.0f;
+    const Bits o = one(src[i], t);
+    if (WRITE) dst[i] = o;
+    acc += static_cast<double>(t);
+  };
+  if (WRITE && ((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) != 0) {
+    for (int i = tid; i < V; i += BLOCK) scalar(i);
+    return acc;
   }
   const RowGeom<DT> G(row, V);
-  if (tid < G.head) dst[tid] = one(src[tid]);
-  if (tid < V - G.tail0) dst[G.tail0 + tid] = one(src[G.tail0 + tid]);
+  if (tid < G.head) scalar(tid);
+  if (tid < V - G.tail0) scalar(G.tail0 + tid);
   // the row's last read and the output's only write: non-temporal both
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   const v4u* vs = reinterpret_cast<const v4u*>(row + static_cast<int64_t>(G.head) * EB);
   v4u* vd = reinterpret_cast<v4u*>(orow + static_cast<int64_t>(G.head) * EB);
-  auto conv = [&](v4u v) {
+  auto vec = [&](v4u v, int i) {
+    float t = 0.0f;
     v4u o;
-    o.x = word(v.x);
-    o.y = word(v.y);
-    o.z = word(v.z);
-    o.w = word(v.w);
-    return o;
+    o.x = word(v.x, t);
+    o.y = word(v.y, t);
+    o.z = word(v.z, t);
+    o.w = word(v.w, t);
+    if (WRITE) __builtin_nontemporal_store(o, &vd[i]);
+    acc += static_cast<double>(t);
   };
   constexpr int U = 4;
   int i = tid;
@@ -1540,15 +1555,17 @@ __device__ __forceinline__ void write_filtered(const char* row, char* orow, int 
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&vs[i + u * BLOCK]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(conv(v[u]), &vd[i + u * BLOCK]);
+    for (int u = 0; u < U; ++u) vec(v[u], i + u * BLOCK);
   }
-  for (; i < G.nvec; i += BLOCK) __builtin_nontemporal_store(conv(__builtin_nontemporal_load(&vs[i])), &vd[i]);
+  for (; i < G.nvec; i += BLOCK) vec(__builtin_nontemporal_load(&vs[i]), i);
+  return acc;
 }
 
 template <int BLOCK, int DT, int VPG>
 __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out, int V,
                                                        float c2, double yscale, int top_k,
-                                                       float top_p, float* thr_out) {
+                                                       float top_p, float* thr_out,
+                                                       float* stats_out) {
   constexpr int NW = BLOCK / kWave;
   __shared__ FilterShared<BLOCK> sh;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
@@ -1672,12 +1689,28 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   if (tid == 0) thr_out[r] = thr;
 
   // the output row (none when out is null): removed tokens as -inf, the rest
-  // copied when out != in
+  // copied when out != in; and the filtered row's stats {m, s} (s NaN for a
+  // row that defines no distribution)
   const bool cut = thr > -__builtin_huge_valf();  // false for NaN too
-  if (out == nullptr || (!cut && out == in)) return;
-  write_filtered<BLOCK, DT>(row,
-                            static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes,
-                            V, cut, thr);
+  const bool write = out != nullptr && (cut || out != in);
+  const bool want = stats_out != nullptr && !bad;
+  char* orow = write ? static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes
+                     : nullptr;
+  double part = 0.0;
+  if (write && want) {
+    part = finish_row<BLOCK, DT, true, true>(row, orow, V, cut, thr, m, c2);
+  } else if (write) {
+    (void)finish_row<BLOCK, DT, true, false>(row, orow, V, cut, thr, m, c2);
+  } else if (want) {
+    part = finish_row<BLOCK, DT, false, true>(row, nullptr, V, cut, thr, m, c2);
+  }
+  if (stats_out != nullptr) {
+    const double sum = want ? block_sum<BLOCK>(part, sh.redd) : 0.0;
+    if (tid == 0) {
+      stats_out[2 * r] = m;
+      stats_out[2 * r + 1] = want ? static_cast<float>(sum) : __builtin_nanf("");
+    }
+  }
 }
 
 // ==================================================================== fused

@@ -374,11 +374,11 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
 }
 
 int spec_filter(const void* logits, int dtype, int R, int V, float temperature, int top_k,
-                float top_p, float* thresholds, void* filtered, void* stream) {
+                float top_p, float* thresholds, float* row_stats, void* filtered, void* stream) {
   if (R < 1) return SPEC_ERR_INVALID_ARG;
   int rc = check_common(logits, logits, dtype, R, 1, V, temperature);
   if (rc != SPEC_OK) return rc;
-  if (!thresholds || !aligned(thresholds, 4)) return SPEC_ERR_INVALID_ARG;
+  if (!thresholds || !aligned(thresholds, 4) || !aligned(row_stats, 4)) return SPEC_ERR_INVALID_ARG;
   if (top_k < 0 || !(top_p > 0.0f) || std::isnan(top_p)) return SPEC_ERR_INVALID_ARG;
   const int eb = elt_bytes(dtype);
   if (filtered != nullptr && filtered != logits) {
@@ -396,11 +396,11 @@ int spec_filter(const void* logits, int dtype, int R, int V, float temperature, 
   if (dtype == SPEC_DTYPE_BF16) {
     hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kBF16, SPEC_FILTER_VPG_BF16>), dim3(R),
                        dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
-                       thresholds);
+                       thresholds, row_stats);
   } else {
     hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kF32, SPEC_FILTER_VPG_F32>), dim3(R),
                        dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
-                       thresholds);
+                       thresholds, row_stats);
   }
   return launched();
 }

@@ -178,10 +178,11 @@ def test_sample_rejects_bad_arguments(case):
 
 
 @pytest.mark.parametrize("case", ["logits", "thr", "R", "V", "T", "top_k", "top_p0", "top_pnan",
-                                  "misaligned_thr", "misaligned_out", "overlap"])
+                                  "misaligned_thr", "misaligned_out", "misaligned_stats",
+                                  "overlap"])
 def test_filter_rejects_bad_arguments(case):
     L = _lib()
-    a = dict(logits=P, R=4, V=100, T=1.0, k=10, p=0.9, thr=P + 4096, out=P + 65536)
+    a = dict(logits=P, R=4, V=100, T=1.0, k=10, p=0.9, thr=P + 4096, stats=None, out=P + 65536)
     if case == "R":
         a["R"] = 0
     elif case == "V":
@@ -196,14 +197,16 @@ def test_filter_rejects_bad_arguments(case):
         a["p"] = math.nan
     elif case == "misaligned_thr":
         a["thr"] = P + 4098
+    elif case == "misaligned_stats":
+        a["stats"] = P + 8194
     elif case == "misaligned_out":
         a["out"] = P + 65537  # bf16 rows: odd byte address
     elif case == "overlap":
         a["out"] = P + 2  # shares all but one element with the input rows
     else:
         a[case] = None
-    rc = L.spec_filter(a["logits"], 1, a["R"], a["V"], a["T"], a["k"], a["p"], a["thr"], a["out"],
-                       None)
+    rc = L.spec_filter(a["logits"], 1, a["R"], a["V"], a["T"], a["k"], a["p"], a["thr"],
+                       a["stats"], a["out"], None)
     assert rc == 1
 
 

@@ -82,10 +82,11 @@ def check_filter(logits: torch.Tensor, T: float, top_k: int, top_p: float, label
         f"inplace={inplace} -> gpu")
     before = host_logits(logits).reshape(R, V).copy()
     src = logits.clone() if inplace else logits
-    out = binding.filter_rows(src, T, top_k, top_p, inplace=inplace)
+    out = binding.filter_rows(src, T, top_k, top_p, inplace=inplace, stats=True)
     torch.cuda.synchronize()
     thr = out["thresholds"].reshape(-1).cpu().numpy().astype(np.float64)
     got = host_logits(out["filtered"]).reshape(R, V)
+    st = out["stats"].reshape(R, 2).cpu().numpy().astype(np.float64)
     rows = list(range(R)) if rows is None else list(rows)
     flagged, checked, kept = 0, 0, []
     for r in rows:
@@ -96,6 +97,7 @@ def check_filter(logits: torch.Tensor, T: float, top_k: int, top_p: float, label
         if o is None:
             assert np.isnan(thr[r]), f"{label}: row {r} should be invalid, got {thr[r]}"
             assert got[r].tobytes() == before[r].tobytes(), f"{label}: invalid row {r} changed"
+            assert np.isnan(st[r, 1]), f"{label}: invalid row {r} has s={st[r, 1]}"
             continue
         if thr[r] != o:
             hi = max(thr[r], o)
@@ -108,6 +110,10 @@ def check_filter(logits: torch.Tensor, T: float, top_k: int, top_p: float, label
         if thr[r] > -np.inf:
             exp[zr < thr[r]] = neg_inf_bits(before)
         assert got[r].tobytes() == exp.tobytes(), f"{label}: row {r} filtered row differs"
+        # the filtered row's stats against the oracle's own row statistics
+        _, M, S = oracle.softmax_row(exp, T32)
+        assert st[r, 0] / T32 == M, f"{label}: row {r} stats max {st[r, 0]}"
+        assert abs(st[r, 1] - S) <= 1e-5 * S, f"{label}: row {r} stats s {st[r, 1]} vs {S}"
     assert flagged <= MAX_NUCLEUS_FLAGGED * max(checked, 1), f"{label}: {flagged} near-tie rows"
     kept = np.asarray(kept)
     say(f"[filter] {label}: {checked} rows checked, {flagged} near-tie thresholds, "
@@ -204,11 +210,12 @@ def test_invalid_rows_and_trivial_parameters():
     assert np.all(thr[[0, 3, 4]] == -np.inf) and np.all(np.isnan(thr[[1, 2, 5]]))
     assert torch.equal(out["filtered"].view(torch.int32), z.view(torch.int32))
     # thresholds only: no rows written
-    only = binding.filter_rows(z, 1.0, 20, 0.9, write_rows=False)
-    full = binding.filter_rows(z, 1.0, 20, 0.9)
+    only = binding.filter_rows(z, 1.0, 20, 0.9, write_rows=False, stats=True)
+    full = binding.filter_rows(z, 1.0, 20, 0.9, stats=True)
     assert only["filtered"] is None
     np.testing.assert_array_equal(only["thresholds"].cpu().numpy(),
                                   full["thresholds"].cpu().numpy())
+    assert only["stats"].cpu().numpy().tobytes() == full["stats"].cpu().numpy().tobytes()
 
 
 @pytest.mark.parametrize("wl,top_k,top_p", [("small", 40, 0.9), ("batch1", 0, 0.8),
@@ -237,13 +244,26 @@ def test_verify_on_filtered_rows(wl, top_k, top_p):
     tok = np.where(tok < 0, 0, tok).astype(np.int32)
     host["tokens"] = tok
     say(f"[filtered verify] {wl} B={B} K={K} V={V} k={top_k} p={p32} -> gpu filter + verify")
-    ft = binding.filter_rows(inp["target"], inp["T"], top_k, top_p)["filtered"]
-    fd = binding.filter_rows(inp["draft"], inp["T"], top_k, top_p)["filtered"]
-    g = parity.gpu_verify(dict(target=ft, draft=fd, tokens=torch.as_tensor(tok, device="cuda"),
-                               uniforms=inp["uniforms"], T=inp["T"]))
+    ftr = binding.filter_rows(inp["target"], inp["T"], top_k, top_p, stats=True)
+    fdr = binding.filter_rows(inp["draft"], inp["T"], top_k, top_p, stats=True)
+    ft, fd = ftr["filtered"], fdr["filtered"]
+    tok_d = torch.as_tensor(tok, device="cuda")
+    g = parity.gpu_verify(dict(target=ft, draft=fd, tokens=tok_d, uniforms=inp["uniforms"],
+                               T=inp["T"]))
     o = oracle.verify_filtered(host["target"], host["draft"], tok, host["uniforms"], T32,
                                top_k=top_k, top_p=p32)
     rep = parity.compare(g, o, inp["T"])
     say(f"[filtered verify] {wl}: draws={rep['draws']} flagged={len(rep['flagged'])} "
         f"failures={len(rep['failures'])} accept_hist={rep['accept_hist']}")
     parity.assert_parity(rep, f"filtered {wl}")
+    # the filter's own stats straight into spec_verify_sample (no stats pass)
+    n, out, probs, ne = binding.verify_sample(ft, fd, tok_d, inp["uniforms"], ftr["stats"],
+                                              fdr["stats"], inp["T"])
+    torch.cuda.synchronize()
+    g2 = dict(target_stats=ftr["stats"].cpu().numpy(), draft_stats=fdr["stats"].cpu().numpy(),
+              num_accepted=n.cpu().numpy(), out_tokens=out.cpu().numpy(),
+              probs=probs.cpu().numpy(), num_emitted=ne.cpu().numpy())
+    rep2 = parity.compare(g2, o, inp["T"])
+    say(f"[filtered verify, filter stats] {wl}: flagged={len(rep2['flagged'])} "
+        f"failures={len(rep2['failures'])}")
+    parity.assert_parity(rep2, f"filtered {wl} (filter stats)")
