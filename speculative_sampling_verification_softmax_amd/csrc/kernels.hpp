@@ -790,15 +790,21 @@ struct DrawShared {
   double seld[4];
 };
 
-// Exact two-sweep draw (whole block).  W: nch doubles of scratch.  Returns the
-// token (every thread), or -1 when no token carries positive weight.
+// Exact two-sweep draw (whole block).  W: nch doubles of scratch.  With
+// have_s the exact normalisers Sq, Sp of a finished fast sweep are taken
+// as given and the first sweep is skipped.  Returns the token (every
+// thread), or -1 when no token carries positive weight.
 template <int BLOCK, int DT, bool ET = false>
-__device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh) {
+__device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh,
+                         bool have_s = false, double Sq_in = 0.0, double Sp_in = 0.0) {
   constexpr int NW = BLOCK / kWave;
   constexpr int E = 16 / Elt<DT>::bytes;
   const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
   double iq = 1.0, ip = 1.0;
-  if (R.mode == kModeResidual) {
+  if (R.mode == kModeResidual && have_s) {
+    iq = 1.0 / Sq_in;
+    ip = 1.0 / Sp_in;
+  } else if (R.mode == kModeResidual) {
     double aq = 0.0, ap = 0.0;
     for (int c = wv; c < nch; c += NW) {
       RawChunk raw;
@@ -859,8 +865,8 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 // normalisers Sq, Sp and, per chunk, the sums A, Bv and the uncertain lists
 // (XB: written by other workgroups of this launch).  W (nch doubles of this
 // workgroup's own memory; it may be A itself when XB is false) receives the
-// chunk totals W_c.  Returns the token, -1 (nothing to draw) or -2 (take the
-// slow path).
+// chunk totals W_c.  Returns the token, -1 (nothing to draw), -2 (take the
+// slow path) or -3 (the residual has no mass: draw from q_n instead).
 template <int BLOCK, int DT, bool XB, bool ET = false>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
@@ -907,7 +913,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   __syncthreads();
   if (R.mode == kModeResidual && !(sh.seld[2] > 0.0)) {
     __syncthreads();
-    return -2;  // residual without mass: the slow path falls back to q
+    return -3;
   }
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
@@ -936,6 +942,7 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
   const int wv = threadIdx.x / kWave, lane = lane_id();
   const int nch = (R.V + kWave * E - 1) / (kWave * E);
   int tok = -2;
+  double Sq = 0.0, Sp = 0.0;
   if (fast) {
     double* A = dyn;
     double* Bv = A + nch;
@@ -955,13 +962,19 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
       wave_sweep<DT, kModeResidual, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     else
       wave_sweep<DT, kModeBonus, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
-    const double Sq = block_sum<BLOCK>(lsq, sh.red);
-    const double Sp = block_sum<BLOCK>(lsp, sh.red);
+    Sq = block_sum<BLOCK>(lsq, sh.red);
+    Sp = block_sum<BLOCK>(lsp, sh.red);
     tok = fast_finish<BLOCK, DT, false, ET>(
         R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
         Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
   }
-  if (tok == -2) tok = slow_draw<BLOCK, DT, ET>(R, nch, dyn, u, sh);
+  if (tok == -3) {  // residual without mass: the bonus draw from q_n
+    DrawRows Rb = R;
+    Rb.mode = kModeBonus;
+    tok = slow_draw<BLOCK, DT, ET>(Rb, nch, dyn, u, sh);
+  } else if (tok == -2) {
+    tok = slow_draw<BLOCK, DT, ET>(R, nch, dyn, u, sh, fast != 0, Sq, Sp);
+  }
   return tok;
 }
 
@@ -1592,6 +1605,8 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   const bool use_k = top_k > 0, use_p = top_p < 1.0f;
   float zlo = m - kFilterWindow / c2;
   unsigned thr_key = 0;
+  bool in_lds = false;  // the selects ran over the window's values in LDS
+  int n_lds = 0;
   if (!bad && use_k && top_k <= BLOCK) {
     // top-k window: the k-th largest of the per-thread maxima.  Those k
     // maxima are k distinct values at or above it, so the window holds the
@@ -1652,6 +1667,8 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
                       (use_k ? static_cast<unsigned>(top_k) <= n
                              : static_cast<double>(win_all) >= static_cast<double>(top_p) * S);
     if (fast) {
+      in_lds = true;
+      n_lds = nc;
       // key range of the values in LDS: [kmin, key(m)]
       unsigned kmin = 0xFFFFFFFFu;
       fe([&](float x) {
@@ -1694,18 +1711,32 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   const bool cut = thr > -__builtin_huge_valf();  // false for NaN too
   const bool write = out != nullptr && (cut || out != in);
   const bool want = stats_out != nullptr && !bad;
+  // When the selects ran in LDS and something is cut, every kept token is in
+  // LDS (the window lies at or below the threshold): s is summed there, in
+  // fixed point (exact in any order).  Otherwise the last pass sums it.
+  const bool s_lds = want && in_lds && cut;
   char* orow = write ? static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes
                      : nullptr;
   double part = 0.0;
-  if (write && want) {
+  if (write && want && !s_lds) {
     part = finish_row<BLOCK, DT, true, true>(row, orow, V, cut, thr, m, c2);
   } else if (write) {
     (void)finish_row<BLOCK, DT, true, false>(row, orow, V, cut, thr, m, c2);
-  } else if (want) {
+  } else if (want && !s_lds) {
     part = finish_row<BLOCK, DT, false, true>(row, nullptr, V, cut, thr, m, c2);
   }
   if (stats_out != nullptr) {
-    const double sum = want ? block_sum<BLOCK>(part, sh.redd) : 0.0;
+    double sum = 0.0;
+    if (s_lds) {
+      unsigned long long f = 0ull;
+      for (int i = tid; i < n_lds; i += BLOCK) {
+        const float z = sh.cand[i];
+        if (z >= thr) f += mass_fixed(z, m, yscale, sh.tab);
+      }
+      sum = static_cast<double>(block_sum_u64<BLOCK>(f, sh.redq)) * (1.0 / kMassScale);
+    } else if (want) {
+      sum = block_sum<BLOCK>(part, sh.redd);
+    }
     if (tid == 0) {
       stats_out[2 * r] = m;
       stats_out[2 * r + 1] = want ? static_cast<float>(sum) : __builtin_nanf("");
@@ -2004,7 +2035,13 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
           Src<true, double>(a.Bv + base, a.nch), Src<true, int>(a.unc_n + base, a.nch),
           Src<true, int>(a.unc_idx + base * kUncMax, static_cast<int64_t>(a.nch) * kUncMax), wbuf,
           u, sh.d);
-      if (tok == -2) tok = slow_draw<BLOCK, DT>(R, a.nch, wbuf, u, sh.d);
+      if (tok == -3) {  // residual without mass: the bonus draw from q_n
+        DrawRows Rb = R;
+        Rb.mode = kModeBonus;
+        tok = slow_draw<BLOCK, DT>(Rb, a.nch, wbuf, u, sh.d);
+      } else if (tok == -2) {
+        tok = slow_draw<BLOCK, DT>(R, a.nch, wbuf, u, sh.d, true, Sq, Sp);
+      }
     }
     if (tid == 0) {
       if (n >= 0 && n <= K) a.out_tokens[static_cast<int64_t>(b) * K1 + n] = tok;
