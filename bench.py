@@ -5,22 +5,27 @@
 
 One step = the whole verify of one batch: row statistics of every target and
 draft row, the accept scan and the residual or bonus draw, inputs resident in
-HBM.  --path three_call (default, the faster path on MI355X) runs it as
-spec_softmax_stats, spec_verify, spec_residual_sample back to back on one
-stream; --path fused as one spec_verify_fused launch.  W untimed steps, then K timed steps bracketed by device
-synchronisation.  Prints one JSON line on stdout; progress goes to stderr.
+HBM.  --path two_call (default, the fastest path on MI355X) runs it as
+spec_softmax_stats then spec_verify_sample on one stream; --path three_call as
+spec_softmax_stats, spec_verify, spec_residual_sample; --path fused as one
+spec_verify_fused launch.  W untimed steps, then K timed steps bracketed by
+device synchronisation, with nothing else on the stream.  Prints one JSON
+line on stdout; progress goes to stderr.
 
 Reported:
   value          verified sequences per second (B / seconds per step)
-  roofline       the dominant kernel (three_call: the stats kernel, every
-                 logit once + stats written; fused: the fused kernel, the
-                 whole step's compulsory bytes) / its mean duration, timed
-                 with events on its stream in the timed region.  traffic is
-                 the HBM bytes per launch that rocprofv3's FETCH_SIZE and
-                 WRITE_SIZE counters measured for that kernel and workload,
-                 scaled by a plain copy of known size, read from a
-                 "traffic-record" line under profiles/; null when no record
-                 matches the current kernel sources
+  roofline       the dominant kernel (two_call, three_call: the stats kernel,
+                 every logit once + stats written; fused: the fused kernel,
+                 the whole step's compulsory bytes) / its mean duration, timed
+                 with an event pair around it on its stream in K further steps
+                 right after the timed region (events recorded between two
+                 kernels add a few microseconds to a step, so they are kept
+                 out of the timed region).  traffic is the HBM bytes per
+                 launch that rocprofv3's FETCH_SIZE and WRITE_SIZE counters
+                 measured for that kernel and workload, scaled by a plain copy
+                 of known size, read from a "traffic-record" line under
+                 profiles/; null when no record matches the current kernel
+                 sources
   cpu_baseline   the fp64 CPU oracle on a bounded sample of the same input
                  bytes (host threads), sequences per second
 
@@ -210,8 +215,10 @@ def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, min_cpu_s: float 
 
 
 def timed(step, steps: int, warmup: int, stream) -> tuple[float, float]:
-    """(ms per step over the timed region, mean ms of the event pairs each
-    step records around its main call)."""
+    """(ms per step over the timed region, mean ms of the event pair that a
+    step records around its main call).  The timed region holds `steps`
+    steps and nothing else; the call's duration comes from `steps` further
+    steps that record the pair."""
     torch.cuda.synchronize()
     for _ in range(warmup):
         step()
@@ -221,9 +228,12 @@ def timed(step, steps: int, warmup: int, stream) -> tuple[float, float]:
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
     for i in range(steps):
         step(evs[i])
-    t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
@@ -540,25 +550,8 @@ def main() -> int:
 
     step = {"fused": step_fused, "two_call": step_two, "three_call": step_three}[args.path]
 
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
-
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"[bench] warmup {args.warmup}, then {args.steps} timed steps")
+    ms, dom_ms = timed(step, args.steps, args.warmup, stream)
     if args.path == "fused":
         dom_kernel, dom_bytes = "fused_kernel", step_bytes(wl)
     else:

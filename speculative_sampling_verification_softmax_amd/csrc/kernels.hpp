@@ -442,42 +442,51 @@ __device__ __forceinline__ double tok_exp(float z, double yscale, double m, cons
 
 // bf16 rows hold few distinct values: every z with 2^-7 <= |z| < 2^6 is one
 // of 2 * 13 * 128 codes.  A workgroup that draws from a row can fill a table
-// of tok_exp over those codes once (kETab doubles per row: positive codes,
-// negative codes, then a 0 for -inf) and look tokens up instead of evaluating
-// the exponential; other values are computed.  The table holds tok_exp's own
-// results, so both ways give the same bits.
+// of tok_exp over those codes once (kETab doubles per row: the positive codes
+// and a 0, then the negative codes and a 0) and look tokens up instead of
+// evaluating the exponential; other values are computed.  The table holds
+// tok_exp's own results, so both ways give the same bits.  With t = |code| -
+// kETabLo (unsigned), a code's entry is sign * (kETabN + 1) + min(t, kETabN):
+// every code outside the table, -inf included, lands on its sign's 0.
 constexpr unsigned kETabLo = 120u << 7;  // bf16 bits of 2^-7, sign cleared
 constexpr unsigned kETabN = 13u << 7;    // codes per sign: exponents 2^-7 .. 2^5
-constexpr int kETabZero = 2 * static_cast<int>(kETabN);
-constexpr int kETab = kETabZero + 2;  // doubles per row (even)
+constexpr int kETab = 2 * (static_cast<int>(kETabN) + 1);  // doubles per row (even)
 
 template <int BLOCK>
 __device__ __forceinline__ void fill_row_exp_table(double* et, double yscale, double m,
                                                    const double* tab) {
+  constexpr unsigned NB = kETabN + 1;
   for (int j = threadIdx.x; j < kETab; j += BLOCK) {
-    if (j >= kETabZero) {
+    const unsigned i = static_cast<unsigned>(j) % NB;
+    if (i == kETabN) {
       et[j] = 0.0;
       continue;
     }
-    const unsigned code = (kETabLo + static_cast<unsigned>(j) % kETabN) |
-                          (static_cast<unsigned>(j) >= kETabN ? 0x8000u : 0u);
+    const unsigned code = (kETabLo + i) | (static_cast<unsigned>(j) >= NB ? 0x8000u : 0u);
     et[j] = tok_exp(__uint_as_float(code << 16), yscale, m, tab);
   }
 }
 
+// Table entry of bf16 code b, and whether b needs the computed exponential
+// (outside the table and not infinite; a row that is drawn from has a finite
+// maximum, so its only infinite logits are -inf).
+__device__ __forceinline__ int etab_index(unsigned b) {
+  const unsigned t = (b & 0x7FFFu) - kETabLo;
+  return static_cast<int>((b >> 15) * (kETabN + 1) + min(t, kETabN));
+}
+__device__ __forceinline__ bool etab_other(unsigned b) {
+  return (b & 0x7FFFu) - kETabLo >= kETabN && (b & 0x7FFFu) != 0x7F80u;
+}
+
 // e(x) of a token of the q row (P false) or the p row (P true) of R.  With
-// the tables (ET), every lane reads one entry (the zero slot for -inf and
-// for codes outside the table), and a wave computes the exponential only
-// when one of its lanes holds such a code.
+// the tables (ET), every lane reads one entry, and a wave computes the
+// exponential only when one of its lanes holds a code outside the table.
 template <int DT, bool ET, bool P>
 __device__ __forceinline__ double row_exp(const DrawRows& R, float z, const double* tab) {
   if constexpr (DT == kBF16 && ET) {
     const unsigned b = __float_as_uint(z) >> 16;
-    const unsigned i = (b & 0x7FFFu) - kETabLo;
-    const bool in = i < kETabN;
-    const int idx = in ? static_cast<int>((b >> 15) * kETabN + i) : kETabZero;
-    double e = R.et[(P ? kETab : 0) + idx];
-    const bool other = !in && b != 0xFF80u;
+    double e = R.et[(P ? kETab : 0) + etab_index(b)];
+    const bool other = etab_other(b);
     if (__builtin_amdgcn_ballot_w64(other) != 0ull) {
       if (other) e = tok_exp(z, R.yscale, P ? R.mp : R.mq, tab);
     }
@@ -497,11 +506,8 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
 #pragma unroll
     for (int k = 0; k < H; ++k) {
       const unsigned b = __float_as_uint(z[k]) >> 16;
-      const unsigned i = (b & 0x7FFFu) - kETabLo;
-      const bool in = i < kETabN;
-      const int idx = in ? static_cast<int>((b >> 15) * kETabN + i) : kETabZero;
-      e[k] = R.et[(P ? kETab : 0) + idx];
-      other[k] = !in && b != 0xFF80u;
+      e[k] = R.et[(P ? kETab : 0) + etab_index(b)];
+      other[k] = etab_other(b);
       any = any || other[k];
     }
     if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
@@ -512,6 +518,48 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
   } else {
 #pragma unroll
     for (int k = 0; k < H; ++k) e[k] = tok_exp(z[k], R.yscale, P ? R.mp : R.mq, tab);
+  }
+}
+
+// The same lookups from the raw words of a bf16 row (two codes per word, the
+// lower token id in the low half), with the index arithmetic done on both
+// halves at once in 16-bit lanes.  A word's flag is nonzero when one of its
+// codes is neither in the table nor -inf.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void etab_offsets(unsigned w, unsigned& o0, unsigned& o1,
+                                             unsigned& flag) {
+  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  const u16x2 t = mag - static_cast<u16x2>(static_cast<unsigned short>(kETabLo));
+  const u16x2 tc = __builtin_elementwise_min(t, static_cast<u16x2>(static_cast<unsigned short>(kETabN)));
+  const u16x2 sg = __builtin_bit_cast(u16x2, w) >> static_cast<u16x2>(static_cast<unsigned short>(15));
+  const u16x2 idx = sg * static_cast<u16x2>(static_cast<unsigned short>(kETabN + 1)) + tc;
+  const unsigned off = __builtin_bit_cast(unsigned, idx << static_cast<u16x2>(static_cast<unsigned short>(3)));
+  o0 = off & 0xFFFFu;  // byte offsets: the table is under 64 KiB
+  o1 = off >> 16;
+  const u16x2 out = __builtin_elementwise_sub_sat(
+      t, static_cast<u16x2>(static_cast<unsigned short>(kETabN - 1)));  // 0 iff in the table
+  const u16x2 ninf = mag ^ static_cast<u16x2>(static_cast<unsigned short>(0x7F80u));  // 0 iff +-inf
+  flag |= __builtin_bit_cast(unsigned, __builtin_elementwise_min(out, ninf));
+}
+
+// e of the 2*NW codes in words w[0..NW) of the q row (P false) or p row.
+template <bool P, int NW>
+__device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned (&w)[NW],
+                                              const double* tab, double (&e)[2 * NW]) {
+  const char* base = reinterpret_cast<const char*>(R.et + (P ? kETab : 0));
+  unsigned o[2 * NW];
+  unsigned flag = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) etab_offsets(w[k], o[2 * k], o[2 * k + 1], flag);
+#pragma unroll
+  for (int k = 0; k < 2 * NW; ++k) e[k] = *reinterpret_cast<const double*>(base + o[k]);
+  if (__builtin_amdgcn_ballot_w64(flag != 0u) != 0ull) {
+#pragma unroll
+    for (int k = 0; k < 2 * NW; ++k) {
+      const unsigned b = (w[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
+      if (etab_other(b)) e[k] = tok_exp(__uint_as_float(b << 16), R.yscale, P ? R.mp : R.mq, tab);
+    }
   }
 }
 
@@ -587,25 +635,19 @@ struct ChunkSums {
   int unc[kUncMax];
 };
 
-// Fast-path arithmetic of one chunk from its values.  Adds every token's e_q,
-// e_p to the lane's lsq, lsp.
-template <int DT, int MODE, bool ET = false>
-__device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
-                                           const float (&zq)[16 / Elt<DT>::bytes],
-                                           const float (&zp)[16 / Elt<DT>::bytes],
-                                           const double* tab, double& lsq, double& lsp,
-                                           ChunkSums& out) {
+// Fast-path arithmetic of one chunk.  lookup(e, eq, ep) gives the exponentials
+// of the lane's tokens e .. e+H-1 of the q row (and the p row for a residual).
+// Adds every token's e_q, e_p to the lane's lsq, lsp.
+template <int DT, int MODE, int H, typename Lookup>
+__device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup lookup, double& lsq,
+                                              double& lsp, ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
-  constexpr int H = E < 4 ? E : 4;  // tokens whose exponentials are formed together
   double a = 0.0, bb = 0.0;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (e % H == 0) {
-      row_exp_n<DT, ET, false, H>(R, zq + e, tab, eqh);
-      if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, eph);
-    }
+    if (e % H == 0) lookup(e, eqh, eph);
     const double eq = eqh[e % H];
     lsq = lsq + eq;
     if (MODE == kModeResidual) {
@@ -620,7 +662,7 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
       const double take = __hiloint2double((certain && d > 0.0) ? 0x3ff00000 : 0, 0);
       a = fma(take, eq, a);
       bb = fma(take, ep, bb);
-      unc_m[e] = __ballot(!certain);
+      unc_m[e] = ~__ballot(certain);  // every lane of the wave is active here
     } else {
       a = a + eq;
     }
@@ -648,6 +690,49 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
   }
 }
 
+// chunk_sums_by from the lane's values.
+template <int DT, int MODE, bool ET = false>
+__device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
+                                           const float (&zq)[16 / Elt<DT>::bytes],
+                                           const float (&zp)[16 / Elt<DT>::bytes],
+                                           const double* tab, double& lsq, double& lsp,
+                                           ChunkSums& out) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  constexpr int H = E < 4 ? E : 4;  // tokens whose exponentials are formed together
+  auto lookup = [&](int e, double (&eq)[H], double (&ep)[H]) {
+    row_exp_n<DT, ET, false, H>(R, zq + e, tab, eq);
+    if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, ep);
+  };
+  chunk_sums_by<DT, MODE, H>(R, c, lookup, lsq, lsp, out);
+}
+
+// chunk_sums_by from the raw words of bf16 rows with the exponential tables.
+template <int MODE>
+__device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const uint4& wq,
+                                                 const uint4& wp, const double* tab,
+                                                 double& lsq, double& lsp, ChunkSums& out) {
+  const unsigned q[4] = {wq.x, wq.y, wq.z, wq.w};
+  const unsigned p[4] = {wp.x, wp.y, wp.z, wp.w};
+  auto lookup = [&](int e, double (&eq)[4], double (&ep)[4]) {
+    const unsigned qw[2] = {q[e / 2], q[e / 2 + 1]};
+    row_exp_words<false, 2>(R, qw, tab, eq);
+    if (MODE == kModeResidual) {
+      const unsigned pw[2] = {p[e / 2], p[e / 2 + 1]};
+      row_exp_words<true, 2>(R, pw, tab, ep);
+    }
+  };
+  chunk_sums_by<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, out);
+}
+
+// The 8 bf16 codes of z (stored values, -inf past V) as 4 words.
+__device__ __forceinline__ uint4 pack_bf16_words(const float (&z)[8]) {
+  unsigned w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = (__float_as_uint(z[2 * k + 1]) & 0xFFFF0000u) | (__float_as_uint(z[2 * k]) >> 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
 // flight (a slot is refilled as soon as its chunk has been unpacked);
 // emit(c, sums) stores a chunk's results.
@@ -669,13 +754,26 @@ __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, in
     for (int j = 0; j < PF; ++j) {
       const int c = base + j * stride;
       if (c < c1) {
-        float zq[E], zp[E];
-        chunk_values<DT, MODE>(R, c, full[j], buf[j], zq, zp);
-        const int cn = c + PF * stride;
-        full[j] = cn < c1 && chunk_full<DT>(R, cn);
-        if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
         ChunkSums cs;
-        chunk_sums<DT, MODE, ET>(R, c, zq, zp, tab, lsq, lsp, cs);
+        const int cn = c + PF * stride;
+        if constexpr (DT == kBF16 && ET) {  // table lookups straight from the words
+          uint4 wq = buf[j].q, wp = buf[j].p;
+          if (!full[j]) {
+            float zq[E], zp[E];
+            chunk_values<DT, MODE>(R, c, false, buf[j], zq, zp);
+            wq = pack_bf16_words(zq);
+            if (MODE == kModeResidual) wp = pack_bf16_words(zp);
+          }
+          full[j] = cn < c1 && chunk_full<DT>(R, cn);
+          if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
+          chunk_sums_words<MODE>(R, c, wq, wp, tab, lsq, lsp, cs);
+        } else {
+          float zq[E], zp[E];
+          chunk_values<DT, MODE>(R, c, full[j], buf[j], zq, zp);
+          full[j] = cn < c1 && chunk_full<DT>(R, cn);
+          if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
+          chunk_sums<DT, MODE, ET>(R, c, zq, zp, tab, lsq, lsp, cs);
+        }
         emit(c, cs);
       }
     }
