@@ -124,16 +124,28 @@ __device__ __forceinline__ double dpp_row_shr(double v, int ctrl_n) {
   return __hiloint2double(rhi, rlo);
 }
 
-__device__ __forceinline__ double wave_sum_rows(double v) {
+// The inclusive scan inside each row of 16 lanes: lanes 15, 31, 47 and 63
+// end with their row's total.
+__device__ __forceinline__ double wave_scan_rows(double v) {
   v = v + dpp_row_shr(v, 1);
   v = v + dpp_row_shr(v, 2);
   v = v + dpp_row_shr(v, 4);
   v = v + dpp_row_shr(v, 8);
+  return v;
+}
+
+// The four row totals added in order (every lane gets the same bits).
+__device__ __forceinline__ double sum_row_totals(double r0, double r1, double r2, double r3) {
+  return ((r0 + r1) + r2) + r3;
+}
+
+__device__ __forceinline__ double wave_sum_rows(double v) {
+  v = wave_scan_rows(v);
   auto lane_val = [&](int l) {
     return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
                             __builtin_amdgcn_readlane(__double2loint(v), l));
   };
-  return ((lane_val(15) + lane_val(31)) + lane_val(47)) + lane_val(63);
+  return sum_row_totals(lane_val(15), lane_val(31), lane_val(47), lane_val(63));
 }
 
 // Inclusive prefix sum across the 64 lanes (Hillis-Steele order, fixed).

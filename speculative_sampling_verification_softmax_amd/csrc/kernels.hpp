@@ -628,7 +628,9 @@ __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq
   }
 }
 
-// Per-chunk results of a fast-path sweep (valid in every lane).
+// Per-chunk results of a fast-path sweep: A and Bv valid in every lane, or
+// with RS their in-row scans (the row totals in lanes 15, 31, 47, 63); the
+// uncertain list valid in every lane.
 struct ChunkSums {
   double A, Bv;
   int n_unc;
@@ -638,7 +640,7 @@ struct ChunkSums {
 // Fast-path arithmetic of one chunk.  lookup(e, eq, ep) gives the exponentials
 // of the lane's tokens e .. e+H-1 of the q row (and the p row for a residual).
 // Adds every token's e_q, e_p to the lane's lsq, lsp.
-template <int DT, int MODE, int H, typename Lookup>
+template <int DT, int MODE, int H, bool RS, typename Lookup>
 __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup lookup, double& lsq,
                                               double& lsp, ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
@@ -667,8 +669,13 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
       a = a + eq;
     }
   }
-  out.A = wave_sum_rows(a);
-  out.Bv = MODE == kModeResidual ? wave_sum_rows(bb) : 0.0;
+  if constexpr (RS) {
+    out.A = wave_scan_rows(a);
+    out.Bv = MODE == kModeResidual ? wave_scan_rows(bb) : 0.0;
+  } else {
+    out.A = wave_sum_rows(a);
+    out.Bv = MODE == kModeResidual ? wave_sum_rows(bb) : 0.0;
+  }
   out.n_unc = 0;
 #pragma unroll
   for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
@@ -691,7 +698,7 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
 }
 
 // chunk_sums_by from the lane's values.
-template <int DT, int MODE, bool ET = false>
+template <int DT, int MODE, bool ET = false, bool RS = false>
 __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
                                            const float (&zq)[16 / Elt<DT>::bytes],
                                            const float (&zp)[16 / Elt<DT>::bytes],
@@ -703,11 +710,11 @@ __device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
     row_exp_n<DT, ET, false, H>(R, zq + e, tab, eq);
     if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, ep);
   };
-  chunk_sums_by<DT, MODE, H>(R, c, lookup, lsq, lsp, out);
+  chunk_sums_by<DT, MODE, H, RS>(R, c, lookup, lsq, lsp, out);
 }
 
 // chunk_sums_by from the raw words of bf16 rows with the exponential tables.
-template <int MODE>
+template <int MODE, bool RS>
 __device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const uint4& wq,
                                                  const uint4& wp, const double* tab,
                                                  double& lsq, double& lsp, ChunkSums& out) {
@@ -721,7 +728,7 @@ __device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const
       row_exp_words<true, 2>(R, pw, tab, ep);
     }
   };
-  chunk_sums_by<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, out);
+  chunk_sums_by<kBF16, MODE, 4, RS>(R, c, lookup, lsq, lsp, out);
 }
 
 // The 8 bf16 codes of z (stored values, -inf past V) as 4 words.
@@ -735,8 +742,8 @@ __device__ __forceinline__ uint4 pack_bf16_words(const float (&z)[8]) {
 
 // One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
 // flight (a slot is refilled as soon as its chunk has been unpacked);
-// emit(c, sums) stores a chunk's results.
-template <int DT, int MODE, int PF, bool ET = false, typename Emit>
+// emit(c, sums) stores a chunk's results (RS: see ChunkSums).
+template <int DT, int MODE, int PF, bool ET = false, bool RS = false, typename Emit>
 __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, int stride,
                                            const double* tab, double& lsq, double& lsp,
                                            Emit emit) {
@@ -766,13 +773,13 @@ __device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, in
           }
           full[j] = cn < c1 && chunk_full<DT>(R, cn);
           if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
-          chunk_sums_words<MODE>(R, c, wq, wp, tab, lsq, lsp, cs);
+          chunk_sums_words<MODE, RS>(R, c, wq, wp, tab, lsq, lsp, cs);
         } else {
           float zq[E], zp[E];
           chunk_values<DT, MODE>(R, c, full[j], buf[j], zq, zp);
           full[j] = cn < c1 && chunk_full<DT>(R, cn);
           if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
-          chunk_sums<DT, MODE, ET>(R, c, zq, zp, tab, lsq, lsp, cs);
+          chunk_sums<DT, MODE, ET, RS>(R, c, zq, zp, tab, lsq, lsp, cs);
         }
         emit(c, cs);
       }
@@ -961,15 +968,23 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 
 // Fast-path finish (whole block) from a sweep's results: the exact
 // normalisers Sq, Sp and, per chunk, the sums A, Bv and the uncertain lists
-// (XB: written by other workgroups of this launch).  W (nch doubles of this
-// workgroup's own memory; it may be A itself when XB is false) receives the
-// chunk totals W_c.  Returns the token, -1 (nothing to draw), -2 (take the
-// slow path) or -3 (the residual has no mass: draw from q_n instead).
-template <int BLOCK, int DT, bool XB, bool ET = false>
+// (XB: written by other workgroups of this launch; RS: A and Bv hold four row
+// totals per chunk, added here in the order wave_sum_rows uses).  W (nch
+// doubles of this workgroup's own memory; it may be A itself when neither XB
+// nor RS is set) receives the chunk totals W_c.  Returns the token, -1
+// (nothing to draw), -2 (take the slow path) or -3 (the residual has no mass:
+// draw from q_n instead).
+template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
                            double* W, double u, DrawShared<BLOCK>& sh) {
   const int tid = threadIdx.x, wv = tid / kWave;
+  auto chunk_total = [&](const Src<XB, double>& X, int c) {
+    if constexpr (RS)
+      return sum_row_totals(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
+    else
+      return X[c];
+  };
   double iq = 1.0, ip = 1.0;
   if (R.mode == kModeResidual) {
     iq = 1.0 / Sq;
@@ -977,7 +992,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
     const double ratio = (Sq / Sp) / (R.sq_t / R.sp_t);
     bool ok = fabs(ratio - 1.0) <= kDelta / 4;
     for (int c = tid; c < nch; c += BLOCK) {
-      const double a = A[c], bv = Bv[c];
+      const double a = chunk_total(A, c), bv = chunk_total(Bv, c);
       const int nu = unc_n[c];
       int x[kUncMax];
 #pragma unroll
@@ -1004,7 +1019,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
     __syncthreads();
     if (slow) return -2;
   } else {
-    for (int c = tid; c < nch; c += BLOCK) W[c] = A[c];
+    for (int c = tid; c < nch; c += BLOCK) W[c] = chunk_total(A, c);
     __syncthreads();
   }
   if (wv == 0) locate_chunk(W, nch, u, sh.sel, sh.seld);
@@ -1028,9 +1043,10 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 }
 
 // The whole draw for one row (pair) by one workgroup: the one-sweep fast path
-// when `fast` (dynamic LDS `dyn` then holds A, Bv: nch doubles each; unc_n:
-// nch ints; unc_idx: nch*kUncMax ints), else or on its failure the exact
-// two-sweep path (dyn: nch doubles).  sh.tab must hold the exp table.
+// when `fast` (dynamic LDS `dyn` then holds A, Bv: four row totals per chunk,
+// 4*nch doubles each; W: nch doubles; unc_n: nch ints; unc_idx: nch*kUncMax
+// ints), else or on its failure the exact two-sweep path (dyn: nch doubles).
+// sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
 template <int BLOCK, int DT, bool ET = false>
 __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
@@ -1043,28 +1059,31 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
   double Sq = 0.0, Sp = 0.0;
   if (fast) {
     double* A = dyn;
-    double* Bv = A + nch;
-    int* unc_n = reinterpret_cast<int*>(Bv + nch);
+    double* Bv = A + 4 * nch;
+    double* W = Bv + 4 * nch;
+    int* unc_n = reinterpret_cast<int*>(W + nch);
     int* unc_idx = unc_n + nch;
     double lsq = 0.0, lsp = 0.0;
     auto emit = [&](int c, const ChunkSums& cs) {
+      if ((lane & 15) == 15) {  // the row totals
+        A[4 * c + (lane >> 4)] = cs.A;
+        Bv[4 * c + (lane >> 4)] = cs.Bv;
+      }
       if (lane == 0) {
-        A[c] = cs.A;
-        Bv[c] = cs.Bv;
         unc_n[c] = cs.n_unc;
 #pragma unroll
         for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
       }
     };
     if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeResidual, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     else
-      wave_sweep<DT, kModeBonus, 1, ET>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeBonus, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     Sq = block_sum<BLOCK>(lsq, sh.red);
     Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false, ET>(
-        R, nch, Sq, Sp, Src<false, double>(A, nch), Src<false, double>(Bv, nch),
-        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), A, u, sh);
+    tok = fast_finish<BLOCK, DT, false, ET, true>(
+        R, nch, Sq, Sp, Src<false, double>(A, 4 * nch), Src<false, double>(Bv, 4 * nch),
+        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), W, u, sh);
   }
   if (tok == -3) {  // residual without mass: the bonus draw from q_n
     DrawRows Rb = R;

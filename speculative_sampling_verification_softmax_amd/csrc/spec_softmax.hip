@@ -42,11 +42,11 @@ constexpr int kFusedBlock = 256;
 constexpr int kFusedNW = kFusedBlock / spec::kWave;
 // Dynamic LDS of the fused kernel: one double per chunk of a row.
 constexpr size_t kFusedMaxDynLds = static_cast<size_t>(SPEC_MAX_V / 64 / 4) * sizeof(double);
-// LDS the one-workgroup residual kernel may take for its fast-path arrays.
-constexpr size_t kResidFastLds = 48 * 1024;
-// Dynamic LDS of a draw workgroup in all (the static part is ~2.3 KB; the
-// total stays within 64 KB).
-constexpr size_t kDrawDynLds = 60 * 1024;
+// Dynamic LDS of a draw workgroup (the fast-path arrays, then the bf16
+// exponential tables if they fit as well).  The static part is ~2.3 KB; a
+// gfx950 workgroup may hold 160 KB, and a draw workgroup has its CU alone.
+constexpr size_t kResidFastLds = 152 * 1024;
+constexpr size_t kDrawDynLds = 152 * 1024;
 
 // Dynamic LDS of the residual / sample kernels: the fast-path arrays (or the
 // slow path's nch doubles), preceded by `rows` bf16 exponential tables when
@@ -59,7 +59,7 @@ struct DrawLds {
 DrawLds draw_lds(int nch, int dtype, int rows) {
   DrawLds d{};
   const size_t fast_lds = static_cast<size_t>(nch) *
-                          (2 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
+                          (9 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
   d.fast = fast_lds <= kResidFastLds ? 1 : 0;
   const size_t work = d.fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
   const size_t tables = static_cast<size_t>(rows) * spec::kETab * sizeof(double);
