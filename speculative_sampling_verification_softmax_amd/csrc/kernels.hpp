@@ -442,27 +442,27 @@ __device__ __forceinline__ double tok_exp(float z, double yscale, double m, cons
 
 // bf16 rows hold few distinct values: every z with 2^-7 <= |z| < 2^6 is one
 // of 2 * 13 * 128 codes.  A workgroup that draws from a row can fill a table
-// of tok_exp over those codes once (kETab doubles per row: the positive codes
-// and a 0, then the negative codes and a 0) and look tokens up instead of
-// evaluating the exponential; other values are computed.  The table holds
-// tok_exp's own results, so both ways give the same bits.  With t = |code| -
-// kETabLo (unsigned), a code's entry is sign * (kETabN + 1) + min(t, kETabN):
-// every code outside the table, -inf included, lands on its sign's 0.
+// of tok_exp over those codes once (kETab doubles per row: a block of
+// kETabSign entries per sign, the codes in order and then 0s) and look tokens
+// up instead of evaluating the exponential; other values are computed.  The
+// table holds tok_exp's own results, so both ways give the same bits.  With
+// t = |code| - kETabLo (unsigned), a code's entry is sign * kETabSign +
+// min(t, kETabN): every code outside the table, -inf included, lands on a 0.
 constexpr unsigned kETabLo = 120u << 7;  // bf16 bits of 2^-7, sign cleared
 constexpr unsigned kETabN = 13u << 7;    // codes per sign: exponents 2^-7 .. 2^5
-constexpr int kETab = 2 * (static_cast<int>(kETabN) + 1);  // doubles per row (even)
+constexpr unsigned kETabSign = 2048;     // entries per sign block (a power of two)
+constexpr int kETab = 2 * static_cast<int>(kETabSign);  // doubles per row
 
 template <int BLOCK>
 __device__ __forceinline__ void fill_row_exp_table(double* et, double yscale, double m,
                                                    const double* tab) {
-  constexpr unsigned NB = kETabN + 1;
   for (int j = threadIdx.x; j < kETab; j += BLOCK) {
-    const unsigned i = static_cast<unsigned>(j) % NB;
-    if (i == kETabN) {
+    const unsigned i = static_cast<unsigned>(j) % kETabSign;
+    if (i >= kETabN) {
       et[j] = 0.0;
       continue;
     }
-    const unsigned code = (kETabLo + i) | (static_cast<unsigned>(j) >= NB ? 0x8000u : 0u);
+    const unsigned code = (kETabLo + i) | (static_cast<unsigned>(j) >= kETabSign ? 0x8000u : 0u);
     et[j] = tok_exp(__uint_as_float(code << 16), yscale, m, tab);
   }
 }
@@ -472,7 +472,7 @@ __device__ __forceinline__ void fill_row_exp_table(double* et, double yscale, do
 // maximum, so its only infinite logits are -inf).
 __device__ __forceinline__ int etab_index(unsigned b) {
   const unsigned t = (b & 0x7FFFu) - kETabLo;
-  return static_cast<int>((b >> 15) * (kETabN + 1) + min(t, kETabN));
+  return static_cast<int>((b >> 15) * kETabSign + min(t, kETabN));
 }
 __device__ __forceinline__ bool etab_other(unsigned b) {
   return (b & 0x7FFFu) - kETabLo >= kETabN && (b & 0x7FFFu) != 0x7F80u;
@@ -527,16 +527,30 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
 // codes is neither in the table nor -inf.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void etab_offsets(unsigned w, unsigned& o0, unsigned& o1,
-                                             unsigned& flag) {
+static_assert(kETabSign * 8 == 0x4000u && kETabN * 8 <= 0x4000u, "sign bit -> byte 0x4000");
+
+// The low 16 bits of x + a wave-uniform base, in one instruction (an SDWA
+// word select; the compiler otherwise masks and adds).
+__device__ __forceinline__ unsigned add_low16(unsigned base, unsigned x) {
+  unsigned r;
+  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 "
+      "src1_sel:DWORD"
+      : "=v"(r)
+      : "v"(x), "s"(base));
+  return r;
+}
+
+// LDS addresses (table base + byte offset) of the two codes of w.
+__device__ __forceinline__ void etab_addresses(unsigned w, unsigned base, unsigned& a0,
+                                               unsigned& a1, unsigned& flag) {
   const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
   const u16x2 t = mag - static_cast<u16x2>(static_cast<unsigned short>(kETabLo));
   const u16x2 tc = __builtin_elementwise_min(t, static_cast<u16x2>(static_cast<unsigned short>(kETabN)));
-  const u16x2 sg = __builtin_bit_cast(u16x2, w) >> static_cast<u16x2>(static_cast<unsigned short>(15));
-  const u16x2 idx = sg * static_cast<u16x2>(static_cast<unsigned short>(kETabN + 1)) + tc;
-  const unsigned off = __builtin_bit_cast(unsigned, idx << static_cast<u16x2>(static_cast<unsigned short>(3)));
-  o0 = off & 0xFFFFu;  // byte offsets: the table is under 64 KiB
-  o1 = off >> 16;
+  const unsigned tc8 =
+      __builtin_bit_cast(unsigned, tc << static_cast<u16x2>(static_cast<unsigned short>(3)));
+  const unsigned off = tc8 | ((w >> 1) & 0x40004000u);  // each half's sign bit -> 0x4000
+  a0 = add_low16(base, off);
+  a1 = base + (off >> 16);
   const u16x2 out = __builtin_elementwise_sub_sat(
       t, static_cast<u16x2>(static_cast<unsigned short>(kETabN - 1)));  // 0 iff in the table
   const u16x2 ninf = mag ^ static_cast<u16x2>(static_cast<unsigned short>(0x7F80u));  // 0 iff +-inf
@@ -547,13 +561,15 @@ __device__ __forceinline__ void etab_offsets(unsigned w, unsigned& o0, unsigned&
 template <bool P, int NW>
 __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned (&w)[NW],
                                               const double* tab, double (&e)[2 * NW]) {
-  const char* base = reinterpret_cast<const char*>(R.et + (P ? kETab : 0));
-  unsigned o[2 * NW];
+  typedef const __attribute__((address_space(3))) double* LdsDouble;
+  const LdsDouble et = (LdsDouble)(R.et + (P ? kETab : 0));  // the tables live in LDS
+  const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(et));
+  unsigned a[2 * NW];
   unsigned flag = 0;
 #pragma unroll
-  for (int k = 0; k < NW; ++k) etab_offsets(w[k], o[2 * k], o[2 * k + 1], flag);
+  for (int k = 0; k < NW; ++k) etab_addresses(w[k], base, a[2 * k], a[2 * k + 1], flag);
 #pragma unroll
-  for (int k = 0; k < 2 * NW; ++k) e[k] = *reinterpret_cast<const double*>(base + o[k]);
+  for (int k = 0; k < 2 * NW; ++k) e[k] = *(LdsDouble)(static_cast<uintptr_t>(a[k]));
   if (__builtin_amdgcn_ballot_w64(flag != 0u) != 0ull) {
 #pragma unroll
     for (int k = 0; k < 2 * NW; ++k) {
