@@ -148,8 +148,9 @@ __device__ __forceinline__ double wave_sum_rows(double v) {
   return sum_row_totals(lane_val(15), lane_val(31), lane_val(47), lane_val(63));
 }
 
-// Inclusive prefix sum across the 64 lanes (Hillis-Steele order, fixed).
-__device__ __forceinline__ double wave_incl_scan(double v) {
+// Inclusive prefix sum across the 64 lanes (Hillis-Steele order, fixed),
+// through the LDS crossbar.
+__device__ __forceinline__ double wave_incl_scan_shfl(double v) {
   const int lane = lane_id();
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
@@ -157,6 +158,35 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
     if (lane >= d) v = v + o;
   }
   return v;
+}
+
+// A DPP move of a double (both halves with the same control); lanes of rows
+// outside row_mask, and lanes without a source, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_mov(double v) {
+  const int lo = __double2loint(v), hi = __double2hiint(v);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(0, hi, CTRL, ROW_MASK, 0xf, true),
+                          __builtin_amdgcn_update_dpp(0, lo, CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum across the 64 lanes in DPP moves only: the in-row
+// scans, then the total of row 0 added to row 1 and of row 2 to row 3
+// (row_bcast:15), then the total of rows 0-1 added to rows 2 and 3
+// (row_bcast:31).  Fixed order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v = wave_scan_rows(v);
+  v = v + dpp_mov<0x142, 0xA>(v);
+  v = v + dpp_mov<0x143, 0xC>(v);
+  return v;
+}
+
+// The value of lane i-1 (0 in lane 0): DPP wave_shr:1.
+__device__ __forceinline__ double wave_shr1(double v) { return dpp_mov<0x138, 0xF>(v); }
+
+// The value of a double in lane l (l wave-uniform).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
 }
 
 // ---------------------------------------------------------------- block ops

@@ -453,18 +453,24 @@ constexpr unsigned kETabN = 13u << 7;    // codes per sign: exponents 2^-7 .. 2^
 constexpr unsigned kETabSign = 2048;     // entries per sign block (a power of two)
 constexpr int kETab = 2 * static_cast<int>(kETabSign);  // doubles per row
 
+// Fills the tables of `rows` rows (1 or 2; row r has maximum m[r]) at et,
+// kETab doubles apart: row by row (m stays wave-uniform), the kETabN codes
+// of each sign block spread evenly over the workgroup, then each block's 0
+// (entries past it are never read).
 template <int BLOCK>
-__device__ __forceinline__ void fill_row_exp_table(double* et, double yscale, double m,
-                                                   const double* tab) {
-  for (int j = threadIdx.x; j < kETab; j += BLOCK) {
-    const unsigned i = static_cast<unsigned>(j) % kETabSign;
-    if (i >= kETabN) {
-      et[j] = 0.0;
-      continue;
+__device__ __forceinline__ void fill_row_exp_tables(double* et, int rows, double yscale,
+                                                    const double (&m)[2], const double* tab) {
+  constexpr unsigned NC = 2 * kETabN;  // codes per row
+  for (int r = 0; r < rows; ++r) {
+    const double mr = r == 0 ? m[0] : m[1];
+    for (unsigned k = threadIdx.x; k < NC; k += BLOCK) {
+      const unsigned sg = k >= kETabN ? 1u : 0u, i = k - sg * kETabN;
+      const unsigned code = (kETabLo + i) | (sg << 15);
+      et[r * kETab + sg * kETabSign + i] = tok_exp(__uint_as_float(code << 16), yscale, mr, tab);
     }
-    const unsigned code = (kETabLo + i) | (static_cast<unsigned>(j) >= kETabSign ? 0x8000u : 0u);
-    et[j] = tok_exp(__uint_as_float(code << 16), yscale, m, tab);
   }
+  if (threadIdx.x < 2 * rows)
+    et[(threadIdx.x >> 1) * kETab + (threadIdx.x & 1) * kETabSign + kETabN] = 0.0;
 }
 
 // Table entry of bf16 code b, and whether b needs the computed exponential
@@ -557,6 +563,15 @@ __device__ __forceinline__ void etab_addresses(unsigned w, unsigned base, unsign
   flag |= __builtin_bit_cast(unsigned, __builtin_elementwise_min(out, ninf));
 }
 
+// The 8 bf16 codes of z (stored values, -inf past V) as 4 words.
+__device__ __forceinline__ uint4 pack_bf16_words(const float (&z)[8]) {
+  unsigned w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = (__float_as_uint(z[2 * k + 1]) & 0xFFFF0000u) | (__float_as_uint(z[2 * k]) >> 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // e of the 2*NW codes in words w[0..NW) of the q row (P false) or p row.
 template <bool P, int NW>
 __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned (&w)[NW],
@@ -631,6 +646,27 @@ __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq
   if (full) chunk_issue<DT, MODE>(R, c, raw);
   float zq[E], zp[E];
   chunk_values<DT, MODE>(R, c, full, raw, zq, zp);
+  if constexpr (DT == kBF16 && ET) {  // all table reads at once, from the words
+    const uint4 wq = pack_bf16_words(zq);
+    const unsigned q[4] = {wq.x, wq.y, wq.z, wq.w};
+    double eq[E], ep[E];
+    row_exp_words<false, 4>(R, q, tab, eq);
+    if (MODE == kModeResidual) {
+      const uint4 wp = pack_bf16_words(zp);
+      const unsigned p[4] = {wp.x, wp.y, wp.z, wp.w};
+      row_exp_words<true, 4>(R, p, tab, ep);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (MODE == kModeResidual) {
+        const double d = eq[e] * iq - ep[e] * ip;
+        w[e] = d > 0.0 ? d : 0.0;
+      } else {
+        w[e] = eq[e];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const double eq = row_exp<DT, ET, false>(R, zq[e], tab);
@@ -747,14 +783,6 @@ __device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const
   chunk_sums_by<kBF16, MODE, 4, RS>(R, c, lookup, lsq, lsp, out);
 }
 
-// The 8 bf16 codes of z (stored values, -inf past V) as 4 words.
-__device__ __forceinline__ uint4 pack_bf16_words(const float (&z)[8]) {
-  unsigned w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    w[k] = (__float_as_uint(z[2 * k + 1]) & 0xFFFF0000u) | (__float_as_uint(z[2 * k]) >> 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 // One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
 // flight (a slot is refilled as soon as its chunk has been unpacked);
@@ -816,12 +844,11 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
   double lt = 0.0;
   for (int c = c0; c < c1; ++c) lt = lt + W[c];
   const double li = wave_incl_scan(lt);
-  double run = __shfl_up(li, 1, kWave);
-  if (lane == 0) run = 0.0;
+  const double run = wave_shr1(li);
   double r = run;
   for (int c = c0; c < c1; ++c) r = r + W[c];
   const int last_lane = (nch - 1) / per;
-  const double S_w = __shfl(r, last_lane, kWave);
+  const double S_w = readlane_d(r, last_lane);
   const double target = u * S_w;
   int hit = -1, lastpos = -1;
   double hit_excl = 0.0, lastpos_excl = 0.0;
@@ -845,12 +872,12 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
   double ex = 0.0;
   if (hm) {
     const int src = __ffsll(static_cast<long long>(hm)) - 1;
-    s = __shfl(hit, src, kWave);
-    ex = __shfl(hit_excl, src, kWave);
+    s = __builtin_amdgcn_readlane(hit, src);
+    ex = readlane_d(hit_excl, src);
   } else if (pm) {
     const int src = 63 - __clzll(static_cast<long long>(pm));
-    s = __shfl(lastpos, src, kWave);
-    ex = __shfl(lastpos_excl, src, kWave);
+    s = __builtin_amdgcn_readlane(lastpos, src);
+    ex = readlane_d(lastpos_excl, src);
   }
   if (lane == 0) {
     sel[0] = s;
@@ -874,8 +901,7 @@ __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool cros
 #pragma unroll
   for (int e = 0; e < E; ++e) ls = ls + w[e];
   const double incl = wave_incl_scan(ls);
-  double lexcl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) lexcl = 0.0;
+  const double lexcl = wave_shr1(incl);
   const bool lane_hit = crossing && ls > 0.0 && (excl + incl) > target;
   const unsigned long long hm = __ballot(lane_hit);
   const unsigned long long pm = __ballot(ls > 0.0);
@@ -897,7 +923,7 @@ __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool cros
     }
     if (pick < 0) pick = lastpos;
   }
-  pick = __shfl(pick, src, kWave);
+  pick = __builtin_amdgcn_readlane(pick, src);
   return c * (kWave * E) + src * E + pick;
 }
 
@@ -987,9 +1013,10 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 // (XB: written by other workgroups of this launch; RS: A and Bv hold four row
 // totals per chunk, added here in the order wave_sum_rows uses).  W (nch
 // doubles of this workgroup's own memory; it may be A itself when neither XB
-// nor RS is set) receives the chunk totals W_c.  Returns the token, -1
-// (nothing to draw), -2 (take the slow path) or -3 (the residual has no mass:
-// draw from q_n instead).
+// nor RS is set) receives the chunk totals W_c.  sh.sel[3] must be 0, with a
+// barrier between the clearing and the call.  Returns the token, -1 (nothing
+// to draw), -2 (take the slow path) or -3 (the residual has no mass: draw
+// from q_n instead).
 template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
@@ -1027,13 +1054,9 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
       }
       W[c] = w;
     }
-    if (tid == 0) sh.sel[3] = 0;
+    if (!ok) sh.sel[3] = 1;  // cleared by the caller before a barrier
     __syncthreads();
-    if (!ok) sh.sel[3] = 1;
-    __syncthreads();
-    const bool slow = sh.sel[3] != 0;
-    __syncthreads();
-    if (slow) return -2;
+    if (sh.sel[3] != 0) return -2;
   } else {
     for (int c = tid; c < nch; c += BLOCK) W[c] = chunk_total(A, c);
     __syncthreads();
@@ -1095,7 +1118,8 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
       wave_sweep<DT, kModeResidual, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
     else
       wave_sweep<DT, kModeBonus, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
-    Sq = block_sum<BLOCK>(lsq, sh.red);
+    if (threadIdx.x == 0) sh.sel[3] = 0;
+    Sq = block_sum<BLOCK>(lsq, sh.red);  // its barriers order the clear above
     Sp = block_sum<BLOCK>(lsp, sh.red);
     tok = fast_finish<BLOCK, DT, false, ET, true>(
         R, nch, Sq, Sp, Src<false, double>(A, 4 * nch), Src<false, double>(Bv, 4 * nch),
@@ -1144,8 +1168,8 @@ __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt,
   __syncthreads();
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the two rows' tables
-    fill_row_exp_table<BLOCK>(dyn, R.yscale, R.mq, sh.tab);
-    if (R.mode == kModeResidual) fill_row_exp_table<BLOCK>(dyn + kETab, R.yscale, R.mp, sh.tab);
+    const double m[2] = {R.mq, R.mp};
+    fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R.yscale, m, sh.tab);
     __syncthreads();
     R.et = dyn;
     work = dyn + 2 * kETab;
@@ -1240,7 +1264,8 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
   __syncthreads();
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the row's table
-    fill_row_exp_table<BLOCK>(dyn, R.yscale, R.mq, sh.tab);
+    const double m[2] = {R.mq, 0.0};
+    fill_row_exp_tables<BLOCK>(dyn, 1, R.yscale, m, sh.tab);
     __syncthreads();
     R.et = dyn;
     work = dyn + kETab;
@@ -1502,7 +1527,7 @@ __device__ __forceinline__ void walk_bins(const unsigned long long* hist, double
     v[j] = static_cast<double>(hist[255 - 4 * lane - j]);
     ls = ls + v[j];
   }
-  const double incl = wave_incl_scan(ls);
+  const double incl = wave_incl_scan_shfl(ls);
   const double excl = incl - ls;
   const unsigned long long hit = __ballot(incl >= need);
   // rounding of the running total can leave it a hair under `need`: then the
@@ -2161,7 +2186,8 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
         lq = lq + sqp[i];
         lp = lp + spp[i];
       }
-      const double Sq = block_sum<BLOCK>(lq, sh.d.red);
+      if (tid == 0) sh.d.sel[3] = 0;
+      const double Sq = block_sum<BLOCK>(lq, sh.d.red);  // its barriers order the clear
       const double Sp = block_sum<BLOCK>(lp, sh.d.red);
       tok = fast_finish<BLOCK, DT, true>(
           R, a.nch, Sq, Sp, Src<true, double>(a.A + base, a.nch),
