@@ -132,7 +132,8 @@ def _pmc_kernels(path: str) -> dict:
 
 def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
-    suffix = "" if path == "three_call" else "_" + path  # pass directories: fetch, fetch_two_call, ...
+    # pass directories: fetch, write (the stats kernel, two or three calls); fetch_fused, ...
+    suffix = "" if path in ("two_call", "three_call") else "_" + path
     fetch, write = f("fetch" + suffix), f("write" + suffix)
     copy_bytes = COPY_MIB << 20
     def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)

@@ -218,6 +218,35 @@ def test_forced_counts_and_zero_residual_fallback():
     assert np.sum(ref["draw_kind"] == 2) >= 5
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_residual_after_a_clean_fast_sweep(dtype):
+    """Both rows at the rejected position keep one and the same token (the
+    rest -inf) and the drafted token lies outside it, so q = p = 0 there: the
+    token is rejected and the residual has no mass, while the one-sweep fast
+    path itself succeeds (one uncertain token).  The draw falls back to q_n
+    (Pitfalls).  Rows before n are identical, so they are always accepted."""
+    rng = np.random.default_rng(11)
+    B, K, V = 48, 4, 2000
+    tgt = (2 * rng.standard_normal((B, K + 1, V))).astype(np.float32)
+    dft = (tgt[:, :K] + 0.5 * rng.standard_normal((B, K, V))).astype(np.float32)
+    tok = _tokens_from(rng, dft, 1.0)
+    n_of = rng.integers(0, K, B)
+    for b in range(0, B, 3):           # every third sequence keeps a control
+        n = int(n_of[b])
+        dft[b, :n] = tgt[b, :n]
+        keep = int(rng.integers(0, V))
+        tgt[b, n] = -np.inf
+        dft[b, n] = -np.inf
+        tgt[b, n, keep] = float(rng.uniform(-3, 3))
+        dft[b, n, keep] = float(rng.uniform(-3, 3))
+        tok[b, n] = (keep + 1 + int(rng.integers(0, V - 1))) % V
+    inp = _to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0, dtype=dtype)
+    g, o = _check(inp, f"empty residual {dtype}")
+    fell_back = [b for b in range(0, B, 3) if g["num_accepted"][b] == n_of[b]]
+    assert len(fell_back) == len(range(0, B, 3))
+    assert np.all(o["draw_kind"][::3] == 2)
+
+
 def test_binding_rejects_bad_tensors():
     inp = synth.make_inputs("tiny", seed=0, device="cuda")
     with pytest.raises(ValueError):
