@@ -546,9 +546,10 @@ __device__ __forceinline__ unsigned add_low16(unsigned base, unsigned x) {
   return r;
 }
 
-// LDS addresses (table base + byte offset) of the two codes of w.
+// LDS addresses (table base + byte offset) of the two codes of w; `out`
+// gains nonzero bits when one of them lies outside the table (-inf included).
 __device__ __forceinline__ void etab_addresses(unsigned w, unsigned base, unsigned& a0,
-                                               unsigned& a1, unsigned& flag) {
+                                               unsigned& a1, unsigned& out) {
   const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
   const u16x2 t = mag - static_cast<u16x2>(static_cast<unsigned short>(kETabLo));
   const u16x2 tc = __builtin_elementwise_min(t, static_cast<u16x2>(static_cast<unsigned short>(kETabN)));
@@ -557,10 +558,19 @@ __device__ __forceinline__ void etab_addresses(unsigned w, unsigned base, unsign
   const unsigned off = tc8 | ((w >> 1) & 0x40004000u);  // each half's sign bit -> 0x4000
   a0 = add_low16(base, off);
   a1 = base + (off >> 16);
+  out |= __builtin_bit_cast(unsigned, __builtin_elementwise_sub_sat(
+                                          t, static_cast<u16x2>(static_cast<unsigned short>(
+                                                 kETabN - 1))));  // 0 iff in the table
+}
+
+// Nonzero when a code of w is neither in the table nor infinite.
+__device__ __forceinline__ unsigned etab_other_word(unsigned w) {
+  const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
+  const u16x2 t = mag - static_cast<u16x2>(static_cast<unsigned short>(kETabLo));
   const u16x2 out = __builtin_elementwise_sub_sat(
-      t, static_cast<u16x2>(static_cast<unsigned short>(kETabN - 1)));  // 0 iff in the table
+      t, static_cast<u16x2>(static_cast<unsigned short>(kETabN - 1)));
   const u16x2 ninf = mag ^ static_cast<u16x2>(static_cast<unsigned short>(0x7F80u));  // 0 iff +-inf
-  flag |= __builtin_bit_cast(unsigned, __builtin_elementwise_min(out, ninf));
+  return __builtin_bit_cast(unsigned, __builtin_elementwise_min(out, ninf));
 }
 
 // The 8 bf16 codes of z (stored values, -inf past V) as 4 words.
@@ -580,16 +590,24 @@ __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned 
   const LdsDouble et = (LdsDouble)(R.et + (P ? kETab : 0));  // the tables live in LDS
   const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(et));
   unsigned a[2 * NW];
-  unsigned flag = 0;
+  unsigned out = 0;
 #pragma unroll
-  for (int k = 0; k < NW; ++k) etab_addresses(w[k], base, a[2 * k], a[2 * k + 1], flag);
+  for (int k = 0; k < NW; ++k) etab_addresses(w[k], base, a[2 * k], a[2 * k + 1], out);
 #pragma unroll
   for (int k = 0; k < 2 * NW; ++k) e[k] = *(LdsDouble)(static_cast<uintptr_t>(a[k]));
-  if (__builtin_amdgcn_ballot_w64(flag != 0u) != 0ull) {
+  // A code outside the table is rare in a plain row; -inf (a filtered row)
+  // reads its 0 correctly, so only finite codes outside it are computed.
+  if (__builtin_amdgcn_ballot_w64(out != 0u) != 0ull) {
+    unsigned other = 0;
 #pragma unroll
-    for (int k = 0; k < 2 * NW; ++k) {
-      const unsigned b = (w[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
-      if (etab_other(b)) e[k] = tok_exp(__uint_as_float(b << 16), R.yscale, P ? R.mp : R.mq, tab);
+    for (int k = 0; k < NW; ++k) other |= etab_other_word(w[k]);
+    if (__builtin_amdgcn_ballot_w64(other != 0u) != 0ull) {
+#pragma unroll
+      for (int k = 0; k < 2 * NW; ++k) {
+        const unsigned b = (w[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
+        if (etab_other(b))
+          e[k] = tok_exp(__uint_as_float(b << 16), R.yscale, P ? R.mp : R.mq, tab);
+      }
     }
   }
 }
