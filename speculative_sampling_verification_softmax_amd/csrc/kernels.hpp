@@ -374,17 +374,24 @@ __global__ __launch_bounds__(kWave) void verify_kernel(
 // lanes contiguous); one wave owns a chunk at a time and loads the next one
 // while it computes the current one.
 //
+// For a residual every e_q is taken times the draft row's fp32 normaliser
+// s~_p from the stats and every e_p times s~_q (the factors cq, cp of
+// DrawRows; the tables hold the products), so that e_q >= e_p reads as
+// q >= p up to the stats' rounding.  The draw is unchanged: q = e_q/S_q with
+// S_q the sum of the same scaled values.
+//
 // Fast path, one sweep over the row(s): every token's e_q, e_p (fp64 table
 // exponential) go into the normalisers S_q, S_p; the sign of the residual is
-// decided with the fp32 normalisers s~ from the stats, e_q*s~_p versus
-// e_p*s~_q, with a relative margin kDelta.  Tokens clearly positive add e_q
-// and e_p to the chunk's sums A_c, B_c; tokens clearly negative add nothing;
-// the few inside the margin are recorded (up to kUncMax per chunk) and
-// resolved once S_q, S_p are exact.  Then W_c = A_c/S_q - B_c/S_p (+ the
-// resolved tokens).  If the exact ratio S_q/S_p falls outside s~_q/s~_p by
-// more than kDelta/4, a chunk records more uncertain tokens than it can hold,
-// or the residual has no mass, the draw takes the exact slow path instead:
-// normalisers first, then every chunk's weights, two sweeps.
+// decided on the scaled values with a relative margin kDelta: e_q >=
+// (1+kDelta) e_p is certainly positive, e_q <= (1-kDelta) e_p certainly not.
+// Tokens clearly positive add e_q and e_p to the chunk's sums A_c, B_c;
+// tokens clearly negative add nothing; the few inside the margin are recorded
+// (up to kUncMax per chunk) and resolved once S_q, S_p are exact.  Then
+// W_c = A_c/S_q - B_c/S_p (+ the resolved tokens).  If the exact ratio
+// S_q/S_p falls outside 1 by more than kDelta/4, a chunk records more
+// uncertain tokens than it can hold, or the residual has no mass, the draw
+// takes the exact slow path instead: normalisers first, then every chunk's
+// weights, two sweeps.
 //
 // Draw: running prefix over chunk totals in chunk order (wave 0), the first
 // chunk whose inclusive prefix exceeds u*S_w, then that chunk's weights are
@@ -397,6 +404,20 @@ enum : int { kModeResidual = 0, kModeBonus = 1 };
 constexpr int kUncMax = 2;
 constexpr double kDelta = 1.0 / 65536.0;
 
+// -(1 + kDelta) and -(1 - kDelta) (their low words are 0) as wave-uniform
+// registers, so that fma(e_p, k, e_q) is one v_fma_f64 (a literal operand
+// would make it a copy and a v_fmac).
+static_assert(-(1.0 + kDelta) == -1.0000152587890625 && -(1.0 - kDelta) == -0.9999847412109375,
+              "the high words below encode -(1 +- 2^-16)");
+__device__ __forceinline__ double uniform_margin(bool upper) {
+  unsigned h;
+  if (upper)
+    asm("s_mov_b32 %0, 0xbff00010" : "=s"(h));
+  else
+    asm("s_mov_b32 %0, 0xbfefffe0" : "=s"(h));
+  return __hiloint2double(static_cast<int>(h), 0);
+}
+
 struct DrawRows {
   const void* qrow;
   const void* prow;
@@ -405,7 +426,7 @@ struct DrawRows {
   bool aligned;       // both rows start on 16-byte boundaries
   double yscale;      // (1/T) * 256/ln2
   double mq, mp;      // row maxima (exact stored logits)
-  double sq_t, sp_t;  // fp32 normalisers from the stats (approximate)
+  double cq, cp;      // factors on e_q and e_p: s~_p and s~_q for a residual, else 1
   const double* et;   // bf16 exponential tables in LDS (q row, then p row), or null
 };
 
@@ -427,8 +448,8 @@ __device__ __forceinline__ bool make_draw_rows(int64_t b, int n, int K, int V, c
   R.yscale = yscale;
   R.mq = mq;
   R.mp = resid ? mp : 0.0;
-  R.sq_t = sq;
-  R.sp_t = resid ? sp : 1.0;
+  R.cq = resid ? sp : 1.0;
+  R.cp = resid ? sq : 1.0;
   R.et = nullptr;
   return row_ok(mq, sq) && (!resid || row_ok(mp, sp));
 }
@@ -440,12 +461,18 @@ __device__ __forceinline__ double tok_exp(float z, double yscale, double m, cons
   return exp64_scaled((static_cast<double>(z) - m) * yscale, tab);
 }
 
+// e of a token of the q row (P false) or the p row of R, times its factor.
+template <bool P>
+__device__ __forceinline__ double row_tok_exp(const DrawRows& R, float z, const double* tab) {
+  return tok_exp(z, R.yscale, P ? R.mp : R.mq, tab) * (P ? R.cp : R.cq);
+}
+
 // bf16 rows hold few distinct values: every z with 2^-7 <= |z| < 2^6 is one
 // of 2 * 13 * 128 codes.  A workgroup that draws from a row can fill a table
-// of tok_exp over those codes once (kETab doubles per row: a block of
+// of row_tok_exp over those codes once (kETab doubles per row: a block of
 // kETabSign entries per sign, the codes in order and then 0s) and look tokens
 // up instead of evaluating the exponential; other values are computed.  The
-// table holds tok_exp's own results, so both ways give the same bits.  With
+// table holds row_tok_exp's own results, so both ways give the same bits.  With
 // t = |code| - kETabLo (unsigned), a code's entry is sign * kETabSign +
 // min(t, kETabN): every code outside the table, -inf included, lands on a 0.
 constexpr unsigned kETabLo = 120u << 7;  // bf16 bits of 2^-7, sign cleared
@@ -453,20 +480,20 @@ constexpr unsigned kETabN = 13u << 7;    // codes per sign: exponents 2^-7 .. 2^
 constexpr unsigned kETabSign = 2048;     // entries per sign block (a power of two)
 constexpr int kETab = 2 * static_cast<int>(kETabSign);  // doubles per row
 
-// Fills the tables of `rows` rows (1 or 2; row r has maximum m[r]) at et,
-// kETab doubles apart: row by row (m stays wave-uniform), the kETabN codes
-// of each sign block spread evenly over the workgroup, then each block's 0
-// (entries past it are never read).
+// Fills the tables of `rows` rows (1 or 2: the q row of R, then its p row)
+// at et, kETab doubles apart: row by row (m stays wave-uniform), the kETabN
+// codes of each sign block spread evenly over the workgroup, then each
+// block's 0 (entries past it are never read).
 template <int BLOCK>
-__device__ __forceinline__ void fill_row_exp_tables(double* et, int rows, double yscale,
-                                                    const double (&m)[2], const double* tab) {
+__device__ __forceinline__ void fill_row_exp_tables(double* et, int rows, const DrawRows& R,
+                                                    const double* tab) {
   constexpr unsigned NC = 2 * kETabN;  // codes per row
   for (int r = 0; r < rows; ++r) {
-    const double mr = r == 0 ? m[0] : m[1];
     for (unsigned k = threadIdx.x; k < NC; k += BLOCK) {
       const unsigned sg = k >= kETabN ? 1u : 0u, i = k - sg * kETabN;
-      const unsigned code = (kETabLo + i) | (sg << 15);
-      et[r * kETab + sg * kETabSign + i] = tok_exp(__uint_as_float(code << 16), yscale, mr, tab);
+      const float z = __uint_as_float(((kETabLo + i) | (sg << 15)) << 16);
+      et[r * kETab + sg * kETabSign + i] =
+          r == 0 ? row_tok_exp<false>(R, z, tab) : row_tok_exp<true>(R, z, tab);
     }
   }
   if (threadIdx.x < 2 * rows)
@@ -494,11 +521,11 @@ __device__ __forceinline__ double row_exp(const DrawRows& R, float z, const doub
     double e = R.et[(P ? kETab : 0) + etab_index(b)];
     const bool other = etab_other(b);
     if (__builtin_amdgcn_ballot_w64(other) != 0ull) {
-      if (other) e = tok_exp(z, R.yscale, P ? R.mp : R.mq, tab);
+      if (other) e = row_tok_exp<P>(R, z, tab);
     }
     return e;
   }
-  return tok_exp(z, R.yscale, P ? R.mp : R.mq, tab);
+  return row_tok_exp<P>(R, z, tab);
 }
 
 // row_exp for H tokens of one row at once: the table reads are issued
@@ -519,48 +546,47 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
     if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
 #pragma unroll
       for (int k = 0; k < H; ++k)
-        if (other[k]) e[k] = tok_exp(z[k], R.yscale, P ? R.mp : R.mq, tab);
+        if (other[k]) e[k] = row_tok_exp<P>(R, z[k], tab);
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < H; ++k) e[k] = tok_exp(z[k], R.yscale, P ? R.mp : R.mq, tab);
+    for (int k = 0; k < H; ++k) e[k] = row_tok_exp<P>(R, z[k], tab);
   }
 }
 
 // The same lookups from the raw words of a bf16 row (two codes per word, the
 // lower token id in the low half), with the index arithmetic done on both
-// halves at once in 16-bit lanes.  A word's flag is nonzero when one of its
-// codes is neither in the table nor -inf.
+// halves at once in 16-bit lanes.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-static_assert(kETabSign * 8 == 0x4000u && kETabN * 8 <= 0x4000u, "sign bit -> byte 0x4000");
+static_assert(kETabSign == 1u << 11 && kETabN < kETabSign, "sign bit 15 -> entry bit 11");
 
-// The low 16 bits of x + a wave-uniform base, in one instruction (an SDWA
-// word select; the compiler otherwise masks and adds).
-__device__ __forceinline__ unsigned add_low16(unsigned base, unsigned x) {
+// base + 8 * (low or high 16 bits of x), one v_mad_u32_u16 each (its op_sel
+// picks the half; the compiler otherwise extracts, shifts and adds).
+__device__ __forceinline__ unsigned lds_entry_lo(unsigned x, unsigned base) {
   unsigned r;
-  asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 "
-      "src1_sel:DWORD"
-      : "=v"(r)
-      : "v"(x), "s"(base));
+  asm("v_mad_u32_u16 %0, %1, 8, %2" : "=v"(r) : "v"(x), "s"(base));
+  return r;
+}
+__device__ __forceinline__ unsigned lds_entry_hi(unsigned x, unsigned base) {
+  unsigned r;
+  asm("v_mad_u32_u16 %0, %1, 8, %2 op_sel:[1,0,0,0]" : "=v"(r) : "v"(x), "s"(base));
   return r;
 }
 
-// LDS addresses (table base + byte offset) of the two codes of w; `out`
-// gains nonzero bits when one of them lies outside the table (-inf included).
+// LDS addresses (table base + 8 * entry) of the two codes of w.  mx keeps
+// per half the largest clamped offset seen: kETabN there means a code outside
+// the table (-inf included).
 __device__ __forceinline__ void etab_addresses(unsigned w, unsigned base, unsigned& a0,
-                                               unsigned& a1, unsigned& out) {
+                                               unsigned& a1, u16x2& mx) {
   const u16x2 mag = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu);
   const u16x2 t = mag - static_cast<u16x2>(static_cast<unsigned short>(kETabLo));
   const u16x2 tc = __builtin_elementwise_min(t, static_cast<u16x2>(static_cast<unsigned short>(kETabN)));
-  const unsigned tc8 =
-      __builtin_bit_cast(unsigned, tc << static_cast<u16x2>(static_cast<unsigned short>(3)));
-  const unsigned off = tc8 | ((w >> 1) & 0x40004000u);  // each half's sign bit -> 0x4000
-  a0 = add_low16(base, off);
-  a1 = base + (off >> 16);
-  out |= __builtin_bit_cast(unsigned, __builtin_elementwise_sub_sat(
-                                          t, static_cast<u16x2>(static_cast<unsigned short>(
-                                                 kETabN - 1))));  // 0 iff in the table
+  mx = __builtin_elementwise_max(mx, tc);
+  // each half's sign bit (15) moves to bit 11: + kETabSign for a negative code
+  const unsigned idx = __builtin_bit_cast(unsigned, tc) | ((w >> 4) & 0x08000800u);
+  a0 = lds_entry_lo(idx, base);
+  a1 = lds_entry_hi(idx, base);
 }
 
 // Nonzero when a code of w is neither in the table nor infinite.
@@ -590,11 +616,15 @@ __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned 
   const LdsDouble et = (LdsDouble)(R.et + (P ? kETab : 0));  // the tables live in LDS
   const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(et));
   unsigned a[2 * NW];
-  unsigned out = 0;
+  u16x2 mx = static_cast<u16x2>(static_cast<unsigned short>(0));
 #pragma unroll
-  for (int k = 0; k < NW; ++k) etab_addresses(w[k], base, a[2 * k], a[2 * k + 1], out);
+  for (int k = 0; k < NW; ++k) etab_addresses(w[k], base, a[2 * k], a[2 * k + 1], mx);
 #pragma unroll
   for (int k = 0; k < 2 * NW; ++k) e[k] = *(LdsDouble)(static_cast<uintptr_t>(a[k]));
+  // 0 iff every code was in the table
+  const unsigned out = __builtin_bit_cast(
+      unsigned, __builtin_elementwise_sub_sat(
+                    mx, static_cast<u16x2>(static_cast<unsigned short>(kETabN - 1))));
   // A code outside the table is rare in a plain row; -inf (a filtered row)
   // reads its 0 correctly, so only finite codes outside it are computed.
   if (__builtin_amdgcn_ballot_w64(out != 0u) != 0ull) {
@@ -605,8 +635,7 @@ __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned 
 #pragma unroll
       for (int k = 0; k < 2 * NW; ++k) {
         const unsigned b = (w[k / 2] >> (16 * (k % 2))) & 0xFFFFu;
-        if (etab_other(b))
-          e[k] = tok_exp(__uint_as_float(b << 16), R.yscale, P ? R.mp : R.mq, tab);
+        if (etab_other(b)) e[k] = row_tok_exp<P>(R, __uint_as_float(b << 16), tab);
       }
     }
   }
@@ -717,6 +746,7 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
   double a = 0.0, bb = 0.0;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
+  const double k_hi = uniform_margin(true), k_lo = uniform_margin(false);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e % H == 0) lookup(e, eqh, eph);
@@ -725,16 +755,18 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
     if (MODE == kModeResidual) {
       const double ep = eph[e % H];
       lsp = lsp + ep;
-      const double r = ep * R.sq_t;
-      const double d = fma(eq, R.sp_t, -r);  // e_q s~_p - e_p s~_q
-      // |d| >= kDelta r: the sign is certain (a token with e_q = e_p = 0 is
-      // certain and carries no weight)
-      const bool certain = fabs(d) >= r * kDelta;
+      // e_q, e_p carry the factors s~_p, s~_q.  Each fma rounds once, so its
+      // sign is exact: pos means e_q >= (1+kDelta) e_p (a token with
+      // e_q = e_p = 0 counts as positive and adds nothing), and lo <= 0 means
+      // e_q <= (1-kDelta) e_p; a token with neither is uncertain.
+      const double hi = fma(ep, k_hi, eq), lo = fma(ep, k_lo, eq);
+      // the masks straight from the comparisons (every lane is active here)
+      const unsigned long long pos_m = __ballot(hi >= 0.0), lo_m = __ballot(lo > 0.0);
       // 1.0 or 0.0 (high word only): clearly positive tokens add e_q and e_p
-      const double take = __hiloint2double((certain && d > 0.0) ? 0x3ff00000 : 0, 0);
+      const double take = __hiloint2double(hi >= 0.0 ? 0x3ff00000 : 0, 0);
       a = fma(take, eq, a);
       bb = fma(take, ep, bb);
-      unc_m[e] = ~__ballot(certain);  // every lane of the wave is active here
+      unc_m[e] = lo_m & ~pos_m;
     } else {
       a = a + eq;
     }
@@ -1050,7 +1082,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   if (R.mode == kModeResidual) {
     iq = 1.0 / Sq;
     ip = 1.0 / Sp;
-    const double ratio = (Sq / Sp) / (R.sq_t / R.sp_t);
+    const double ratio = Sq / Sp;  // the scaled sums: exact / fp32 normaliser ratio
     bool ok = fabs(ratio - 1.0) <= kDelta / 4;
     for (int c = tid; c < nch; c += BLOCK) {
       const double a = chunk_total(A, c), bv = chunk_total(Bv, c);
@@ -1186,8 +1218,7 @@ __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt,
   __syncthreads();
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the two rows' tables
-    const double m[2] = {R.mq, R.mp};
-    fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R.yscale, m, sh.tab);
+    fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R, sh.tab);
     __syncthreads();
     R.et = dyn;
     work = dyn + 2 * kETab;
@@ -1275,15 +1306,14 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
   R.yscale = yscale;
   R.mq = m;
   R.mp = 0.0;
-  R.sq_t = s;
-  R.sp_t = 1.0;
+  R.cq = 1.0;
+  R.cp = 1.0;
   R.et = nullptr;
   fill_exp2_table(sh.tab);
   __syncthreads();
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the row's table
-    const double m[2] = {R.mq, 0.0};
-    fill_row_exp_tables<BLOCK>(dyn, 1, R.yscale, m, sh.tab);
+    fill_row_exp_tables<BLOCK>(dyn, 1, R, sh.tab);
     __syncthreads();
     R.et = dyn;
     work = dyn + kETab;
