@@ -239,8 +239,10 @@ struct Exp64 {
   static constexpr double kFloor = -300000.0;
 };
 
-__device__ __forceinline__ void fill_exp2_table(double* tab) {
-  for (int j = threadIdx.x; j < Exp64::kTab; j += blockDim.x)
+// Threads first .. blockDim.x-1 fill the table.
+__device__ __forceinline__ void fill_exp2_table(double* tab, int first = 0) {
+  for (int j = static_cast<int>(threadIdx.x) - first; j < Exp64::kTab;
+       j += static_cast<int>(blockDim.x) - first)
     tab[j] = exp2(static_cast<double>(j) / Exp64::kTab);
 }
 

@@ -487,13 +487,23 @@ constexpr int kETab = 2 * static_cast<int>(kETabSign);  // doubles per row
 template <int BLOCK>
 __device__ __forceinline__ void fill_row_exp_tables(double* et, int rows, const DrawRows& R,
                                                     const double* tab) {
-  constexpr unsigned NC = 2 * kETabN;  // codes per row
+  constexpr unsigned NC = 2 * kETabN;        // codes per row
+  constexpr int J = (NC + BLOCK - 1) / BLOCK;  // entries per thread and row
+  // all of a thread's entries of a row at once: independent exponentials
   for (int r = 0; r < rows; ++r) {
-    for (unsigned k = threadIdx.x; k < NC; k += BLOCK) {
+    double v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const unsigned k = threadIdx.x + j * BLOCK;
       const unsigned sg = k >= kETabN ? 1u : 0u, i = k - sg * kETabN;
       const float z = __uint_as_float(((kETabLo + i) | (sg << 15)) << 16);
-      et[r * kETab + sg * kETabSign + i] =
-          r == 0 ? row_tok_exp<false>(R, z, tab) : row_tok_exp<true>(R, z, tab);
+      v[j] = r == 0 ? row_tok_exp<false>(R, z, tab) : row_tok_exp<true>(R, z, tab);
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const unsigned k = threadIdx.x + j * BLOCK;
+      const unsigned sg = k >= kETabN ? 1u : 0u, i = k - sg * kETabN;
+      if (k < NC) et[r * kETab + sg * kETabSign + i] = v[j];
     }
   }
   if (threadIdx.x < 2 * rows)
@@ -996,7 +1006,7 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
                          bool have_s = false, double Sq_in = 0.0, double Sp_in = 0.0) {
   constexpr int NW = BLOCK / kWave;
   constexpr int E = 16 / Elt<DT>::bytes;
-  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
+  const int tid = threadIdx.x, wv = uniform(tid / kWave), lane = lane_id();
   double iq = 1.0, ip = 1.0;
   if (R.mode == kModeResidual && have_s) {
     iq = 1.0 / Sq_in;
@@ -1142,7 +1152,7 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
                                           DrawShared<BLOCK>& sh) {
   constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int NW = BLOCK / kWave;
-  const int wv = threadIdx.x / kWave, lane = lane_id();
+  const int wv = uniform(static_cast<int>(threadIdx.x) / kWave), lane = lane_id();
   const int nch = (R.V + kWave * E - 1) / (kWave * E);
   int tok = -2;
   double Sq = 0.0, Sp = 0.0;
@@ -1190,14 +1200,15 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
 // the fast layout (A, Bv: nch doubles each; unc_n: nch ints; unc_idx:
 // nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow
 // path; with `etab` (bf16) the two rows' exponential tables come first.
-// n must be uniform across the workgroup.
+// n must be uniform across the workgroup.  tab_ready: sh.tab is already
+// filled (and a barrier has passed since).
 template <int BLOCK, int DT>
 __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt, const void* dft,
                                               const float* uni, const float* tstats,
                                               const float* dstats, int K, int V, double yscale,
                                               int fast, int etab, int32_t* out_tokens,
                                               int32_t* num_emitted, double* dyn,
-                                              DrawShared<BLOCK>& sh) {
+                                              DrawShared<BLOCK>& sh, bool tab_ready = false) {
   const int64_t K1 = K + 1;
   const int tid = threadIdx.x;
   if (n < 0 || n > K) {
@@ -1214,8 +1225,10 @@ __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt,
     }
     return;
   }
-  fill_exp2_table(sh.tab);
-  __syncthreads();
+  if (!tab_ready) {
+    fill_exp2_table(sh.tab);
+    __syncthreads();
+  }
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the two rows' tables
     fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R, sh.tab);
@@ -1248,8 +1261,8 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
 }
 
 // One workgroup per sequence (the spec_verify_sample path): wave 0 runs the
-// accept tests and the first-rejection scan (verify_seq), then the whole
-// workgroup draws the final token.  The same results as spec_verify followed
+// accept tests and the first-rejection scan (verify_seq) while the other
+// waves fill the exp2 table, then the whole workgroup draws the final token.  The same results as spec_verify followed
 // by spec_residual_sample, in one launch.
 template <int BLOCK, int DT>
 __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
@@ -1259,6 +1272,7 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
     double invT, double yscale, int fast, int etab, int32_t* __restrict__ num_accepted,
     int32_t* __restrict__ out_tokens, float* __restrict__ probs,
     int32_t* __restrict__ num_emitted) {
+  static_assert(BLOCK > kWave, "waves other than the first fill the exp2 table");
   extern __shared__ double dyn[];
   __shared__ DrawShared<BLOCK> sh;
   const int64_t b = blockIdx.x;
@@ -1267,12 +1281,14 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
                                         dstats + 2 * b * K, K, V, invT, num_accepted,
                                         out_tokens, probs, true);
     if (threadIdx.x == 0) sh.sel[0] = n;
+  } else {
+    fill_exp2_table(sh.tab, kWave);
   }
   __syncthreads();
   const int n = uniform(sh.sel[0]);
   __syncthreads();  // sel[] is reused by the draw
   draw_sequence<BLOCK, DT>(b, n, tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
-                           out_tokens, num_emitted, dyn, sh);
+                           out_tokens, num_emitted, dyn, sh, true);
 }
 
 // ============================================================ draft sampling
