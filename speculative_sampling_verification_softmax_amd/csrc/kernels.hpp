@@ -746,14 +746,22 @@ struct ChunkSums {
   int unc[kUncMax];
 };
 
+// An empty uncertain list.
+__device__ __forceinline__ void chunk_sums_init(ChunkSums& out) {
+  out.n_unc = 0;
+#pragma unroll
+  for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
+}
+
 // Fast-path arithmetic of one chunk.  lookup(e, eq, ep) gives the exponentials
 // of the lane's tokens e .. e+H-1 of the q row (and the p row for a residual).
-// Adds every token's e_q, e_p to the lane's lsq, lsp.
-template <int DT, int MODE, int H, bool RS, typename Lookup>
-__device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup lookup, double& lsq,
-                                              double& lsp, ChunkSums& out) {
+// Adds every token's e_q, e_p to the lane's lsq, lsp, the clearly positive
+// ones to a, bb, and the chunk's uncertain tokens to out's list.
+template <int DT, int MODE, int H, typename Lookup>
+__device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Lookup lookup,
+                                                 double& lsq, double& lsp, double& a, double& bb,
+                                                 ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
-  double a = 0.0, bb = 0.0;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
   const double k_hi = uniform_margin(true), k_lo = uniform_margin(false);
@@ -781,16 +789,6 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
       a = a + eq;
     }
   }
-  if constexpr (RS) {
-    out.A = wave_scan_rows(a);
-    out.Bv = MODE == kModeResidual ? wave_scan_rows(bb) : 0.0;
-  } else {
-    out.A = wave_sum_rows(a);
-    out.Bv = MODE == kModeResidual ? wave_sum_rows(bb) : 0.0;
-  }
-  out.n_unc = 0;
-#pragma unroll
-  for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
   if (MODE == kModeResidual) {
     const int x0 = c * (kWave * E) + lane_id() * E;
 #pragma unroll
@@ -809,27 +807,40 @@ __device__ __forceinline__ void chunk_sums_by(const DrawRows& R, int c, Lookup l
   }
 }
 
-// chunk_sums_by from the lane's values.
-template <int DT, int MODE, bool ET = false, bool RS = false>
-__device__ __forceinline__ void chunk_sums(const DrawRows& R, int c,
-                                           const float (&zq)[16 / Elt<DT>::bytes],
-                                           const float (&zp)[16 / Elt<DT>::bytes],
-                                           const double* tab, double& lsq, double& lsp,
-                                           ChunkSums& out) {
+// The sums a, bb of a sweep item into out.A, out.Bv (RS: in-row scans).
+template <int MODE, bool RS>
+__device__ __forceinline__ void chunk_reduce(double a, double bb, ChunkSums& out) {
+  if constexpr (RS) {
+    out.A = wave_scan_rows(a);
+    out.Bv = MODE == kModeResidual ? wave_scan_rows(bb) : 0.0;
+  } else {
+    out.A = wave_sum_rows(a);
+    out.Bv = MODE == kModeResidual ? wave_sum_rows(bb) : 0.0;
+  }
+}
+
+// chunk_accumulate from the lane's values.
+template <int DT, int MODE, bool ET = false>
+__device__ __forceinline__ void chunk_acc(const DrawRows& R, int c,
+                                          const float (&zq)[16 / Elt<DT>::bytes],
+                                          const float (&zp)[16 / Elt<DT>::bytes],
+                                          const double* tab, double& lsq, double& lsp, double& a,
+                                          double& bb, ChunkSums& out) {
   constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int H = E < 4 ? E : 4;  // tokens whose exponentials are formed together
   auto lookup = [&](int e, double (&eq)[H], double (&ep)[H]) {
     row_exp_n<DT, ET, false, H>(R, zq + e, tab, eq);
     if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, ep);
   };
-  chunk_sums_by<DT, MODE, H, RS>(R, c, lookup, lsq, lsp, out);
+  chunk_accumulate<DT, MODE, H>(R, c, lookup, lsq, lsp, a, bb, out);
 }
 
-// chunk_sums_by from the raw words of bf16 rows with the exponential tables.
-template <int MODE, bool RS>
-__device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const uint4& wq,
-                                                 const uint4& wp, const double* tab,
-                                                 double& lsq, double& lsp, ChunkSums& out) {
+// chunk_accumulate from the raw words of bf16 rows with the exponential tables.
+template <int MODE>
+__device__ __forceinline__ void chunk_acc_words(const DrawRows& R, int c, const uint4& wq,
+                                                const uint4& wp, const double* tab, double& lsq,
+                                                double& lsp, double& a, double& bb,
+                                                ChunkSums& out) {
   const unsigned q[4] = {wq.x, wq.y, wq.z, wq.w};
   const unsigned p[4] = {wp.x, wp.y, wp.z, wp.w};
   auto lookup = [&](int e, double (&eq)[4], double (&ep)[4]) {
@@ -840,54 +851,57 @@ __device__ __forceinline__ void chunk_sums_words(const DrawRows& R, int c, const
       row_exp_words<true, 2>(R, pw, tab, ep);
     }
   };
-  chunk_sums_by<kBF16, MODE, 4, RS>(R, c, lookup, lsq, lsp, out);
+  chunk_accumulate<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, a, bb, out);
 }
 
 
-// One wave sweeps chunks c0, c0+stride, ... < c1 with PF chunks' loads in
-// flight (a slot is refilled as soon as its chunk has been unpacked);
-// emit(c, sums) stores a chunk's results (RS: see ChunkSums).
-template <int DT, int MODE, int PF, bool ET = false, bool RS = false, typename Emit>
-__device__ __forceinline__ void wave_sweep(const DrawRows& R, int c0, int c1, int stride,
+// One wave sweeps items s0, s0+stride, ... < s1; item s is the chunks G*s ..
+// G*s+G-1 that are below nsub, added into one ChunkSums (one cross-lane
+// reduction per item).  The next chunk's loads are issued as soon as the
+// current one has been unpacked.  emit(s, sums) stores an item's results
+// (RS: see ChunkSums).
+template <int DT, int MODE, int G, bool ET = false, bool RS = false, typename Emit>
+__device__ __forceinline__ void wave_sweep(const DrawRows& R, int s0, int s1, int stride, int nsub,
                                            const double* tab, double& lsq, double& lsp,
                                            Emit emit) {
   constexpr int E = 16 / Elt<DT>::bytes;
-  RawChunk buf[PF];
-  bool full[PF];
-#pragma unroll
-  for (int j = 0; j < PF; ++j) {
-    const int c = c0 + j * stride;
-    full[j] = c < c1 && chunk_full<DT>(R, c);
-    if (full[j]) chunk_issue<DT, MODE>(R, c, buf[j]);
-  }
-  for (int base = c0; base < c1; base += PF * stride) {
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int c = base + j * stride;
-      if (c < c1) {
-        ChunkSums cs;
-        const int cn = c + PF * stride;
+  RawChunk buf;
+  bool full = s0 < s1 && chunk_full<DT>(R, G * s0);
+  if (full) chunk_issue<DT, MODE>(R, G * s0, buf);
+  for (int s = s0; s < s1; s += stride) {
+    ChunkSums cs;
+    chunk_sums_init(cs);
+    double a = 0.0, bb = 0.0;
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+      const int c = G * s + g;
+      if (c < nsub) {
+        // the chunk after c in this wave's order
+        const bool in_item = g + 1 < G && c + 1 < nsub;
+        const int cn = in_item ? c + 1 : G * (s + stride);
+        const bool has_next = in_item || s + stride < s1;
         if constexpr (DT == kBF16 && ET) {  // table lookups straight from the words
-          uint4 wq = buf[j].q, wp = buf[j].p;
-          if (!full[j]) {
+          uint4 wq = buf.q, wp = buf.p;
+          if (!full) {
             float zq[E], zp[E];
-            chunk_values<DT, MODE>(R, c, false, buf[j], zq, zp);
+            chunk_values<DT, MODE>(R, c, false, buf, zq, zp);
             wq = pack_bf16_words(zq);
             if (MODE == kModeResidual) wp = pack_bf16_words(zp);
           }
-          full[j] = cn < c1 && chunk_full<DT>(R, cn);
-          if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
-          chunk_sums_words<MODE, RS>(R, c, wq, wp, tab, lsq, lsp, cs);
+          full = has_next && chunk_full<DT>(R, cn);
+          if (full) chunk_issue<DT, MODE>(R, cn, buf);
+          chunk_acc_words<MODE>(R, c, wq, wp, tab, lsq, lsp, a, bb, cs);
         } else {
           float zq[E], zp[E];
-          chunk_values<DT, MODE>(R, c, full[j], buf[j], zq, zp);
-          full[j] = cn < c1 && chunk_full<DT>(R, cn);
-          if (full[j]) chunk_issue<DT, MODE>(R, cn, buf[j]);
-          chunk_sums<DT, MODE, ET, RS>(R, c, zq, zp, tab, lsq, lsp, cs);
+          chunk_values<DT, MODE>(R, c, full, buf, zq, zp);
+          full = has_next && chunk_full<DT>(R, cn);
+          if (full) chunk_issue<DT, MODE>(R, cn, buf);
+          chunk_acc<DT, MODE, ET>(R, c, zq, zp, tab, lsq, lsp, a, bb, cs);
         }
-        emit(c, cs);
       }
     }
+    chunk_reduce<MODE, RS>(a, bb, cs);
+    emit(s, cs);
   }
 }
 
@@ -948,11 +962,14 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
   }
 }
 
-// Token inside chunk c (wave 0): returns the token id in every lane, or -1.
+// Draw inside chunk c (wave 0), whose tokens follow a prefix excl: returns
+// the first token whose cumulative weight exceeds target (in every lane) when
+// crossing is set and one does, else -1 after adding the chunk's total to
+// excl and setting lastpos to its last token of positive weight, if any.
 template <int DT, int MODE, bool ET = false>
-__device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool crossing, double excl,
-                                             double target, double iq, double ip,
-                                             const double* tab) {
+__device__ __forceinline__ int draw_in_one_chunk(const DrawRows& R, int c, bool crossing,
+                                                 double& excl, double target, double iq,
+                                                 double ip, const double* tab, int& lastpos) {
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
   double w[E];
@@ -965,26 +982,51 @@ __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int c, bool cros
   const bool lane_hit = crossing && ls > 0.0 && (excl + incl) > target;
   const unsigned long long hm = __ballot(lane_hit);
   const unsigned long long pm = __ballot(ls > 0.0);
+  if (pm == 0ull) return -1;  // nothing of positive weight here (excl unchanged: all 0)
   const int src = hm ? (__ffsll(static_cast<long long>(hm)) - 1)
-                     : (pm ? 63 - __clzll(static_cast<long long>(pm)) : -1);
-  if (src < 0) return -1;
+                     : 63 - __clzll(static_cast<long long>(pm));
   int pick = -1;
   if (lane == src) {
     const double base = excl + lexcl;
-    int lastpos = -1;
+    int last = -1;
     double a = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       a = a + w[e];
       if (w[e] > 0.0) {
         if (pick < 0 && hm && (base + a) > target) pick = e;
-        lastpos = e;
+        last = e;
       }
     }
-    if (pick < 0) pick = lastpos;
+    if (pick < 0) pick = last;
   }
-  pick = __builtin_amdgcn_readlane(pick, src);
-  return c * (kWave * E) + src * E + pick;
+  pick = c * (kWave * E) + src * E + __builtin_amdgcn_readlane(pick, src);
+  if (hm) return pick;
+  lastpos = pick;
+  excl = excl + readlane_d(incl, kWave - 1);
+  return -1;
+}
+
+// Token inside sweep item s (its chunks G*s .. G*s+G-1 below the row's end),
+// in token order (wave 0): the crossing if `crossing` and one is found, else
+// the item's last token of positive weight; the token id in every lane, or -1.
+template <int DT, int MODE, bool ET = false, int G = 1>
+__device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int s, bool crossing, double excl,
+                                             double target, double iq, double ip,
+                                             const double* tab) {
+  constexpr int CH = kWave * (16 / Elt<DT>::bytes);
+  const int nsub = (R.V + CH - 1) / CH;
+  int last = -1;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int c = G * s + g;
+    if (c < nsub) {
+      const int tok = draw_in_one_chunk<DT, MODE, ET>(R, c, crossing, excl, target, iq, ip, tab,
+                                                      last);
+      if (tok >= 0) return tok;
+    }
+  }
+  return last;
 }
 
 // LDS the draw routines need, per workgroup.
@@ -1077,7 +1119,7 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 // barrier between the clearing and the call.  Returns the token, -1 (nothing
 // to draw), -2 (take the slow path) or -3 (the residual has no mass: draw
 // from q_n instead).
-template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false>
+template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false, int G = 1>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
                            double* W, double u, DrawShared<BLOCK>& sh) {
@@ -1130,10 +1172,10 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   int tok = -1;
   if (sh.sel[0] >= 0 && wv == 0)
     tok = R.mode == kModeResidual
-              ? draw_in_chunk<DT, kModeResidual, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                                     sh.seld[1], iq, ip, sh.tab)
-              : draw_in_chunk<DT, kModeBonus, ET>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
-                                                  sh.seld[1], iq, ip, sh.tab);
+              ? draw_in_chunk<DT, kModeResidual, ET, G>(R, sh.sel[0], sh.sel[1] != 0,
+                                                        sh.seld[0], sh.seld[1], iq, ip, sh.tab)
+              : draw_in_chunk<DT, kModeBonus, ET, G>(R, sh.sel[0], sh.sel[1] != 0, sh.seld[0],
+                                                     sh.seld[1], iq, ip, sh.tab);
   if (tid == 0) sh.sel[2] = tok;
   __syncthreads();
   tok = sh.sel[2];
@@ -1142,11 +1184,14 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 }
 
 // The whole draw for one row (pair) by one workgroup: the one-sweep fast path
-// when `fast` (dynamic LDS `dyn` then holds A, Bv: four row totals per chunk,
-// 4*nch doubles each; W: nch doubles; unc_n: nch ints; unc_idx: nch*kUncMax
-// ints), else or on its failure the exact two-sweep path (dyn: nch doubles).
+// when `fast`, else or on its failure the exact two-sweep path (dyn: nch
+// doubles).  The fast sweep's items are kDrawG chunks each, and dynamic LDS
+// `dyn` holds, for its ni items, A, Bv: four row totals per item, 4*ni
+// doubles each; W: ni doubles; unc_n: ni ints; unc_idx: ni*kUncMax ints
+// (within the slow path's nch doubles plus the fast layout per chunk).
 // sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
+constexpr int kDrawG = 2;
 template <int BLOCK, int DT, bool ET = false>
 __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
                                           DrawShared<BLOCK>& sh) {
@@ -1154,14 +1199,15 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
   constexpr int NW = BLOCK / kWave;
   const int wv = uniform(static_cast<int>(threadIdx.x) / kWave), lane = lane_id();
   const int nch = (R.V + kWave * E - 1) / (kWave * E);
+  const int ni = (nch + kDrawG - 1) / kDrawG;  // sweep items
   int tok = -2;
   double Sq = 0.0, Sp = 0.0;
   if (fast) {
     double* A = dyn;
-    double* Bv = A + 4 * nch;
-    double* W = Bv + 4 * nch;
-    int* unc_n = reinterpret_cast<int*>(W + nch);
-    int* unc_idx = unc_n + nch;
+    double* Bv = A + 4 * ni;
+    double* W = Bv + 4 * ni;
+    int* unc_n = reinterpret_cast<int*>(W + ni);
+    int* unc_idx = unc_n + ni;
     double lsq = 0.0, lsp = 0.0;
     auto emit = [&](int c, const ChunkSums& cs) {
       if ((lane & 15) == 15) {  // the row totals
@@ -1175,15 +1221,15 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
       }
     };
     if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeResidual, kDrawG, ET, true>(R, wv, ni, NW, nch, sh.tab, lsq, lsp, emit);
     else
-      wave_sweep<DT, kModeBonus, 1, ET, true>(R, wv, nch, NW, sh.tab, lsq, lsp, emit);
+      wave_sweep<DT, kModeBonus, kDrawG, ET, true>(R, wv, ni, NW, nch, sh.tab, lsq, lsp, emit);
     if (threadIdx.x == 0) sh.sel[3] = 0;
     Sq = block_sum<BLOCK>(lsq, sh.red);  // its barriers order the clear above
     Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false, ET, true>(
-        R, nch, Sq, Sp, Src<false, double>(A, 4 * nch), Src<false, double>(Bv, 4 * nch),
-        Src<false, int>(unc_n, nch), Src<false, int>(unc_idx, nch * kUncMax), W, u, sh);
+    tok = fast_finish<BLOCK, DT, false, ET, true, kDrawG>(
+        R, ni, Sq, Sp, Src<false, double>(A, 4 * ni), Src<false, double>(Bv, 4 * ni),
+        Src<false, int>(unc_n, ni), Src<false, int>(unc_idx, ni * kUncMax), W, u, sh);
   }
   if (tok == -3) {  // residual without mass: the bonus draw from q_n
     DrawRows Rb = R;
@@ -2214,9 +2260,9 @@ __global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a)
         }
       };
       if (R.mode == kModeResidual)
-        wave_sweep<DT, kModeResidual, 1>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+        wave_sweep<DT, kModeResidual, 1>(R, c0, c1, NW, a.nch, sh.d.tab, lsq, lsp, emit);
       else
-        wave_sweep<DT, kModeBonus, 1>(R, c0, c1, NW, sh.d.tab, lsq, lsp, emit);
+        wave_sweep<DT, kModeBonus, 1>(R, c0, c1, NW, a.nch, sh.d.tab, lsq, lsp, emit);
       const double Sq = block_sum<BLOCK>(lsq, sh.d.red);  // its barriers also order the LDS above
       const double Sp = block_sum<BLOCK>(lsp, sh.d.red);
       if (tid < c1 - cb) {
