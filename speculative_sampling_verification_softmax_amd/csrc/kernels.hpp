@@ -403,6 +403,14 @@ __global__ __launch_bounds__(kWave) void verify_kernel(
 enum : int { kModeResidual = 0, kModeBonus = 1 };
 constexpr int kUncMax = 2;
 constexpr double kDelta = 1.0 / 65536.0;
+constexpr int kDrawG = 2;  // chunks per item of the fast sweep
+
+// Dynamic LDS of the fast sweep for a row of nch chunks: per item, four row
+// totals of each of A, Bv, Lq, Lp, then W, then unc_n and kUncMax unc_idx.
+constexpr size_t draw_fast_lds(int nch) {
+  return static_cast<size_t>((nch + kDrawG - 1) / kDrawG) *
+         (17 * sizeof(double) + (1 + kUncMax) * sizeof(int));
+}
 
 // -(1 + kDelta) and -(1 - kDelta) (their low words are 0) as wave-uniform
 // registers, so that fma(e_p, k, e_q) is one v_fma_f64 (a literal operand
@@ -1037,6 +1045,7 @@ struct DrawShared {
   float redf[BLOCK / kWave];
   int sel[4];
   double seld[4];
+  unsigned next;  // the fast sweep's item counter
 };
 
 // Exact two-sweep draw (whole block).  W: nch doubles of scratch.  With
@@ -1183,15 +1192,75 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   return tok;
 }
 
+// The fast sweep of one workgroup in items of G chunks, handed out in the
+// order the waves ask for them: wave wv starts with item s0 = wv, and each
+// further item comes from the LDS counter *next (which starts at the number
+// of waves), claimed one item ahead so that its first chunk's loads are
+// issued while the current item is computed.  Waves that the hardware
+// schedules first take more items, and all finish within about one item of
+// each other.  Every sum is formed per item -- a, bb and the normaliser parts
+// lq, lp, each reduced to four row totals -- and emit(s, cs, lq, lp) stores
+// them by item, so no result depends on which wave took which item.
+template <int DT, int MODE, int G, bool ET, typename Emit>
+__device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, int ni, int nsub,
+                                                   unsigned* next, const double* tab,
+                                                   Emit emit) {
+  constexpr int E = 16 / Elt<DT>::bytes;
+  const int lane = lane_id();
+  RawChunk buf;
+  int s = s0;
+  bool full = s < ni && chunk_full<DT>(R, G * s);
+  if (full) chunk_issue<DT, MODE>(R, G * s, buf);
+  while (s < ni) {
+    unsigned claimed = 0;
+    if (lane == 0) claimed = atomicAdd(next, 1u);
+    const int sn = static_cast<int>(uniform(claimed));  // the item after this one
+    ChunkSums cs;
+    chunk_sums_init(cs);
+    double a = 0.0, bb = 0.0, lq = 0.0, lp = 0.0;
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+      const int c = G * s + g;
+      if (c < nsub) {
+        // the chunk after c in this wave's order
+        const bool in_item = g + 1 < G && c + 1 < nsub;
+        const int cn = in_item ? c + 1 : G * sn;
+        const bool has_next = in_item || sn < ni;
+        if constexpr (DT == kBF16 && ET) {  // table lookups straight from the words
+          uint4 wq = buf.q, wp = buf.p;
+          if (!full) {
+            float zq[E], zp[E];
+            chunk_values<DT, MODE>(R, c, false, buf, zq, zp);
+            wq = pack_bf16_words(zq);
+            if (MODE == kModeResidual) wp = pack_bf16_words(zp);
+          }
+          full = has_next && chunk_full<DT>(R, cn);
+          if (full) chunk_issue<DT, MODE>(R, cn, buf);
+          chunk_acc_words<MODE>(R, c, wq, wp, tab, lq, lp, a, bb, cs);
+        } else {
+          float zq[E], zp[E];
+          chunk_values<DT, MODE>(R, c, full, buf, zq, zp);
+          full = has_next && chunk_full<DT>(R, cn);
+          if (full) chunk_issue<DT, MODE>(R, cn, buf);
+          chunk_acc<DT, MODE, ET>(R, c, zq, zp, tab, lq, lp, a, bb, cs);
+        }
+      }
+    }
+    chunk_reduce<MODE, true>(a, bb, cs);
+    const double lqr = wave_scan_rows(lq);
+    const double lpr = MODE == kModeResidual ? wave_scan_rows(lp) : 0.0;
+    emit(s, cs, lqr, lpr);
+    s = sn;
+  }
+}
+
 // The whole draw for one row (pair) by one workgroup: the one-sweep fast path
 // when `fast`, else or on its failure the exact two-sweep path (dyn: nch
 // doubles).  The fast sweep's items are kDrawG chunks each, and dynamic LDS
-// `dyn` holds, for its ni items, A, Bv: four row totals per item, 4*ni
-// doubles each; W: ni doubles; unc_n: ni ints; unc_idx: ni*kUncMax ints
-// (within the slow path's nch doubles plus the fast layout per chunk).
-// sh.tab must hold the exp table.
+// `dyn` holds, for its ni items (draw_fast_lds bytes), A, Bv, Lq, Lp: four
+// row totals per item, 4*ni doubles each; W: ni doubles; unc_n: ni ints;
+// unc_idx: ni*kUncMax ints.  sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
-constexpr int kDrawG = 2;
 template <int BLOCK, int DT, bool ET = false>
 __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
                                           DrawShared<BLOCK>& sh) {
@@ -1205,14 +1274,18 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
   if (fast) {
     double* A = dyn;
     double* Bv = A + 4 * ni;
-    double* W = Bv + 4 * ni;
+    double* Lq = Bv + 4 * ni;
+    double* Lp = Lq + 4 * ni;
+    double* W = Lp + 4 * ni;
     int* unc_n = reinterpret_cast<int*>(W + ni);
     int* unc_idx = unc_n + ni;
-    double lsq = 0.0, lsp = 0.0;
-    auto emit = [&](int c, const ChunkSums& cs) {
+    auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) {
       if ((lane & 15) == 15) {  // the row totals
-        A[4 * c + (lane >> 4)] = cs.A;
-        Bv[4 * c + (lane >> 4)] = cs.Bv;
+        const int i = 4 * c + (lane >> 4);
+        A[i] = cs.A;
+        Bv[i] = cs.Bv;
+        Lq[i] = lq;
+        Lp[i] = lp;
       }
       if (lane == 0) {
         unc_n[c] = cs.n_unc;
@@ -1220,12 +1293,23 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
         for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
       }
     };
+    if (threadIdx.x == 0) {
+      sh.next = NW;
+      sh.sel[3] = 0;
+    }
+    __syncthreads();
     if (R.mode == kModeResidual)
-      wave_sweep<DT, kModeResidual, kDrawG, ET, true>(R, wv, ni, NW, nch, sh.tab, lsq, lsp, emit);
+      wave_sweep_claimed<DT, kModeResidual, kDrawG, ET>(R, wv, ni, nch, &sh.next, sh.tab, emit);
     else
-      wave_sweep<DT, kModeBonus, kDrawG, ET, true>(R, wv, ni, NW, nch, sh.tab, lsq, lsp, emit);
-    if (threadIdx.x == 0) sh.sel[3] = 0;
-    Sq = block_sum<BLOCK>(lsq, sh.red);  // its barriers order the clear above
+      wave_sweep_claimed<DT, kModeBonus, kDrawG, ET>(R, wv, ni, nch, &sh.next, sh.tab, emit);
+    __syncthreads();
+    // the exact normalisers: item parts in item order, then a fixed tree
+    double lsq = 0.0, lsp = 0.0;
+    for (int c = threadIdx.x; c < ni; c += BLOCK) {
+      lsq = lsq + sum_row_totals(Lq[4 * c], Lq[4 * c + 1], Lq[4 * c + 2], Lq[4 * c + 3]);
+      lsp = lsp + sum_row_totals(Lp[4 * c], Lp[4 * c + 1], Lp[4 * c + 2], Lp[4 * c + 3]);
+    }
+    Sq = block_sum<BLOCK>(lsq, sh.red);
     Sp = block_sum<BLOCK>(lsp, sh.red);
     tok = fast_finish<BLOCK, DT, false, ET, true, kDrawG>(
         R, ni, Sq, Sp, Src<false, double>(A, 4 * ni), Src<false, double>(Bv, 4 * ni),

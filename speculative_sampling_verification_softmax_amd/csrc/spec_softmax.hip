@@ -58,8 +58,7 @@ struct DrawLds {
 
 DrawLds draw_lds(int nch, int dtype, int rows) {
   DrawLds d{};
-  const size_t fast_lds = static_cast<size_t>(nch) *
-                          (9 * sizeof(double) + (1 + spec::kUncMax) * sizeof(int));
+  const size_t fast_lds = spec::draw_fast_lds(nch);
   d.fast = fast_lds <= kResidFastLds ? 1 : 0;
   const size_t work = d.fast ? fast_lds : static_cast<size_t>(nch) * sizeof(double);
   const size_t tables = static_cast<size_t>(rows) * spec::kETab * sizeof(double);
