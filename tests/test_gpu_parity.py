@@ -168,3 +168,26 @@ def test_two_call_equals_three_call_bit_for_bit(wl):
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     for k in ("target_stats", "draft_stats", "probs"):
         assert a[k].tobytes() == b[k].tobytes(), k
+
+
+def test_two_call_repeats_bit_for_bit_under_load():
+    """The draw's sweep hands its items to waves in the order the hardware
+    schedules them, and every sum is formed per item and added in item order:
+    repeated calls, with another stream's copies competing for the CUs, give
+    identical bits."""
+    inp = synth.make_inputs("headline", seed=3, device="cuda")
+    torch.cuda.synchronize()
+    say("[repeat] headline two_call: reference call")
+    first = parity.gpu_verify(inp, path="two_call")
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    for rep in range(4):
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                dst.copy_(src)
+        say(f"[repeat] call {rep} with copies on a second stream")
+        b = parity.gpu_verify(inp, path="two_call")
+        torch.cuda.synchronize()
+        for k in first:
+            np.testing.assert_array_equal(first[k], b[k], err_msg=f"{k} repeat {rep}")
