@@ -96,6 +96,11 @@ RAGGED = [
     (1, 1, "bf16", 3), (2, 2, "f32", 5), (63, 3, "bf16", 7), (65, 4, "f32", 9),
     (777, 5, "bf16", 11), (1001, 2, "f32", 6), (4097, 64, "bf16", 3), (40000, 7, "f32", 5),
     (129, 64, "f32", 2), (32003, 3, "bf16", 17),
+    # the draw's fast sweep takes items of two 16-byte-per-lane chunks (1024 bf16 or 512 fp32
+    # tokens) across 16 waves: fewer items than waves, exactly 16, one more (with a lone or
+    # ragged last chunk)
+    (15360, 3, "bf16", 8), (16384, 3, "bf16", 8), (16385, 3, "bf16", 8), (16896, 2, "bf16", 6),
+    (8192, 3, "f32", 8), (8449, 2, "f32", 6),
 ]
 
 
