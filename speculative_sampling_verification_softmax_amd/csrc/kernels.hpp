@@ -406,10 +406,11 @@ constexpr double kDelta = 1.0 / 65536.0;
 constexpr int kDrawG = 2;  // chunks per item of the fast sweep
 
 // Dynamic LDS of the fast sweep for a row of nch chunks: per item, four row
-// totals of each of A, Bv, Lq, Lp, then W, then unc_n and kUncMax unc_idx.
+// totals of each of A, Bv, Lq, Lp, then W, then unc_n, kUncMax unc_idx and
+// kUncMax unc_code.
 constexpr size_t draw_fast_lds(int nch) {
   return static_cast<size_t>((nch + kDrawG - 1) / kDrawG) *
-         (17 * sizeof(double) + (1 + kUncMax) * sizeof(int));
+         (17 * sizeof(double) + (1 + 2 * kUncMax) * sizeof(int));
 }
 
 // -(1 + kDelta) and -(1 - kDelta) (their low words are 0) as wave-uniform
@@ -701,14 +702,21 @@ __device__ __forceinline__ void chunk_values(const DrawRows& R, int c, bool full
 }
 
 // Exact weights of this lane's E tokens (used to re-derive the chosen chunk).
+// pre: the chunk's loads, already issued (for a full chunk), or null.
 template <int DT, int MODE, bool ET = false>
 __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq, double ip,
                                              const double* tab,
-                                             double (&w)[16 / Elt<DT>::bytes]) {
+                                             double (&w)[16 / Elt<DT>::bytes],
+                                             const RawChunk* pre = nullptr) {
   constexpr int E = 16 / Elt<DT>::bytes;
   RawChunk raw;
   const bool full = chunk_full<DT>(R, c);
-  if (full) chunk_issue<DT, MODE>(R, c, raw);
+  if (full) {
+    if (pre != nullptr)
+      raw = *pre;
+    else
+      chunk_issue<DT, MODE>(R, c, raw);
+  }
   float zq[E], zp[E];
   chunk_values<DT, MODE>(R, c, full, raw, zq, zp);
   if constexpr (DT == kBF16 && ET) {  // all table reads at once, from the words
@@ -752,23 +760,29 @@ struct ChunkSums {
   double A, Bv;
   int n_unc;
   int unc[kUncMax];
+  unsigned ucode[kUncMax];  // bf16 words path: the token's q code | p code << 16
 };
 
 // An empty uncertain list.
 __device__ __forceinline__ void chunk_sums_init(ChunkSums& out) {
   out.n_unc = 0;
 #pragma unroll
-  for (int j = 0; j < kUncMax; ++j) out.unc[j] = -1;
+  for (int j = 0; j < kUncMax; ++j) {
+    out.unc[j] = -1;
+    out.ucode[j] = 0u;
+  }
 }
 
 // Fast-path arithmetic of one chunk.  lookup(e, eq, ep) gives the exponentials
 // of the lane's tokens e .. e+H-1 of the q row (and the p row for a residual).
 // Adds every token's e_q, e_p to the lane's lsq, lsp, the clearly positive
-// ones to a, bb, and the chunk's uncertain tokens to out's list.
+// ones to a, bb, and the chunk's uncertain tokens to out's list -- with their
+// two bf16 codes when words (the lane's 4+4 raw words of a bf16 chunk) is set.
 template <int DT, int MODE, int H, typename Lookup>
 __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Lookup lookup,
                                                  double& lsq, double& lsp, double& a, double& bb,
-                                                 ChunkSums& out) {
+                                                 ChunkSums& out,
+                                                 const unsigned* words = nullptr) {
   constexpr int E = 16 / Elt<DT>::bytes;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
@@ -805,9 +819,18 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
       while (m) {  // wave-uniform; rare
         const int src = __ffsll(static_cast<long long>(m)) - 1;
         const int idx = __shfl(x0, src, kWave) + e;
+        unsigned code = 0u;
+        if (words != nullptr) {  // token e sits in word e/2, lower id in the low half
+          const unsigned wq = static_cast<unsigned>(__shfl(static_cast<int>(words[e / 2]), src, kWave));
+          const unsigned wp = static_cast<unsigned>(__shfl(static_cast<int>(words[4 + e / 2]), src, kWave));
+          code = (e & 1) ? ((wq >> 16) | (wp & 0xFFFF0000u)) : ((wq & 0xFFFFu) | (wp << 16));
+        }
 #pragma unroll
         for (int j = 0; j < kUncMax; ++j)
-          if (j == out.n_unc) out.unc[j] = idx;
+          if (j == out.n_unc) {
+            out.unc[j] = idx;
+            out.ucode[j] = code;
+          }
         out.n_unc += 1;
         m &= m - 1;
       }
@@ -849,17 +872,16 @@ __device__ __forceinline__ void chunk_acc_words(const DrawRows& R, int c, const 
                                                 const uint4& wp, const double* tab, double& lsq,
                                                 double& lsp, double& a, double& bb,
                                                 ChunkSums& out) {
-  const unsigned q[4] = {wq.x, wq.y, wq.z, wq.w};
-  const unsigned p[4] = {wp.x, wp.y, wp.z, wp.w};
+  const unsigned w8[8] = {wq.x, wq.y, wq.z, wq.w, wp.x, wp.y, wp.z, wp.w};
   auto lookup = [&](int e, double (&eq)[4], double (&ep)[4]) {
-    const unsigned qw[2] = {q[e / 2], q[e / 2 + 1]};
+    const unsigned qw[2] = {w8[e / 2], w8[e / 2 + 1]};
     row_exp_words<false, 2>(R, qw, tab, eq);
     if (MODE == kModeResidual) {
-      const unsigned pw[2] = {p[e / 2], p[e / 2 + 1]};
+      const unsigned pw[2] = {w8[4 + e / 2], w8[4 + e / 2 + 1]};
       row_exp_words<true, 2>(R, pw, tab, ep);
     }
   };
-  chunk_accumulate<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, a, bb, out);
+  chunk_accumulate<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, a, bb, out, w8);
 }
 
 
@@ -977,11 +999,12 @@ __device__ __forceinline__ void locate_chunk(const double* W, int nch, double u,
 template <int DT, int MODE, bool ET = false>
 __device__ __forceinline__ int draw_in_one_chunk(const DrawRows& R, int c, bool crossing,
                                                  double& excl, double target, double iq,
-                                                 double ip, const double* tab, int& lastpos) {
+                                                 double ip, const double* tab, int& lastpos,
+                                                 const RawChunk* pre = nullptr) {
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
   double w[E];
-  lane_weights<DT, MODE, ET>(R, c, iq, ip, tab, w);
+  lane_weights<DT, MODE, ET>(R, c, iq, ip, tab, w, pre);
   double ls = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) ls = ls + w[e];
@@ -1024,13 +1047,20 @@ __device__ __forceinline__ int draw_in_chunk(const DrawRows& R, int s, bool cros
                                              const double* tab) {
   constexpr int CH = kWave * (16 / Elt<DT>::bytes);
   const int nsub = (R.V + CH - 1) / CH;
+  // every chunk's loads at once: a later chunk's latency hides behind the earlier scans
+  RawChunk pre[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int c = G * s + g;
+    if (c < nsub && chunk_full<DT>(R, c)) chunk_issue<DT, MODE>(R, c, pre[g]);
+  }
   int last = -1;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int c = G * s + g;
     if (c < nsub) {
       const int tok = draw_in_one_chunk<DT, MODE, ET>(R, c, crossing, excl, target, iq, ip, tab,
-                                                      last);
+                                                      last, &pre[g]);
       if (tok >= 0) return tok;
     }
   }
@@ -1131,7 +1161,8 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
 template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false, int G = 1>
 __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
                            Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
-                           double* W, double u, DrawShared<BLOCK>& sh) {
+                           double* W, double u, DrawShared<BLOCK>& sh,
+                           const unsigned* unc_code = nullptr) {
   const int tid = threadIdx.x, wv = tid / kWave;
   auto chunk_total = [&](const Src<XB, double>& X, int c) {
     if constexpr (RS)
@@ -1157,8 +1188,19 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
 #pragma unroll
       for (int j = 0; j < kUncMax; ++j) {
         if (j < nu) {
-          const double eq = row_exp<DT, ET, false>(R, logit_f32<DT>(R.qrow, x[j]), sh.tab);
-          const double ep = row_exp<DT, ET, true>(R, logit_f32<DT>(R.prow, x[j]), sh.tab);
+          // the token's stored logits: the codes the sweep kept (bf16 words
+          // path, exact), else read back from the rows
+          float zq, zp;
+          if (DT == kBF16 && unc_code != nullptr) {
+            const unsigned cw = unc_code[static_cast<int64_t>(c) * kUncMax + j];
+            zq = __uint_as_float(cw << 16);
+            zp = __uint_as_float(cw & 0xFFFF0000u);
+          } else {
+            zq = logit_f32<DT>(R.qrow, x[j]);
+            zp = logit_f32<DT>(R.prow, x[j]);
+          }
+          const double eq = row_exp<DT, ET, false>(R, zq, sh.tab);
+          const double ep = row_exp<DT, ET, true>(R, zp, sh.tab);
           const double d = eq * iq - ep * ip;
           w = w + (d > 0.0 ? d : 0.0);
         }
@@ -1259,7 +1301,7 @@ __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, in
 // doubles).  The fast sweep's items are kDrawG chunks each, and dynamic LDS
 // `dyn` holds, for its ni items (draw_fast_lds bytes), A, Bv, Lq, Lp: four
 // row totals per item, 4*ni doubles each; W: ni doubles; unc_n: ni ints;
-// unc_idx: ni*kUncMax ints.  sh.tab must hold the exp table.
+// unc_idx, unc_code: ni*kUncMax ints each.  sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
 template <int BLOCK, int DT, bool ET = false>
 __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
@@ -1279,6 +1321,7 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
     double* W = Lp + 4 * ni;
     int* unc_n = reinterpret_cast<int*>(W + ni);
     int* unc_idx = unc_n + ni;
+    unsigned* unc_code = reinterpret_cast<unsigned*>(unc_idx + ni * kUncMax);
     auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) {
       if ((lane & 15) == 15) {  // the row totals
         const int i = 4 * c + (lane >> 4);
@@ -1290,7 +1333,10 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
       if (lane == 0) {
         unc_n[c] = cs.n_unc;
 #pragma unroll
-        for (int j = 0; j < kUncMax; ++j) unc_idx[c * kUncMax + j] = cs.unc[j];
+        for (int j = 0; j < kUncMax; ++j) {
+          unc_idx[c * kUncMax + j] = cs.unc[j];
+          unc_code[c * kUncMax + j] = cs.ucode[j];
+        }
       }
     };
     if (threadIdx.x == 0) {
@@ -1313,7 +1359,8 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
     Sp = block_sum<BLOCK>(lsp, sh.red);
     tok = fast_finish<BLOCK, DT, false, ET, true, kDrawG>(
         R, ni, Sq, Sp, Src<false, double>(A, 4 * ni), Src<false, double>(Bv, 4 * ni),
-        Src<false, int>(unc_n, ni), Src<false, int>(unc_idx, ni * kUncMax), W, u, sh);
+        Src<false, int>(unc_n, ni), Src<false, int>(unc_idx, ni * kUncMax), W, u, sh,
+        DT == kBF16 && ET ? unc_code : nullptr);
   }
   if (tok == -3) {  // residual without mass: the bonus draw from q_n
     DrawRows Rb = R;
