@@ -266,12 +266,13 @@ BOUNDARY_BF16 = [0x3C00, 0xBC00,   # +-2^-7: the first codes the residual kernel
                  0xFF80]           # -inf
 
 
-@pytest.mark.parametrize("T", [1.0, 20.0])
+@pytest.mark.parametrize("T", [0.01, 0.05, 1.0, 20.0])
 def test_bf16_table_boundary_codes(T):
     """bf16 rows made of the codes at and around the edges of the draw
     kernels' exponential table (2^-7 <= |z| < 2^6), -inf, zeros and
     denormals: the three-call path (tabulated), the fused path (computed)
-    and the draft sampler all against the oracle."""
+    and the draft sampler all against the oracle.  The low temperatures put
+    most table entries at or near 0 and the top codes' entries far apart."""
     rng = np.random.default_rng(int(T))
     B, K, V = 64, 3, 700
     codes = np.array(BOUNDARY_BF16, np.uint32)
