@@ -101,6 +101,10 @@ RAGGED = [
     # ragged last chunk)
     (15360, 3, "bf16", 8), (16384, 3, "bf16", 8), (16385, 3, "bf16", 8), (16896, 2, "bf16", 6),
     (8192, 3, "f32", 8), (8449, 2, "f32", 6),
+    # the draw's LDS routes at large vocabularies: bf16 without the exponential tables (fast
+    # sweep, computed exponentials), bf16 at the largest V (slow two-sweep path, tables on),
+    # fp32 past the fast sweep's LDS (slow path, computed)
+    (600000, 2, "bf16", 3), (1 << 20, 2, "bf16", 2), (600000, 2, "f32", 2),
 ]
 
 
