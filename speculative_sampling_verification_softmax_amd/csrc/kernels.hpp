@@ -778,6 +778,8 @@ __device__ __forceinline__ void chunk_sums_init(ChunkSums& out) {
 // Adds every token's e_q, e_p to the lane's lsq, lsp, the clearly positive
 // ones to a, bb, and the chunk's uncertain tokens to out's list -- with their
 // two bf16 codes when words (the lane's 4+4 raw words of a bf16 chunk) is set.
+// A bonus draw needs no normaliser (its weights are e_q, the draw is
+// scale-free): there every e_q goes to a alone and lsq, lsp stay as they are.
 template <int DT, int MODE, int H, typename Lookup>
 __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Lookup lookup,
                                                  double& lsq, double& lsp, double& a, double& bb,
@@ -791,8 +793,8 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
   for (int e = 0; e < E; ++e) {
     if (e % H == 0) lookup(e, eqh, eph);
     const double eq = eqh[e % H];
-    lsq = lsq + eq;
     if (MODE == kModeResidual) {
+      lsq = lsq + eq;
       const double ep = eph[e % H];
       lsp = lsp + ep;
       // e_q, e_p carry the factors s~_p, s~_q.  Each fma rounds once, so its
@@ -1289,7 +1291,7 @@ __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, in
       }
     }
     chunk_reduce<MODE, true>(a, bb, cs);
-    const double lqr = wave_scan_rows(lq);
+    const double lqr = MODE == kModeResidual ? wave_scan_rows(lq) : 0.0;
     const double lpr = MODE == kModeResidual ? wave_scan_rows(lp) : 0.0;
     emit(s, cs, lqr, lpr);
     s = sn;
