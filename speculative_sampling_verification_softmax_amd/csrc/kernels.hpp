@@ -436,7 +436,12 @@ struct DrawRows {
   double yscale;      // (1/T) * 256/ln2
   double mq, mp;      // row maxima (exact stored logits)
   double cq, cp;      // factors on e_q and e_p: s~_p and s~_q for a residual, else 1
-  const double* et;   // bf16 exponential tables in LDS (q row, then p row), or null
+  const double* et;   // bf16 exponential table of the q row in LDS, or null
+  const double* etp;  // ... of the p row (the same table when the rows share one)
+  // the sign test's constants -(1 + kDelta) * rho, -(1 - kDelta) * rho, and rho,
+  // the ratio e_q / e_p takes at q = p up to the fp32 normalisers (1 when the
+  // factors cq, cp already balance the two rows)
+  double k_hi, k_lo, rho;
 };
 
 // The rows at position n of sequence b and their stats.  Returns false when a
@@ -460,6 +465,10 @@ __device__ __forceinline__ bool make_draw_rows(int64_t b, int n, int K, int V, c
   R.cq = resid ? sp : 1.0;
   R.cp = resid ? sq : 1.0;
   R.et = nullptr;
+  R.etp = nullptr;
+  R.k_hi = uniform_margin(true);
+  R.k_lo = uniform_margin(false);
+  R.rho = 1.0;
   return row_ok(mq, sq) && (!resid || row_ok(mp, sp));
 }
 
@@ -519,6 +528,64 @@ __device__ __forceinline__ void fill_row_exp_tables(double* et, int rows, const 
     et[(threadIdx.x >> 1) * kETab + (threadIdx.x & 1) * kETabSign + kETabN] = 0.0;
 }
 
+// The table both rows of a draw can share: exp(z/T) over the codes, no row
+// maximum (so it can be filled before the drawn rows are known), by threads
+// first .. blockDim.x-1, with 1/T = yscale * ln2/256 formed the same way
+// wherever it is filled.  Usable for rows whose maxima have |m|/T <= 300
+// (draw_rows_share_table): then no entry a row looks up overflows, the row's
+// own maximum stays a normal double, and only entries more than ~400 nats
+// below it (weights below 1e-170 of the row's top) can lose precision.
+constexpr double kSharedTableMax = 300.0;
+template <int BLOCK>
+__device__ __forceinline__ void fill_shared_exp_table(double* et, double yscale, int first) {
+  constexpr int NC = 2 * static_cast<int>(kETabN);
+  constexpr int J = (NC + (BLOCK - kWave) - 1) / (BLOCK - kWave);
+  const int nt = BLOCK - first, t0 = static_cast<int>(threadIdx.x) - first;
+  const double invT = yscale / Exp64::kScale;
+  double v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {  // independent exponentials
+    const int k = t0 + j * nt;
+    const int sg = k >= static_cast<int>(kETabN) ? 1 : 0, i = k - sg * static_cast<int>(kETabN);
+    const float z = __uint_as_float(((kETabLo + i) | (static_cast<unsigned>(sg) << 15)) << 16);
+    v[j] = k < NC ? exp(static_cast<double>(z) * invT) : 0.0;
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int k = t0 + j * nt;
+    const int sg = k >= static_cast<int>(kETabN) ? 1 : 0, i = k - sg * static_cast<int>(kETabN);
+    if (k < NC) et[sg * static_cast<int>(kETabSign) + i] = v[j];
+  }
+  if (t0 >= 0 && t0 < 2) et[t0 * static_cast<int>(kETabSign) + static_cast<int>(kETabN)] = 0.0;
+}
+
+// Whether the rows of R may share the table above.
+__device__ __forceinline__ bool draw_rows_share_table(const DrawRows& R) {
+  const double invT = R.yscale / Exp64::kScale;
+  return fabs(R.mq) * invT <= kSharedTableMax &&
+         (R.mode != kModeResidual || fabs(R.mp) * invT <= kSharedTableMax);
+}
+
+// Switch R to the shared table at et: e_q = exp(z_q/T), e_p = exp(z_p/T)
+// (no maxima, no factors), with the sign test's balance
+// rho = exp((m_q - m_p)/T) * s~_q / s~_p -- the ratio e_q / e_p takes where
+// q = p up to the fp32 normalisers.  The draw's weights e_q/S_q - e_p/S_p
+// do not depend on these scales.
+__device__ __forceinline__ void use_shared_table(DrawRows& R, const double* et) {
+  const double invT = R.yscale / Exp64::kScale;
+  const double rho =
+      R.mode == kModeResidual ? exp((R.mq - R.mp) * invT) * (R.cp / R.cq) : 1.0;
+  R.rho = rho;
+  R.k_hi = uniform_margin(true) * rho;
+  R.k_lo = uniform_margin(false) * rho;
+  R.mq = 0.0;
+  R.mp = 0.0;
+  R.cq = 1.0;
+  R.cp = 1.0;
+  R.et = et;
+  R.etp = et;
+}
+
 // Table entry of bf16 code b, and whether b needs the computed exponential
 // (outside the table and not infinite; a row that is drawn from has a finite
 // maximum, so its only infinite logits are -inf).
@@ -537,7 +604,7 @@ template <int DT, bool ET, bool P>
 __device__ __forceinline__ double row_exp(const DrawRows& R, float z, const double* tab) {
   if constexpr (DT == kBF16 && ET) {
     const unsigned b = __float_as_uint(z) >> 16;
-    double e = R.et[(P ? kETab : 0) + etab_index(b)];
+    double e = (P ? R.etp : R.et)[etab_index(b)];
     const bool other = etab_other(b);
     if (__builtin_amdgcn_ballot_w64(other) != 0ull) {
       if (other) e = row_tok_exp<P>(R, z, tab);
@@ -558,7 +625,7 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
 #pragma unroll
     for (int k = 0; k < H; ++k) {
       const unsigned b = __float_as_uint(z[k]) >> 16;
-      e[k] = R.et[(P ? kETab : 0) + etab_index(b)];
+      e[k] = (P ? R.etp : R.et)[etab_index(b)];
       other[k] = etab_other(b);
       any = any || other[k];
     }
@@ -632,7 +699,7 @@ template <bool P, int NW>
 __device__ __forceinline__ void row_exp_words(const DrawRows& R, const unsigned (&w)[NW],
                                               const double* tab, double (&e)[2 * NW]) {
   typedef const __attribute__((address_space(3))) double* LdsDouble;
-  const LdsDouble et = (LdsDouble)(R.et + (P ? kETab : 0));  // the tables live in LDS
+  const LdsDouble et = (LdsDouble)(P ? R.etp : R.et);  // the tables live in LDS
   const unsigned base = static_cast<unsigned>(reinterpret_cast<uintptr_t>(et));
   unsigned a[2 * NW];
   u16x2 mx = static_cast<u16x2>(static_cast<unsigned short>(0));
@@ -788,7 +855,7 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
   constexpr int E = 16 / Elt<DT>::bytes;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
-  const double k_hi = uniform_margin(true), k_lo = uniform_margin(false);
+  const double k_hi = R.k_hi, k_lo = R.k_lo;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     if (e % H == 0) lookup(e, eqh, eph);
@@ -797,10 +864,10 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
       lsq = lsq + eq;
       const double ep = eph[e % H];
       lsp = lsp + ep;
-      // e_q, e_p carry the factors s~_p, s~_q.  Each fma rounds once, so its
-      // sign is exact: pos means e_q >= (1+kDelta) e_p (a token with
-      // e_q = e_p = 0 counts as positive and adds nothing), and lo <= 0 means
-      // e_q <= (1-kDelta) e_p; a token with neither is uncertain.
+      // pos means e_q >= (1+kDelta) rho e_p (a token with e_q = e_p = 0
+      // counts as positive and adds nothing), and lo <= 0 means
+      // e_q <= (1-kDelta) rho e_p; a token with neither is uncertain.  Each
+      // fma rounds once, so its sign is exact for its rounded constant.
       const double hi = fma(ep, k_hi, eq), lo = fma(ep, k_lo, eq);
       // the masks straight from the comparisons (every lane is active here)
       const unsigned long long pos_m = __ballot(hi >= 0.0), lo_m = __ballot(lo > 0.0);
@@ -1176,7 +1243,7 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
   if (R.mode == kModeResidual) {
     iq = 1.0 / Sq;
     ip = 1.0 / Sp;
-    const double ratio = Sq / Sp;  // the scaled sums: exact / fp32 normaliser ratio
+    const double ratio = (Sq / Sp) / R.rho;  // exact over fp32-normaliser ratio
     bool ok = fabs(ratio - 1.0) <= kDelta / 4;
     for (int c = tid; c < nch; c += BLOCK) {
       const double a = chunk_total(A, c), bv = chunk_total(Bv, c);
@@ -1380,14 +1447,16 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
 // nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow
 // path; with `etab` (bf16) the two rows' exponential tables come first.
 // n must be uniform across the workgroup.  tab_ready: sh.tab is already
-// filled (and a barrier has passed since).
+// filled (and a barrier has passed since); shared_ready: so is the shared
+// exponential table at dyn (fill_shared_exp_table).
 template <int BLOCK, int DT>
 __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt, const void* dft,
                                               const float* uni, const float* tstats,
                                               const float* dstats, int K, int V, double yscale,
                                               int fast, int etab, int32_t* out_tokens,
                                               int32_t* num_emitted, double* dyn,
-                                              DrawShared<BLOCK>& sh, bool tab_ready = false) {
+                                              DrawShared<BLOCK>& sh, bool tab_ready = false,
+                                              bool shared_ready = false) {
   const int64_t K1 = K + 1;
   const int tid = threadIdx.x;
   if (n < 0 || n > K) {
@@ -1410,9 +1479,18 @@ __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt,
   }
   double* work = dyn;
   if (DT == kBF16 && etab) {  // dynamic LDS starts with the two rows' tables
-    fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R, sh.tab);
-    __syncthreads();
-    R.et = dyn;
+    if (draw_rows_share_table(R)) {  // one table of exp(z/T) for both rows
+      if (!shared_ready) {
+        fill_shared_exp_table<BLOCK>(dyn, R.yscale, 0);
+        __syncthreads();
+      }
+      use_shared_table(R, dyn);
+    } else {  // per-row tables (rows with extreme maxima)
+      fill_row_exp_tables<BLOCK>(dyn, R.mode == kModeResidual ? 2 : 1, R, sh.tab);
+      __syncthreads();
+      R.et = dyn;
+      R.etp = dyn + kETab;
+    }
     work = dyn + 2 * kETab;
   }
   const int tok = R.et != nullptr ? draw_block<BLOCK, DT, true>(R, uni[b * K1 + K], fast, work, sh)
@@ -1441,7 +1519,8 @@ __global__ __launch_bounds__(BLOCK) void residual_kernel(
 
 // One workgroup per sequence (the spec_verify_sample path): wave 0 runs the
 // accept tests and the first-rejection scan (verify_seq) while the other
-// waves fill the exp2 table, then the whole workgroup draws the final token.  The same results as spec_verify followed
+// waves fill the exp2 table and (bf16) the shared exponential table, then the
+// whole workgroup draws the final token.  The same results as spec_verify followed
 // by spec_residual_sample, in one launch.
 template <int BLOCK, int DT>
 __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
@@ -1462,12 +1541,13 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
     if (threadIdx.x == 0) sh.sel[0] = n;
   } else {
     fill_exp2_table(sh.tab, kWave);
+    if (DT == kBF16 && etab) fill_shared_exp_table<BLOCK>(dyn, yscale, kWave);
   }
   __syncthreads();
   const int n = uniform(sh.sel[0]);
   __syncthreads();  // sel[] is reused by the draw
   draw_sequence<BLOCK, DT>(b, n, tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
-                           out_tokens, num_emitted, dyn, sh, true);
+                           out_tokens, num_emitted, dyn, sh, true, DT == kBF16 && etab);
 }
 
 // ============================================================ draft sampling
@@ -1504,6 +1584,10 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
   R.cq = 1.0;
   R.cp = 1.0;
   R.et = nullptr;
+  R.etp = nullptr;
+  R.k_hi = uniform_margin(true);
+  R.k_lo = uniform_margin(false);
+  R.rho = 1.0;
   fill_exp2_table(sh.tab);
   __syncthreads();
   double* work = dyn;
@@ -1511,6 +1595,7 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
     fill_row_exp_tables<BLOCK>(dyn, 1, R, sh.tab);
     __syncthreads();
     R.et = dyn;
+    R.etp = dyn;
     work = dyn + kETab;
   }
   const int tok = R.et != nullptr ? draw_block<BLOCK, DT, true>(R, uni[r], fast, work, sh)
