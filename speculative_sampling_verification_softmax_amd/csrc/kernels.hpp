@@ -942,15 +942,15 @@ __device__ __forceinline__ void chunk_acc_words(const DrawRows& R, int c, const 
                                                 double& lsp, double& a, double& bb,
                                                 ChunkSums& out) {
   const unsigned w8[8] = {wq.x, wq.y, wq.z, wq.w, wp.x, wp.y, wp.z, wp.w};
-  auto lookup = [&](int e, double (&eq)[4], double (&ep)[4]) {
-    const unsigned qw[2] = {w8[e / 2], w8[e / 2 + 1]};
-    row_exp_words<false, 2>(R, qw, tab, eq);
+  auto lookup = [&](int e, double (&eq)[8], double (&ep)[8]) {
+    const unsigned qw[4] = {w8[0], w8[1], w8[2], w8[3]};
+    row_exp_words<false, 4>(R, qw, tab, eq);
     if (MODE == kModeResidual) {
-      const unsigned pw[2] = {w8[4 + e / 2], w8[4 + e / 2 + 1]};
-      row_exp_words<true, 2>(R, pw, tab, ep);
+      const unsigned pw[4] = {w8[4], w8[5], w8[6], w8[7]};
+      row_exp_words<true, 4>(R, pw, tab, ep);
     }
   };
-  chunk_accumulate<kBF16, MODE, 4>(R, c, lookup, lsq, lsp, a, bb, out, w8);
+  chunk_accumulate<kBF16, MODE, 8>(R, c, lookup, lsq, lsp, a, bb, out, w8);
 }
 
 
