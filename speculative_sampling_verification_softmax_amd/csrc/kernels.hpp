@@ -376,19 +376,21 @@ __global__ __launch_bounds__(kWave) void verify_kernel(
 //
 // For a residual every e_q is taken times the draft row's fp32 normaliser
 // s~_p from the stats and every e_p times s~_q (the factors cq, cp of
-// DrawRows; the tables hold the products), so that e_q >= e_p reads as
-// q >= p up to the stats' rounding.  The draw is unchanged: q = e_q/S_q with
-// S_q the sum of the same scaled values.
+// DrawRows; per-row tables hold the products), so that e_q >= e_p reads as
+// q >= p up to the stats' rounding.  With the table both rows share, e is
+// exp(z/T) with no maximum and no factor, and the balance moves into the
+// sign test's constants instead (rho of DrawRows).  Either way the draw is
+// unchanged: q = e_q/S_q with S_q the sum of the same values.
 //
 // Fast path, one sweep over the row(s): every token's e_q, e_p (fp64 table
 // exponential) go into the normalisers S_q, S_p; the sign of the residual is
-// decided on the scaled values with a relative margin kDelta: e_q >=
-// (1+kDelta) e_p is certainly positive, e_q <= (1-kDelta) e_p certainly not.
+// decided with a relative margin kDelta: e_q >= (1+kDelta) rho e_p is
+// certainly positive, e_q <= (1-kDelta) rho e_p certainly not.
 // Tokens clearly positive add e_q and e_p to the chunk's sums A_c, B_c;
 // tokens clearly negative add nothing; the few inside the margin are recorded
 // (up to kUncMax per chunk) and resolved once S_q, S_p are exact.  Then
 // W_c = A_c/S_q - B_c/S_p (+ the resolved tokens).  If the exact ratio
-// S_q/S_p falls outside 1 by more than kDelta/4, a chunk records more
+// S_q/S_p falls outside rho by more than kDelta/4, a chunk records more
 // uncertain tokens than it can hold, or the residual has no mass, the draw
 // takes the exact slow path instead: normalisers first, then every chunk's
 // weights, two sweeps.
@@ -489,8 +491,9 @@ __device__ __forceinline__ double row_tok_exp(const DrawRows& R, float z, const 
 // of 2 * 13 * 128 codes.  A workgroup that draws from a row can fill a table
 // of row_tok_exp over those codes once (kETab doubles per row: a block of
 // kETabSign entries per sign, the codes in order and then 0s) and look tokens
-// up instead of evaluating the exponential; other values are computed.  The
-// table holds row_tok_exp's own results, so both ways give the same bits.  With
+// up instead of evaluating the exponential; other values are computed.  Every
+// use of a code's value (sweep, uncertain tokens, in-chunk draw, slow path)
+// goes through the same lookup, so each code has one value.  With
 // t = |code| - kETabLo (unsigned), a code's entry is sign * kETabSign +
 // min(t, kETabN): every code outside the table, -inf included, lands on a 0.
 constexpr unsigned kETabLo = 120u << 7;  // bf16 bits of 2^-7, sign cleared

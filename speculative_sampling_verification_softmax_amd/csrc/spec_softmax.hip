@@ -42,9 +42,9 @@ constexpr int kFusedBlock = 256;
 constexpr int kFusedNW = kFusedBlock / spec::kWave;
 // Dynamic LDS of the fused kernel: one double per chunk of a row.
 constexpr size_t kFusedMaxDynLds = static_cast<size_t>(SPEC_MAX_V / 64 / 4) * sizeof(double);
-// Dynamic LDS of a draw workgroup (the fast-path arrays, then the bf16
-// exponential tables if they fit as well).  The static part is ~2.3 KB; a
-// gfx950 workgroup may hold 160 KB, and a draw workgroup has its CU alone.
+// Dynamic LDS of a draw workgroup (the bf16 exponential tables when they fit
+// too, then the fast-path arrays).  The static part is ~2.3 KB; a gfx950
+// workgroup may hold 160 KB, and a draw workgroup has its CU alone.
 constexpr size_t kResidFastLds = 152 * 1024;
 constexpr size_t kDrawDynLds = 152 * 1024;
 
