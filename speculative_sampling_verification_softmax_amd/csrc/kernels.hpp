@@ -1630,7 +1630,10 @@ __global__ __launch_bounds__(BLOCK) void argmax_kernel(const void* __restrict__ 
   const RowGeom<DT> G(row, V);
   float best = -__builtin_huge_valf();
   int best_i = 0x7fffffff;
-  unsigned long long nanm = 0;
+  // NaN check in vector registers: the largest |bits| seen; a NaN is exactly
+  // a value above 0x7F800000 (one ballot at the end, none in the loop)
+  unsigned mag = 0u;
+  auto note = [&](float v) { mag = max(mag, __float_as_uint(v) & 0x7FFFFFFFu); };
   // a candidate (value, index) that beats the best so far: larger, or equal
   // with a smaller index
   auto offer = [&](float v, int i) {
@@ -1641,13 +1644,13 @@ __global__ __launch_bounds__(BLOCK) void argmax_kernel(const void* __restrict__ 
   };
   {  // head elements (indices below the body's)
     const float v = tid < G.head ? logit_f32<DT>(row, tid) : -__builtin_huge_valf();
-    nanm |= __ballot(v != v);
+    note(v);
     if (tid < G.head) offer(v, tid);
   }
   const char* body = row + static_cast<int64_t>(G.head) * EB;
   stream_body<BLOCK, DT, VPG, kLoadStream>(body, G.nvec, [&](const float(&x)[VPG * EPV], int i0) {
 #pragma unroll
-    for (int k = 0; k < VPG * EPV; ++k) nanm |= __ballot(x[k] != x[k]);
+    for (int k = 0; k < VPG * EPV; ++k) note(x[k]);
     const float g = group_max(x);
     if (g > best) {  // rare after the first groups: find the group's first maximal element
       int gi = 0x7fffffff;
@@ -1663,9 +1666,10 @@ __global__ __launch_bounds__(BLOCK) void argmax_kernel(const void* __restrict__ 
   {  // tail elements (indices above the body's), after it so that ties keep the body's
     const bool has = tid < V - G.tail0;
     const float v = has ? logit_f32<DT>(row, G.tail0 + tid) : -__builtin_huge_valf();
-    nanm |= __ballot(v != v);
+    note(v);
     if (has) offer(v, G.tail0 + tid);
   }
+  const unsigned long long nanm = __ballot(mag > 0x7F800000u);
   // wave, then block: the largest value, and among equal values the smallest index
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
