@@ -19,9 +19,10 @@
  *           at the drafted token; a separate accepted count; residual denominator
  *           0 falls back to q.
  *   [THM1]  Method: Theorem 1, P(X=x) = min(p(x),q(x)) + max(0, q(x)-p(x)) = q(x).
- *   [GREEDY] Pitfalls: greedy mode.  The card infers the rule from the general
- *           one applied to one-hot distributions: accept while the drafted
- *           token is the target argmax, else emit the target argmax.
+ *   [GREEDY] Pitfalls: greedy mode.  The card derives the rule by applying the
+ *           general test to one-hot distributions: a drafted token survives
+ *           only when it is the target row's largest entry, and the first
+ *           one that is not is replaced by that entry.
  *   [DRAFT] "Algorithm: Speculative Sampling (SpS)" (alg. 2) step 1 and
  *           Pitfalls: draft tokens are sampled from the (transformed) draft
  *           distributions p.

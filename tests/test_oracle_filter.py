@@ -79,6 +79,67 @@ def test_top_k_then_nucleus_nest():
         assert prob[zf[r] >= tb].sum() >= p - 1e-12
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
+def test_top_k_then_nucleus_is_the_smallest_sufficient_set_of_the_survivors(dtype, T):
+    """The nucleus after top-k measures mass over the top-k survivors only:
+    renormalised over that set (numpy, no oracle call), the kept classes hold
+    at least top_p, and without the smallest kept class they hold less.  A
+    normaliser taken over the whole row instead keeps too many classes and
+    fails the second check."""
+    rng = np.random.default_rng(6)
+    st, zf = rows(rng, 120, 400, dtype)
+    T = float(np.float32(T))
+    narrowed = 0
+    for r in range(120):
+        k, p = int(rng.integers(2, 200)), float(rng.uniform(0.05, 0.97))
+        tk = oracle.filter_threshold(st[r], T, top_k=k)
+        tb = oracle.filter_threshold(st[r], T, top_k=k, top_p=p)
+        srt = np.sort(zf[r])[::-1]
+        survivors = zf[r] >= srt[k - 1]
+        e = np.where(survivors, np.exp((zf[r] - srt[0]) / T), 0.0)
+        prob_k = e / e.sum()
+        kept = zf[r] >= tb
+        assert np.all(kept <= survivors)                       # inside the top-k set
+        assert prob_k[kept].sum() >= p - 1e-12                  # sufficient
+        smallest = zf[r][kept].min()
+        assert prob_k[kept & (zf[r] > smallest)].sum() < p + 1e-12   # minimal
+        narrowed += int(tb > tk)
+    assert narrowed > 30  # the nucleus really cuts inside the top-k set in many rows
+
+
+# Equal-mass rows: with T = 2^60 every (z - m)/T is below 2^-56 in magnitude,
+# so every token's mass exp((z - m)/T) is exactly 1.0 in binary64 and the
+# nucleus reduces to counting tokens: the threshold is the largest value v
+# with #{x : z[x] >= v} >= top_p * (number of top-k survivors).  The expected
+# thresholds below are counted by hand on the row 7,7,6,6,...,0,0 (two
+# tokens per value, V = 16), with dyadic top_p placing several cases exactly
+# on the boundary, where ">=" keeps the class and ">" would not.
+EQUAL_MASS_T = 2.0 ** 60
+EQUAL_MASS_ROW = np.repeat(np.arange(7, -1, -1, dtype=np.float32), 2)
+EQUAL_MASS_CASES = [
+    # (top_k, top_p, threshold)            count needed -> classes kept
+    (0, 0.5, 4.0),    # 8 of 16: values 7..4 hold exactly 8
+    (0, 0.75, 2.0),   # 12 of 16: values 7..2 hold exactly 12
+    (0, 0.3, 5.0),    # 4.8 of 16: values 7..5 hold 6
+    (8, 0.5, 6.0),    # survivors 7..4 (8): 4 needed, values 7..6 hold exactly 4
+    (8, 0.25, 7.0),   # 2 needed, value 7 holds exactly 2
+    (3, 0.5, 7.0),    # 3rd largest is 6, ties kept: 4 survivors, 2 needed, value 7 holds 2
+    (3, 0.75, 6.0),   # 3 needed: value 7 holds 2, 7..6 hold 4
+    (5, 1.0, 5.0),    # top-k alone: 5th largest is 5
+    (0, 1e-9, 7.0),   # a vanishing top_p keeps the top class
+    (16, 1.0, -np.inf),  # nothing removed
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("top_k,top_p,want", EQUAL_MASS_CASES)
+def test_nucleus_boundary_on_equal_mass_rows(dtype, top_k, top_p, want):
+    row = EQUAL_MASS_ROW if dtype == "f32" else bf16_bits(EQUAL_MASS_ROW)
+    got = oracle.filter_threshold(row, EQUAL_MASS_T, top_k=top_k, top_p=top_p)
+    assert got == want
+
+
 def test_invalid_rows_and_parameters():
     assert oracle.filter_threshold(np.array([0.0, np.nan], np.float32), 1.0, top_k=1) is None
     assert oracle.filter_threshold(np.full(4, -np.inf, np.float32), 1.0, top_p=0.5) is None

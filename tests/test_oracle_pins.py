@@ -245,9 +245,10 @@ def test_disjoint_supports_reject_first_and_resample_from_q():
 
 
 def test_one_hot_rows_reduce_to_greedy_rule():
-    """One-hot p and q (every other logit -inf): accept iff the drafted argmax
-    equals the target argmax, otherwise emit the target argmax (Pitfalls,
-    greedy mode)."""
+    """One-hot p and q (every other logit -inf): the general accept test then
+    becomes a match of the two rows' single supported tokens, and the residual
+    at the first mismatch puts all its mass on the target row's token (card's
+    Pitfalls, greedy mode)."""
     rng = np.random.default_rng(9)
     K, V = 5, 16
     for trial in range(100):
