@@ -5,18 +5,18 @@
 
 One step = the whole verify of one batch: row statistics of every target and
 draft row, the accept scan and the residual or bonus draw, inputs resident in
-HBM.  --path two_call (default, the fastest path on MI355X) runs it as
-spec_softmax_stats then spec_verify_sample on one stream; --path three_call as
-spec_softmax_stats, spec_verify, spec_residual_sample; --path fused as one
-spec_verify_fused launch.  W untimed steps, then K timed steps bracketed by
+HBM.  --path two_call (default) runs it as spec_softmax_stats then
+spec_verify_sample on one stream; --path three_call as spec_softmax_stats,
+spec_verify, spec_residual_sample; --path step as spec_verify_step (the same
+two launches, with rows and sequences split over several workgroups when
+the batch is small).  W untimed steps, then K timed steps bracketed by
 device synchronisation, with nothing else on the stream.  Prints one JSON
 line on stdout; progress goes to stderr.
 
 Reported:
   value          verified sequences per second (B / seconds per step)
   roofline       the dominant kernel (two_call, three_call: the stats kernel,
-                 every logit once + stats written; fused: the fused kernel,
-                 the whole step's compulsory bytes) / its mean duration, timed
+                 every logit once + stats written) / its mean duration, timed
                  with an event pair around it on its stream in K further steps
                  right after the timed region (events recorded between two
                  kernels add a few microseconds to a step, so they are kept
@@ -39,10 +39,17 @@ read once) / its mean duration.
 
     python bench.py --mode ksweep [--ks 1,2,4,8,16]
 
-the K trade-off of the pages' fig. 1 on synthetic rows: for each K, the
-three-call verify at the workload's B, V, T and draft noise (fresh inputs per
-K), its time per call and the mean tokens emitted per sequence; one JSON line
-with a "sweep" list.
+the K trade-off of the pages' fig. 1 on synthetic rows: one batch drawn at the
+largest K, and for each K the step on its prefix rows (paired), with the time
+per step, the mean and spread of the tokens emitted per sequence, the time per
+emitted token and the oracle's closed-form expectation; one JSON line with a
+"sweep" list.
+
+    python bench.py --mode read-ceiling
+
+what a kernel that only reads gets from HBM here (the probe library's plain
+16-byte non-temporal reads of the workload's logit bytes, in several launch
+shapes) next to the stats kernel on the same bytes.
 
     python bench.py --pmc-summary DIR [--path P] [--workload W] [--command CMD]
 
@@ -132,8 +139,8 @@ def _pmc_kernels(path: str) -> dict:
 
 def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
-    # pass directories: fetch, write (the stats kernel, two or three calls); fetch_fused, ...
-    suffix = "" if path in ("two_call", "three_call") else "_" + path
+    # pass directories: fetch, write (the stats kernel, any path)
+    suffix = ""
     fetch, write = f("fetch" + suffix), f("write" + suffix)
     copy_bytes = COPY_MIB << 20
     def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)
@@ -144,8 +151,8 @@ def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     kf = copy_bytes / (cf * 1024)
     kw = copy_bytes / (cw * 1024)
     wl = synth.WORKLOADS[workload]
-    dom = "fused_kernel" if path == "fused" else "stats_kernel"
-    alg = step_bytes(wl) if path == "fused" else stats_bytes(wl)
+    dom = "stats_kernel"
+    alg = stats_bytes(wl)
     lines = [f"# HBM traffic per launch: {path} path, {workload} workload "
              f"(B={wl.B}, K={wl.K}, V={wl.V}, {wl.dtype}, T={wl.T})", "",
              "Commands (one MI355X, from the repository root; each pass is a run of its own):", "",
@@ -180,7 +187,7 @@ def trace_summary(d: str, command: str) -> str:
     rows = []
     with open(f[0]) as fh:
         for r in csv.DictReader(fh):
-            if "spec::" in r["Name"]:
+            if "spec::" in r["Name"] or "spec_probe::" in r["Name"]:
                 rows.append((r["Name"].replace("void ", "").split("(")[0], int(r["Calls"]),
                              float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"])))
     lines = ["Command (one MI355X, from the repository root):", "", "```", command, "```", "",
@@ -191,10 +198,17 @@ def trace_summary(d: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, min_cpu_s: float = 12.0) -> dict:
+def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, gpu_out: dict,
+                 min_cpu_s: float = 12.0) -> tuple[dict, dict, dict]:
     """The oracle on the first max_seqs sequences of the batch, repeated until
-    about min_cpu_s CPU-seconds (wall time x threads) have been spent."""
+    about min_cpu_s CPU-seconds (wall time x threads) have been spent on all
+    host threads, then once more on one thread over a smaller sample.
+    Returns (baseline, one-thread baseline, parity): parity compares the
+    oracle's outputs with the timed step's own outputs (gpu_out: numpy
+    arrays of the last timed step) under the tests' rule."""
     import oracle
+    sys.path.insert(0, ROOT)
+    from tests import parity as par
     n = min(wl.B, max_seqs)
     idx = torch.arange(n, device=inp["target"].device)
     sub = dict(target=inp["target"][idx], draft=inp["draft"][idx], tokens=inp["tokens"][idx],
@@ -202,17 +216,36 @@ def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, min_cpu_s: float 
     host = synth.to_host_arrays(sub)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
     T = float(np.float32(wl.T))
-    reps, wall = 0, 0.0
+    reps, wall, o = 0, 0.0, None
     while reps == 0 or (wall * threads < min_cpu_s and reps < 200):
         t0 = time.perf_counter()
-        oracle.verify(host["target"], host["draft"], host["tokens"], host["uniforms"], T,
-                      nthreads=threads)
+        o = oracle.verify(host["target"], host["draft"], host["tokens"], host["uniforms"], T,
+                          nthreads=threads)
         wall += time.perf_counter() - t0
         reps += 1
-    return {"value": n * reps / wall, "unit": "seqs/s", "cores": threads, "kind": "oracle",
+    base = {"value": n * reps / wall, "unit": "seqs/s", "cores": threads, "kind": "oracle",
             "sample": f"the first {n} of {wl.B} sequences of the same {wl.name} batch, verified "
                       f"{reps} times (fp64; {threads} OpenMP threads; {wall:.2f} s wall, "
                       f"{wall * threads:.1f} CPU-s)"}
+    n1 = min(n, 32)
+    t0 = time.perf_counter()
+    oracle.verify(host["target"][:n1], host["draft"][:n1], host["tokens"][:n1],
+                  host["uniforms"][:n1], T, nthreads=1)
+    w1 = time.perf_counter() - t0
+    one = {"value": n1 / w1, "unit": "seqs/s", "cores": 1, "kind": "oracle",
+           "sample": f"the first {n1} sequences, verified once on one thread ({w1:.2f} s)"}
+    rep = par.compare(gpu_out, o, wl.T, seqs=np.arange(n))
+    parity = {"sequences": n, "draws": rep["draws"], "flagged": len(rep["flagged"]),
+              "failures": len(rep["failures"]),
+              "flagged_limit": par.MAX_FLAGGED_FRACTION * rep["draws"],
+              "stats_max_rel": rep["stats_max_rel"], "probs_max_rel": rep["probs_max_rel"],
+              "stats_max_exact": rep["stats_max_not_exact"] == 0,
+              "ok": (not rep["failures"] and rep["stats_validity_mismatch"] == 0
+                     and rep["stats_max_not_exact"] == 0
+                     and rep["stats_max_rel"] <= par.PROB_RTOL
+                     and rep["probs_max_rel"] <= par.PROB_RTOL
+                     and len(rep["flagged"]) <= par.MAX_FLAGGED_FRACTION * rep["draws"])}
+    return base, one, parity
 
 
 def timed(step, steps: int, warmup: int, stream) -> tuple[float, float]:
@@ -404,14 +437,43 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
 
 
 def ksweep(args, base: synth.Workload) -> dict:
-    """Verify time and emitted tokens per sequence as K varies (fig. 1 analogue)."""
-    out = []
+    """Verify time and emitted tokens per sequence as K varies (the pages' fig. 1
+    trade-off on synthetic rows).  Paired: one batch is drawn at the largest K,
+    and every K verifies its first K+1 target rows, K draft rows and drafted
+    tokens (the uniform of slot K drives the final draw), so the curves differ
+    only through K.  Reported per K: time per step, the mean and standard
+    deviation of the tokens emitted per sequence, the time per emitted token,
+    and the expectation the oracle gives in closed form,
+    E[emitted] = 1 + sum_{j=1..K} prod_{i<j} alpha_i with
+    alpha_i = sum_x min(p_i(x), q_i(x)) (the accept probability at position i
+    when the drafted token follows p_i), averaged over the batch."""
+    ks = sorted(int(k) for k in args.ks.split(","))
+    kmax = ks[-1]
     stream = torch.cuda.current_stream()
-    for K in [int(k) for k in args.ks.split(",")]:
-        wl = synth.workload(base.name, K=K)
-        inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
-        tgt, dft, tok, uni = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"]
-        B = wl.B
+    wl = synth.workload(base.name, K=kmax)
+    log(f"[bench] ksweep: one batch at K={kmax}, B={wl.B}, V={wl.V}")
+    inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
+    B, V = wl.B, wl.V
+    alpha = None
+    if args.cpu_seqs > 0:  # the oracle's per-position accept probabilities (fp64)
+        import oracle
+        host = synth.to_host_arrays(inp)
+        T = float(np.float32(wl.T))
+        nb = min(B, args.cpu_seqs)
+        alpha = np.empty((nb, kmax))
+        for b in range(nb):
+            for t in range(kmax):
+                q = oracle.softmax_row(host["target"][b, t], T)[0]
+                p_ = oracle.softmax_row(host["draft"][b, t], T)[0]
+                alpha[b, t] = np.minimum(p_, q).sum()
+        log(f"[bench] ksweep: oracle alpha over {nb} sequences, mean {alpha.mean():.4f}")
+    out = []
+    for K in ks:
+        tgt = inp["target"][:, :K + 1].contiguous()
+        dft = inp["draft"][:, :K].contiguous()
+        tok = inp["tokens"][:, :K].contiguous()
+        uni = inp["uniforms"][:, :K + 1].contiguous()
+        ws = binding.new_workspace(B, K, V, tgt.dtype, "cuda")
         ts = torch.empty((B, K + 1, 2), dtype=torch.float32, device="cuda")
         ds = torch.empty((B, K, 2), dtype=torch.float32, device="cuda")
         nacc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -422,24 +484,93 @@ def ksweep(args, base: synth.Workload) -> dict:
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            binding.softmax_stats(tgt, dft, wl.T, ts, ds, stream=stream)
-            binding.verify(tgt, dft, tok, uni, ts, ds, wl.T, nacc, o, pr, stream=stream)
-            binding.residual_sample(tgt, dft, uni, ts, ds, nacc, wl.T, o, ne, stream=stream)
+            binding.verify_step(tgt, dft, tok, uni, wl.T, ws, ts, ds, nacc, o, pr, ne,
+                                stream=stream)
             if ev is not None:
                 ev[1].record(stream)
         ms, _ = timed(step, args.steps, args.warmup, stream)
-        emitted = float(ne.double().mean().item())
-        out.append({"K": K, "us_per_call": ms * 1e3, "emitted_per_seq": emitted,
-                    "emitted_tokens_per_s": B * emitted / (ms * 1e-3),
-                    "GBps": step_bytes(wl) / (ms * 1e-3) / 1e9})
-        log(f"[bench] K={K}: {ms * 1e3:.1f} us, {emitted:.3f} tokens/seq")
-        del inp, tgt, dft
+        em = ne.double()
+        mean, std = float(em.mean().item()), float(em.std().item())
+        rec = {"K": K, "us_per_step": ms * 1e3, "emitted_mean": mean, "emitted_std": std,
+               "us_per_emitted_token": ms * 1e3 / mean,
+               "emitted_tokens_per_s": B * mean / (ms * 1e-3),
+               "GBps": step_bytes(synth.workload(base.name, K=K)) / (ms * 1e-3) / 1e9}
+        if alpha is not None:
+            cum = np.cumprod(alpha[:, :K], axis=1)
+            expect = 1.0 + cum.sum(axis=1)
+            rec["emitted_expected"] = float(expect.mean())
+            # the batch mean's standard error around the expectation
+            rec["emitted_mean_stderr"] = std / np.sqrt(B)
+        out.append(rec)
+        log(f"[bench] K={K}: {ms * 1e3:.1f} us, emitted {mean:.3f} +- {std:.3f}"
+            + (f" (oracle expectation {rec['emitted_expected']:.3f})" if alpha is not None else ""))
+        del tgt, dft, ws
         torch.cuda.empty_cache()
     return {"metric": f"verify time and emitted tokens per sequence vs K, B={base.B} "
-                      f"V={base.V} {base.dtype} T={base.T}",
+                      f"V={base.V} {base.dtype} T={base.T} (paired: prefixes of one K={kmax} "
+                      f"batch)",
             "unit": "per K", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "data": "synthetic", "config": {"workload": base.name, "mode": "ksweep"},
+            "data": "synthetic", "config": {"workload": base.name, "mode": "ksweep",
+                                            "path": "step"},
             "sweep": out}
+
+
+def read_ceiling(args, wl: synth.Workload) -> dict:
+    """What a kernel that only reads gets from HBM on this part: the probe of
+    libspec_probe.so (16-byte non-temporal loads, as the stats kernel issues)
+    over a buffer of the workload's logit bytes, in three shapes, and the
+    stats kernel itself on the workload's rows; event-timed per launch."""
+    import ctypes
+    from speculative_sampling_verification_softmax_amd import build as hip_build
+    probe = ctypes.CDLL(hip_build.PROBE_LIB)
+    vp = ctypes.c_void_p
+    probe.spec_probe_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp, vp]
+    probe.spec_probe_read.restype = ctypes.c_int
+    rows = wl.B * (2 * wl.K + 1)
+    nbytes = rows * wl.V * wl.elt
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x3F)
+    sink = torch.empty(max(rows, 8192), dtype=torch.int32, device="cuda")
+    res = []
+    for name, mode, groups in [("grid-stride, 8 loads in flight", 0, rows),
+                               ("grid-stride, 4 loads in flight", 1, rows),
+                               ("grid-stride, 8 loads in flight, 1024 workgroups", 0, 1024),
+                               ("one row per workgroup, 4 loads in flight", 2, rows)]:
+        def call(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            rc = probe.spec_probe_read(buf.data_ptr(), nbytes, mode, groups, sink.data_ptr(),
+                                       stream.cuda_stream)
+            if ev is not None:
+                ev[1].record(stream)
+            if rc != 0:
+                raise RuntimeError(f"spec_probe_read mode {mode}: {rc}")
+        ms, _ = timed(call, args.steps, args.warmup, stream)
+        res.append({"shape": name, "workgroups": groups, "us": ms * 1e3,
+                    "GBps": nbytes / (ms * 1e-3) / 1e9})
+        log(f"[bench] read ceiling, {name}: {ms * 1e3:.1f} us, {res[-1]['GBps']:.0f} GB/s")
+    del buf
+    torch.cuda.empty_cache()
+    inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
+    ts = torch.empty((wl.B, wl.K + 1, 2), dtype=torch.float32, device="cuda")
+    ds = torch.empty((wl.B, wl.K, 2), dtype=torch.float32, device="cuda")
+
+    def stats(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.softmax_stats(inp["target"], inp["draft"], wl.T, ts, ds, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+    ms, _ = timed(stats, args.steps, args.warmup, stream)
+    sk = {"us": ms * 1e3, "GBps": stats_bytes(wl) / (ms * 1e-3) / 1e9}
+    sk["of_best_read"] = sk["GBps"] / max(r["GBps"] for r in res)
+    log(f"[bench] stats_kernel: {ms * 1e3:.1f} us, {sk['GBps']:.0f} GB/s "
+        f"({100 * sk['of_best_read']:.1f} % of the best plain read)")
+    return {"metric": f"streaming read ceiling over {nbytes} bytes (the {wl.name} logits)",
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic", "config": {"workload": wl.name, "mode": "read-ceiling"},
+            "peak_GBps": HBM_PEAK_GBPS, "reads": res, "stats_kernel": sk}
 
 
 def main() -> int:
@@ -450,18 +581,23 @@ def main() -> int:
     ap.add_argument("--workload", default="headline", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--mode", default="verify",
-                    choices=["verify", "greedy", "sample", "filter", "filtered", "ksweep"],
+                    choices=["verify", "greedy", "sample", "filter", "filtered", "ksweep",
+                             "read-ceiling"],
                     help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
                          "sweep K")
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
     ap.add_argument("--top-k", type=int, default=50, help="top-k for --mode filter (0: off)")
     ap.add_argument("--top-p", type=float, default=0.9, help="nucleus top_p for --mode filter")
-    ap.add_argument("--path", default="two_call", choices=["three_call", "two_call", "fused"],
+    ap.add_argument("--path", default="two_call", choices=["three_call", "two_call", "step"],
                     help="three_call: spec_softmax_stats, spec_verify, spec_residual_sample; "
                          "two_call: spec_softmax_stats, spec_verify_sample; "
-                         "fused: spec_verify_fused (one launch)")
+                         "step: spec_verify_step (split launches for small batches)")
     ap.add_argument("--cpu-seqs", type=int, default=256,
-                    help="sequences in the CPU oracle sample (0 = skip)")
+                    help="sequences in the CPU oracle sample, also checked for parity against "
+                         "the timed step's outputs (0 = skip)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (for the "
+                         "launch-bound small shapes)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(a known-size reference for HBM byte counters) and exit")
@@ -504,6 +640,9 @@ def main() -> int:
     if args.mode == "ksweep":
         print(json.dumps(ksweep(args, wl)), flush=True)
         return 0
+    if args.mode == "read-ceiling":
+        print(json.dumps(read_ceiling(args, wl)), flush=True)
+        return 0
     log(f"[bench] generating {wl.name}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype} T={wl.T}")
     inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
     tgt, dft, tok, uni, T = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], wl.T
@@ -523,51 +662,93 @@ def main() -> int:
 
     ws = binding.new_workspace(B, K, wl.V, tgt.dtype, dev)
 
-    def step_fused(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        binding.verify_fused(tgt, dft, tok, uni, T, ws, ts, ds, nacc, out, probs, nemit,
-                             stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+    def launch(st, path=args.path):
+        """One whole step on stream st."""
+        if path == "step":
+            binding.verify_step(tgt, dft, tok, uni, T, ws, ts, ds, nacc, out, probs, nemit,
+                                stream=st)
+        elif path == "two_call":
+            binding.softmax_stats(tgt, dft, T, ts, ds, stream=st)
+            binding.verify_sample(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, nemit,
+                                  stream=st)
+        else:
+            binding.softmax_stats(tgt, dft, T, ts, ds, stream=st)
+            binding.verify(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, stream=st)
+            binding.residual_sample(tgt, dft, uni, ts, ds, nacc, T, out, nemit, stream=st)
 
-    def step_three(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(ev=None):
+        if ev is None:
+            launch(stream)
+            return
+        # the dominant kernel's event pair: spec_softmax_stats (the stats kernel
+        # every path launches first when rows fill the device), then the rest
+        ev[0].record(stream)
         binding.softmax_stats(tgt, dft, T, ts, ds, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        binding.verify(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, stream=stream)
-        binding.residual_sample(tgt, dft, uni, ts, ds, nacc, T, out, nemit, stream=stream)
-
-    def step_two(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        binding.softmax_stats(tgt, dft, T, ts, ds, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         binding.verify_sample(tgt, dft, tok, uni, ts, ds, T, nacc, out, probs, nemit,
                               stream=stream)
 
-    step = {"fused": step_fused, "two_call": step_two, "three_call": step_three}[args.path]
+    graph = None
+    if args.graph:
+        # one step captured in a HIP graph and replayed: the launch-bound shapes
+        # then measure the GPU rather than the host's per-call overhead
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            launch(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            launch(torch.cuda.current_stream())
+        torch.cuda.synchronize()
 
-    log(f"[bench] warmup {args.warmup}, then {args.steps} timed steps")
-    ms, dom_ms = timed(step, args.steps, args.warmup, stream)
-    if args.path == "fused":
-        dom_kernel, dom_bytes = "fused_kernel", step_bytes(wl)
-    else:
-        dom_kernel, dom_bytes = "stats_kernel", stats_bytes(wl)
+    def timed_step(ev=None):
+        if graph is not None and ev is None:
+            graph.replay()
+        else:
+            step(ev)
+
+    log(f"[bench] warmup {args.warmup}, then {args.steps} timed steps"
+        + (" (graph replay)" if graph is not None else ""))
+    ms, dom_ms = timed(timed_step, args.steps, args.warmup, stream)
+    dom_kernel, dom_bytes = "stats_kernel", stats_bytes(wl)
     log(f"[bench] {args.path}: {ms * 1e3:.1f} us/step, {dom_kernel} {dom_ms * 1e3:.1f} us")
+    launch(stream)  # the outputs of one plain step, for the parity check
+    torch.cuda.synchronize()
+    gpu_out = {k: v.cpu().numpy() for k, v in dict(
+        target_stats=ts, draft_stats=ds, num_accepted=nacc, out_tokens=out, probs=probs,
+        num_emitted=nemit).items()}
+
+    # cold-cache step time: a 1 GiB write between steps evicts the 256 MB
+    # MALL, for working sets that would otherwise stay resident in it
+    cold = None
+    if wl.logit_bytes() < (512 << 20):
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(max(args.steps, 20)):
+            scratch.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            timed_step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        cold = float(np.median(times))
+        del scratch
+        log(f"[bench] cold-cache step (MALL evicted between steps): {cold * 1e3:.1f} us median")
 
     seqs_per_s = B / (ms * 1e-3)
     gbps_step = step_bytes(wl) / (ms * 1e-3) / 1e9
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     hist = torch.bincount(nacc.clamp(min=0).long(), minlength=K + 1).cpu().tolist()
 
-    cpu = None
+    cpu = cpu1 = par = None
     if args.cpu_seqs > 0:
-        log(f"[bench] cpu_baseline: oracle on {min(B, args.cpu_seqs)} sequences")
-        cpu = cpu_baseline(inp, wl, args.cpu_seqs)
+        log(f"[bench] cpu_baseline: oracle on {min(B, args.cpu_seqs)} sequences, checked "
+            f"against the timed step's outputs")
+        cpu, cpu1, par = cpu_baseline(inp, wl, args.cpu_seqs, gpu_out)
+        log(f"[bench] parity: {par}")
 
     rec = {
         "metric": METRIC,
@@ -583,16 +764,23 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "K": K, "V": wl.V, "logits": wl.dtype,
-                   "T": wl.T, "seed": args.seed, "path": args.path},
+                   "T": wl.T, "seed": args.seed, "path": args.path,
+                   "timing": "graph replay" if graph is not None else "eager launches"},
         "draft_rows_per_s": B * K / (ms * 1e-3),
         "achieved_GBps": gbps_step,
         "pct_of_peak": 100.0 * gbps_step / HBM_PEAK_GBPS,
+        "ms_per_step_cold": cold,
         "accepted_hist": hist,
         "roofline": {"bound": "hbm", "kernel": dom_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": find_traffic(dom_kernel, wl.name), "launch_us": dom_ms * 1e3,
-                     "bytes_per_launch": dom_bytes},
+                     "bytes_per_launch": dom_bytes,
+                     "timing": "hip events recorded around spec_softmax_stats on the step's "
+                               "stream in steps after the timed region (kernel plus its "
+                               "dispatch gap; a kernel trace reads ~2% less)"},
         "cpu_baseline": cpu,
+        "cpu_baseline_1thread": cpu1,
+        "parity": par,
     }
     print(json.dumps(rec), flush=True)
     return 0

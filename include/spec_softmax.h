@@ -45,7 +45,9 @@
  *     sequence's num_accepted -1 and its out_tokens all -1; no out-of-bounds
  *     access happens.
  *   - Limits: 1 <= B, 1 <= K <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V,
- *     T finite and > 0, B*(K+1)*V < 2^62.
+ *     T finite and > 0, B*(2K+1) <= SPEC_MAX_ROWS (the row count of one
+ *     launch of 1024-thread workgroups); R <= SPEC_MAX_ROWS for the per-row
+ *     calls.  Larger shapes return SPEC_ERR_INVALID_ARG.
  */
 #ifndef SPEC_SOFTMAX_H
 #define SPEC_SOFTMAX_H
@@ -67,6 +69,7 @@ extern "C" {
 
 #define SPEC_MAX_K 64
 #define SPEC_MAX_V (1 << 20)
+#define SPEC_MAX_ROWS 4194303 /* (2^32 - 1) / 1024 */
 
 /*
  * spec_softmax_stats -- temperature softmax statistics of every row.
@@ -223,44 +226,41 @@ int spec_filter(const void* logits, int dtype, int R, int V, float temperature, 
                 float top_p, float* thresholds, float* row_stats, void* filtered, void* stream);
 
 /*
- * spec_verify_workspace_size -- bytes of device workspace spec_verify_fused
- * needs for this shape (0 for an invalid shape).  Independent of T.
+ * spec_verify_step_workspace_size -- bytes of device workspace spec_verify_step
+ * needs for this shape (0 for an invalid shape).  Independent of T and of the
+ * device.
  */
-size_t spec_verify_workspace_size(int B, int K, int V, int dtype);
+size_t spec_verify_step_workspace_size(int B, int K, int V, int dtype);
 
 /*
- * spec_verify_fused -- the whole verify (spec_softmax_stats, spec_verify and
- * spec_residual_sample together) in one persistent launch, with the same
- * results.  The residual/bonus work of each sequence runs while the rows of
- * later sequences are still streaming, so its cost hides under the HBM-bound
- * row statistics.
- * Defines: everything cited above (alg. 2 steps 2-4, sec. 4.2, Decoding
- * transforms, Pitfalls).
- *   inputs         as for the three calls (target, draft, tokens, uniforms)
+ * spec_verify_step -- the whole verify step (what spec_softmax_stats followed
+ * by spec_verify_sample computes: alg. 2 steps 2-4, sec. 4.2, "Decoding
+ * transforms" and the Pitfalls readings cited above) in two launches.  With
+ * fewer than 32 sequences, too few to occupy the device one workgroup per
+ * sequence, each sequence's final draw is split over several workgroups
+ * that sweep parts of its row(s) and hand their sums to the one that
+ * finishes last; from 32 sequences on it is spec_softmax_stats followed by
+ * spec_verify_sample.  The outputs are the same bits as those two calls give
+ * (the split draw forms the same sums in the same order).
+ *   inputs         as for the calls above (target, draft, tokens, uniforms)
  *   target_stats, draft_stats, num_accepted, out_tokens   outputs as above
  *   probs, num_emitted   optional outputs as above (NULL to skip)
- *   workspace      device memory of at least spec_verify_workspace_size(...)
+ *   workspace      device memory of at least spec_verify_step_workspace_size
  *                  bytes, 256-byte aligned, owned by the caller.  It must be
- *                  all zero before its first use; every completed call puts
- *                  its counters and flags back to zero, so it can be reused
- *                  call after call by any call with B and K no larger than
- *                  those of the calls before it (a larger B or K needs a
- *                  zeroed workspace).
- *                  Two calls that are in flight at the same time need two
- *                  workspaces.  A non-zero third 32-bit word after a call
- *                  means a bounded wait inside the kernel gave up (never
- *                  expected; the sequence concerned then has no final token)
- *                  and the workspace must be cleared before it is used again.
+ *                  all zero before its first use; every completed call leaves
+ *                  its counters zero again, so it can be reused by any later
+ *                  call whose workspace size is not larger.  Two calls in
+ *                  flight at the same time need two workspaces.
  * Returns SPEC_OK, SPEC_ERR_INVALID_ARG (also for a workspace that is too
  * small or misaligned) or SPEC_ERR_LAUNCH.
  */
-int spec_verify_fused(const void* target_logits, const void* draft_logits, int dtype,
-                      const int32_t* draft_tokens, const float* uniforms,
-                      int B, int K, int V, float temperature,
-                      float* target_stats, float* draft_stats,
-                      int32_t* num_accepted, int32_t* out_tokens, float* probs,
-                      int32_t* num_emitted, void* workspace, size_t workspace_bytes,
-                      void* stream);
+int spec_verify_step(const void* target_logits, const void* draft_logits, int dtype,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     int B, int K, int V, float temperature,
+                     float* target_stats, float* draft_stats,
+                     int32_t* num_accepted, int32_t* out_tokens, float* probs,
+                     int32_t* num_emitted, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* spec_status_string(int status);

@@ -22,10 +22,11 @@ SPEC_DTYPE_BF16 = 1
 SPEC_OK = 0
 SPEC_MAX_K = 64
 SPEC_MAX_V = 1 << 20
+SPEC_MAX_ROWS = 4194303
 
 EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
-           "spec_verify_workspace_size", "spec_verify_fused", "spec_greedy_verify", "spec_sample",
-           "spec_filter", "spec_verify_sample")
+           "spec_verify_step_workspace_size", "spec_verify_step", "spec_greedy_verify",
+           "spec_sample", "spec_filter", "spec_verify_sample")
 
 _lib = None
 
@@ -51,11 +52,11 @@ def load(path: str = LIB_PATH):
     L.spec_residual_sample.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, f32,
                                        vp, vp, vp]
     L.spec_residual_sample.restype = i32
-    L.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32]
-    L.spec_verify_workspace_size.restype = ctypes.c_size_t
-    L.spec_verify_fused.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
-                                    vp, vp, ctypes.c_size_t, vp]
-    L.spec_verify_fused.restype = i32
+    L.spec_verify_step_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.spec_verify_step_workspace_size.restype = ctypes.c_size_t
+    L.spec_verify_step.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                   vp, vp, ctypes.c_size_t, vp]
+    L.spec_verify_step.restype = i32
     L.spec_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.spec_greedy_verify.restype = i32
     L.spec_sample.argtypes = [vp, i32, i32, i32, f32, vp, vp, vp, vp]
@@ -236,31 +237,22 @@ def verify_two_call(target, draft, tokens, uniforms, T: float, stream=None) -> d
 
 
 def workspace_size(B: int, K: int, V: int, dtype: torch.dtype) -> int:
-    """Bytes of workspace spec_verify_fused needs for this shape."""
+    """Bytes of workspace spec_verify_step needs for this shape."""
     code = SPEC_DTYPE_F32 if dtype == torch.float32 else SPEC_DTYPE_BF16
-    n = load().spec_verify_workspace_size(B, K, V, code)
+    n = load().spec_verify_step_workspace_size(B, K, V, code)
     if n == 0:
         raise ValueError(f"invalid shape B={B} K={K} V={V}")
     return int(n)
 
 
 def new_workspace(B: int, K: int, V: int, dtype: torch.dtype, device) -> torch.Tensor:
-    """A zeroed workspace for spec_verify_fused (reusable: each completed call
-    leaves it zeroed)."""
+    """A zeroed workspace for spec_verify_step (reusable: each completed call
+    leaves its counters zero)."""
     return torch.zeros(workspace_size(B, K, V, dtype), dtype=torch.uint8, device=device)
 
 
-def workspace_error(workspace: torch.Tensor) -> int:
-    """The workspace's error word (0 unless a wait inside the kernel gave up)."""
-    return int(workspace[8:12].view(torch.int32).item())
-
-
-def verify_fused(target, draft, tokens, uniforms, T: float, workspace: torch.Tensor,
-                 target_stats=None, draft_stats=None, num_accepted=None, out_tokens=None,
-                 probs=True, num_emitted=True, stream=None) -> dict:
-    """spec_verify_fused: the whole verify in one launch."""
-    B, K, V = _shapes(target, draft)
-    dev = target.device
+def _step_outputs(B, K, dev, target_stats, draft_stats, num_accepted, out_tokens, probs,
+                  num_emitted):
     if target_stats is None:
         target_stats = torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev)
     if draft_stats is None:
@@ -277,22 +269,33 @@ def verify_fused(target, draft, tokens, uniforms, T: float, workspace: torch.Ten
         num_emitted = torch.empty(B, dtype=torch.int32, device=dev)
     elif num_emitted is False:
         num_emitted = None
+    return target_stats, draft_stats, num_accepted, out_tokens, probs, num_emitted
+
+
+def verify_step(target, draft, tokens, uniforms, T: float, workspace: torch.Tensor,
+                target_stats=None, draft_stats=None, num_accepted=None, out_tokens=None,
+                probs=True, num_emitted=True, stream=None) -> dict:
+    """spec_verify_step: the whole verify in two launches that split rows and
+    sequences over several workgroups when the batch is small."""
+    B, K, V = _shapes(target, draft)
+    ts, ds, n, out, pr, ne = _step_outputs(B, K, target.device, target_stats, draft_stats,
+                                           num_accepted, out_tokens, probs, num_emitted)
     if workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a uint8 tensor")
-    rc = load().spec_verify_fused(
+    rc = load().spec_verify_step(
         _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
         _dev(tokens, "tokens", torch.int32, (B, K)),
         _dev(uniforms, "uniforms", torch.float32, (B, K + 1)), B, K, V, float(T),
-        _dev(target_stats, "target_stats", torch.float32, (B, K + 1, 2)),
-        _dev(draft_stats, "draft_stats", torch.float32, (B, K, 2)),
-        _dev(num_accepted, "num_accepted", torch.int32, (B,)),
-        _dev(out_tokens, "out_tokens", torch.int32, (B, K + 1)),
-        None if probs is None else _dev(probs, "probs", torch.float32, (B, K, 2)),
-        None if num_emitted is None else _dev(num_emitted, "num_emitted", torch.int32, (B,)),
+        _dev(ts, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(ds, "draft_stats", torch.float32, (B, K, 2)),
+        _dev(n, "num_accepted", torch.int32, (B,)),
+        _dev(out, "out_tokens", torch.int32, (B, K + 1)),
+        None if pr is None else _dev(pr, "probs", torch.float32, (B, K, 2)),
+        None if ne is None else _dev(ne, "num_emitted", torch.int32, (B,)),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
-    _check(rc, "spec_verify_fused")
-    return dict(target_stats=target_stats, draft_stats=draft_stats, num_accepted=num_accepted,
-                out_tokens=out_tokens, probs=probs, num_emitted=num_emitted)
+    _check(rc, "spec_verify_step")
+    return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=pr,
+                num_emitted=ne)
 
 
 def greedy_verify(target, tokens, target_argmax=None, num_accepted=None, out_tokens=None,

@@ -4,7 +4,9 @@
 
 Compiles csrc/spec_softmax.hip with hipcc for gfx950 only.  Packed fp32
 instructions are disabled (-packed-fp32-ops) and floating-point contraction
-is off, so every rounding is the one written in the source.
+is off, so every rounding is the one written in the source.  Also builds
+libspec_probe.so from csrc/read_ceiling.hip, a streaming-read probe the
+benchmark uses to measure this part's read ceiling (not part of the verify).
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "spec_softmax.hip")
 LIB = os.path.join(PKG, "libspec_softmax.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "read_ceiling.hip")
+PROBE_LIB = os.path.join(PKG, "libspec_probe.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 
@@ -28,17 +32,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libspec_softmax.so)")
 
 
-def command(out: str = LIB) -> list[str]:
+def command(out: str = LIB, src: str = SRC) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"),
-            SRC, "-o", out]
+            src, "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def _compile(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp"
+    cmd = command(tmp, src)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +53,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the verify library and the read-ceiling probe; returns the library's path."""
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
+    return _compile(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -6,8 +6,6 @@
 //                    tests, first rejection
 //   residual_kernel  one workgroup per sequence: residual (or bonus) weights on
 //                    the row(s) at the first rejection and the inverse-CDF draw
-//   fused_kernel     persistent: all of the above in one launch, with the
-//                    residual work interleaved with the row streaming
 //
 // What is computed: wikillm.com card for arXiv 2302.01318, Method
 // ("Modified rejection sampling", paper sec. 4.2; "Algorithm: Speculative
@@ -309,9 +307,10 @@ template <int DT, bool XB>
 __device__ int verify_seq(int64_t b, const void* tgt, const void* dft, const int32_t* tokens,
                            const float* uni, const float* ts_b, const float* ds_b, int K,
                            int V, double invT, int32_t* num_accepted, int32_t* out_tokens,
-                           float* probs, bool skip_final) {
+                           float* probs, bool skip_final, bool write = true) {
   // ts_b: this sequence's target stats [K+1][2]; ds_b: its draft stats [K][2].
   // skip_final: leave out_tokens[b][n] to the final draw (written elsewhere).
+  // write: store num_accepted, out_tokens and probs (false: only return n).
   const int t = lane_id();
   const int64_t K1 = K + 1;
   bool valid = true;
@@ -337,6 +336,7 @@ __device__ int verify_seq(int64_t b, const void* tgt, const void* dft, const int
   const bool all_valid = __all(valid);
   const unsigned long long rej = __ballot(reject);
   const int n = !all_valid ? -1 : (rej ? __ffsll(static_cast<long long>(rej)) - 1 : K);
+  if (!write) return n;
   if (t == 0) num_accepted[b] = n;
   for (int pos = t; pos <= K; pos += kWave)
     if (!(skip_final && pos == n)) out_tokens[b * K1 + pos] = (pos < n) ? tokens[b * K + pos] : -1;
@@ -407,9 +407,9 @@ constexpr int kUncMax = 2;
 constexpr double kDelta = 1.0 / 65536.0;
 constexpr int kDrawG = 2;  // chunks per item of the fast sweep
 
-// Dynamic LDS of the fast sweep for a row of nch chunks: per item, four row
-// totals of each of A, Bv, Lq, Lp, then W, then unc_n, kUncMax unc_idx and
-// kUncMax unc_code.
+// Dynamic LDS of the fast sweep for a row of nch chunks: per item, the
+// finish's total W, then four row totals of each of A, Bv, Lq, Lp, unc_n,
+// kUncMax unc_idx and kUncMax unc_code (LdsItems).
 constexpr size_t draw_fast_lds(int nch) {
   return static_cast<size_t>((nch + kDrawG - 1) / kDrawG) *
          (17 * sizeof(double) + (1 + 2 * kUncMax) * sizeof(int));
@@ -1147,7 +1147,9 @@ struct DrawShared {
   float redf[BLOCK / kWave];
   int sel[4];
   double seld[4];
-  unsigned next;  // the fast sweep's item counter
+  double norm[2];  // the exact normalisers S_q, S_p of a finished fast sweep
+  unsigned next;   // the fast sweep's item counter
+  unsigned last;   // split draw: this workgroup finishes the sequence
 };
 
 // Exact two-sweep draw (whole block).  W: nch doubles of scratch.  With
@@ -1155,7 +1157,7 @@ struct DrawShared {
 // as given and the first sweep is skipped.  Returns the token (every
 // thread), or -1 when no token carries positive weight.
 template <int BLOCK, int DT, bool ET = false>
-__device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh,
+__device__ __forceinline__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BLOCK>& sh,
                          bool have_s = false, double Sq_in = 0.0, double Sp_in = 0.0) {
   constexpr int NW = BLOCK / kWave;
   constexpr int E = 16 / Elt<DT>::bytes;
@@ -1221,55 +1223,200 @@ __device__ int slow_draw(DrawRows R, int nch, double* W, double u, DrawShared<BL
   return tok;
 }
 
+// ------------------------------------------------------ sweep item results
+//
+// What the fast sweep leaves per item: the sums A, Bv of the clearly positive
+// tokens' e_q and e_p, the normaliser parts Lq, Lp, and the uncertain tokens
+// (count, token ids, and their two bf16 codes on the table path).  Each sum is
+// kept as the four in-row scan totals of the wave that swept the item (lanes
+// 15, 31, 47, 63) and added in sum_row_totals' order where it is read, so no
+// result depends on which wave, or which workgroup, swept which item.
+
+// In the LDS of the one workgroup that sweeps and draws: A, Bv, Lq, Lp as
+// arrays of 4*ni doubles, then unc_n[ni], unc_idx[ni*kUncMax],
+// unc_code[ni*kUncMax].
+struct LdsItems {
+  double* A;
+  double* Bv;
+  double* Lq;
+  double* Lp;
+  int* unc_n;
+  int* unc_idx;
+  unsigned* unc_code;
+  __device__ __forceinline__ LdsItems(double* base, int ni)
+      : A(base), Bv(base + 4 * ni), Lq(base + 8 * ni), Lp(base + 12 * ni),
+        unc_n(reinterpret_cast<int*>(base + 16 * ni)), unc_idx(unc_n + ni),
+        unc_code(reinterpret_cast<unsigned*>(unc_idx + ni * kUncMax)) {}
+  // cs.A, cs.Bv, lq, lp: in-row scans (chunk_reduce with RS); the uncertain
+  // list is the same in every lane.
+  __device__ __forceinline__ void emit(int s, const ChunkSums& cs, double lq, double lp) const {
+    const int lane = lane_id();
+    if ((lane & 15) == 15) {
+      const int i = 4 * s + (lane >> 4);
+      A[i] = cs.A;
+      Bv[i] = cs.Bv;
+      Lq[i] = lq;
+      Lp[i] = lp;
+    }
+    if (lane == 0) {
+      unc_n[s] = cs.n_unc;
+#pragma unroll
+      for (int j = 0; j < kUncMax; ++j) {
+        unc_idx[s * kUncMax + j] = cs.unc[j];
+        unc_code[s * kUncMax + j] = cs.ucode[j];
+      }
+    }
+  }
+  __device__ __forceinline__ double a(int c) const {
+    return sum_row_totals(A[4 * c], A[4 * c + 1], A[4 * c + 2], A[4 * c + 3]);
+  }
+  __device__ __forceinline__ double bv(int c) const {
+    return sum_row_totals(Bv[4 * c], Bv[4 * c + 1], Bv[4 * c + 2], Bv[4 * c + 3]);
+  }
+  __device__ __forceinline__ double lq(int c) const {
+    return sum_row_totals(Lq[4 * c], Lq[4 * c + 1], Lq[4 * c + 2], Lq[4 * c + 3]);
+  }
+  __device__ __forceinline__ double lp(int c) const {
+    return sum_row_totals(Lp[4 * c], Lp[4 * c + 1], Lp[4 * c + 2], Lp[4 * c + 3]);
+  }
+  __device__ __forceinline__ int n_unc(int c) const { return unc_n[c]; }
+  __device__ __forceinline__ int unc(int c, int j) const { return unc_idx[c * kUncMax + j]; }
+  __device__ __forceinline__ unsigned code(int c, int j) const {
+    return unc_code[c * kUncMax + j];
+  }
+};
+
+// Bytes of the LDS item arrays for ni items.
+constexpr size_t lds_items_bytes(int ni) {
+  return static_cast<size_t>(ni) * (16 * sizeof(double) + (1 + 2 * kUncMax) * sizeof(int));
+}
+
+// In device memory, for a sequence whose sweep is split over several
+// workgroups: one record of kItemRec doubles per item -- doubles 4r..4r+3 hold
+// row r's totals of A, Bv, Lq, Lp, then the ints unc_n, unc_idx[kUncMax],
+// unc_code[kUncMax] -- written with sc1 stores by the workgroup that swept the
+// item and read with sc1 loads by the workgroup that draws, possibly on
+// another XCD (device_common.hpp).  `rec` must be uniform.
+constexpr int kItemRec = 20;  // doubles per record (160 bytes)
+static_assert(16 + (1 + 2 * kUncMax + 1) / 2 <= kItemRec, "record layout");
+
+struct GlobalItems {
+  double* rec;
+  Src<true, double> D;
+  Src<true, int> I;
+  __device__ __forceinline__ GlobalItems(double* base, int ni)
+      : rec(base), D(base, static_cast<int64_t>(ni) * kItemRec),
+        I(reinterpret_cast<const int*>(base), static_cast<int64_t>(ni) * kItemRec * 2) {}
+  // Writes the records of items s0 .. s0+n-1 from their LDS copy `L`
+  // (LdsItems holding them as items 0 .. n-1), the whole block one double
+  // each.  The stores are issued here, after the sweep, and not item by item
+  // during it: on this architecture stores count in the same vmcnt as loads,
+  // so a long write-through store would hold up the sweep's next loads.
+  __device__ __forceinline__ void write_from(const LdsItems& L, int s0, int n) const {
+    double* base = rec + static_cast<int64_t>(s0) * kItemRec;
+    for (int k = threadIdx.x; k < n * kItemRec; k += blockDim.x) {
+      const int i = k / kItemRec, w = k - i * kItemRec;
+      double v;
+      if (w < 16) {
+        const int r = w >> 2, f = w & 3;
+        const double* src = f == 0 ? L.A : f == 1 ? L.Bv : f == 2 ? L.Lq : L.Lp;
+        v = src[4 * i + r];
+      } else {
+        // int words 32 + 2(w-16), +1: unc_n, unc_idx[..], unc_code[..], 0 padding
+        int lo_hi[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int q = 2 * (w - 16) + h;
+          lo_hi[h] = q == 0 ? L.unc_n[i]
+                   : q <= kUncMax ? L.unc_idx[i * kUncMax + q - 1]
+                   : q <= 2 * kUncMax ? static_cast<int>(L.unc_code[i * kUncMax + q - 1 - kUncMax])
+                   : 0;
+        }
+        v = __hiloint2double(lo_hi[1], lo_hi[0]);
+      }
+      st<true>(&base[k], v);
+    }
+  }
+  __device__ __forceinline__ double field(int c, int f) const {
+    const int64_t o = static_cast<int64_t>(c) * kItemRec + f;
+    return sum_row_totals(D[o], D[o + 4], D[o + 8], D[o + 12]);
+  }
+  __device__ __forceinline__ double a(int c) const { return field(c, 0); }
+  __device__ __forceinline__ double bv(int c) const { return field(c, 1); }
+  __device__ __forceinline__ double lq(int c) const { return field(c, 2); }
+  __device__ __forceinline__ double lp(int c) const { return field(c, 3); }
+  __device__ __forceinline__ int word(int c, int k) const {
+    return I[static_cast<int64_t>(c) * (2 * kItemRec) + 32 + k];
+  }
+  __device__ __forceinline__ int n_unc(int c) const { return word(c, 0); }
+  __device__ __forceinline__ int unc(int c, int j) const { return word(c, 1 + j); }
+  __device__ __forceinline__ unsigned code(int c, int j) const {
+    return static_cast<unsigned>(word(c, 1 + kUncMax + j));
+  }
+};
+
+// The exact normalisers S_q, S_p of a finished fast sweep, to every thread:
+// wave 0 adds the items' parts, item c in lane c % 64 in item order, then a
+// butterfly -- the same order whatever the block size and however many
+// workgroups swept.  Contains a barrier.
+template <int BLOCK, typename Items>
+__device__ __forceinline__ void item_normalisers(const Items& it, int ni, DrawShared<BLOCK>& sh,
+                                                 double& Sq, double& Sp) {
+  if (threadIdx.x < kWave) {
+    double lq = 0.0, lp = 0.0;
+    for (int c = lane_id(); c < ni; c += kWave) {
+      lq = lq + it.lq(c);
+      lp = lp + it.lp(c);
+    }
+    lq = wave_sum(lq);
+    lp = wave_sum(lp);
+    if (threadIdx.x == 0) {
+      sh.norm[0] = lq;
+      sh.norm[1] = lp;
+    }
+  }
+  __syncthreads();
+  Sq = sh.norm[0];
+  Sp = sh.norm[1];
+}
+
 // Fast-path finish (whole block) from a sweep's results: the exact
-// normalisers Sq, Sp and, per chunk, the sums A, Bv and the uncertain lists
-// (XB: written by other workgroups of this launch; RS: A and Bv hold four row
-// totals per chunk, added here in the order wave_sum_rows uses).  W (nch
-// doubles of this workgroup's own memory; it may be A itself when neither XB
-// nor RS is set) receives the chunk totals W_c.  sh.sel[3] must be 0, with a
-// barrier between the clearing and the call.  Returns the token, -1 (nothing
-// to draw), -2 (take the slow path) or -3 (the residual has no mass: draw
-// from q_n instead).
-template <int BLOCK, int DT, bool XB, bool ET = false, bool RS = false, int G = 1>
-__device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src<XB, double> A,
-                           Src<XB, double> Bv, Src<XB, int> unc_n, Src<XB, int> unc_idx,
-                           double* W, double u, DrawShared<BLOCK>& sh,
-                           const unsigned* unc_code = nullptr) {
+// normalisers Sq, Sp and, per item of G chunks, the view `it` (LdsItems or
+// GlobalItems).  W (ni doubles of this workgroup's LDS) receives the item
+// totals W_c.  sh.sel[3] must be 0, with a barrier between the clearing and
+// the call.  ET: the sweep took the bf16 table path, which records the
+// uncertain tokens' codes.  Returns the token, -1 (nothing to draw), -2 (take
+// the slow path) or -3 (the residual has no mass: draw from q_n instead).
+template <int BLOCK, int DT, bool ET, int G, typename Items>
+__device__ __forceinline__ int fast_finish(const DrawRows& R, int ni, double Sq, double Sp, const Items& it,
+                           double* W, double u, DrawShared<BLOCK>& sh) {
   const int tid = threadIdx.x, wv = tid / kWave;
-  auto chunk_total = [&](const Src<XB, double>& X, int c) {
-    if constexpr (RS)
-      return sum_row_totals(X[4 * c], X[4 * c + 1], X[4 * c + 2], X[4 * c + 3]);
-    else
-      return X[c];
-  };
   double iq = 1.0, ip = 1.0;
   if (R.mode == kModeResidual) {
     iq = 1.0 / Sq;
     ip = 1.0 / Sp;
     const double ratio = (Sq / Sp) / R.rho;  // exact over fp32-normaliser ratio
     bool ok = fabs(ratio - 1.0) <= kDelta / 4;
-    for (int c = tid; c < nch; c += BLOCK) {
-      const double a = chunk_total(A, c), bv = chunk_total(Bv, c);
-      const int nu = unc_n[c];
-      int x[kUncMax];
-#pragma unroll
-      for (int j = 0; j < kUncMax; ++j) x[j] = unc_idx[static_cast<int64_t>(c) * kUncMax + j];
+    for (int c = tid; c < ni; c += BLOCK) {
+      const double a = it.a(c), bv = it.bv(c);
+      const int nu = it.n_unc(c);
       double w = a * iq - bv * ip;
       w = w > 0.0 ? w : 0.0;
       if (nu > kUncMax) ok = false;
 #pragma unroll
       for (int j = 0; j < kUncMax; ++j) {
         if (j < nu) {
-          // the token's stored logits: the codes the sweep kept (bf16 words
+          // the token's stored logits: the codes the sweep kept (bf16 table
           // path, exact), else read back from the rows
           float zq, zp;
-          if (DT == kBF16 && unc_code != nullptr) {
-            const unsigned cw = unc_code[static_cast<int64_t>(c) * kUncMax + j];
+          if constexpr (DT == kBF16 && ET) {
+            const unsigned cw = it.code(c, j);
             zq = __uint_as_float(cw << 16);
             zp = __uint_as_float(cw & 0xFFFF0000u);
           } else {
-            zq = logit_f32<DT>(R.qrow, x[j]);
-            zp = logit_f32<DT>(R.prow, x[j]);
+            const int x = it.unc(c, j);
+            zq = logit_f32<DT>(R.qrow, x);
+            zp = logit_f32<DT>(R.prow, x);
           }
           const double eq = row_exp<DT, ET, false>(R, zq, sh.tab);
           const double ep = row_exp<DT, ET, true>(R, zp, sh.tab);
@@ -1283,10 +1430,10 @@ __device__ int fast_finish(const DrawRows& R, int nch, double Sq, double Sp, Src
     __syncthreads();
     if (sh.sel[3] != 0) return -2;
   } else {
-    for (int c = tid; c < nch; c += BLOCK) W[c] = chunk_total(A, c);
+    for (int c = tid; c < ni; c += BLOCK) W[c] = it.a(c);
     __syncthreads();
   }
-  if (wv == 0) locate_chunk(W, nch, u, sh.sel, sh.seld);
+  if (wv == 0) locate_chunk(W, ni, u, sh.sel, sh.seld);
   __syncthreads();
   if (R.mode == kModeResidual && !(sh.seld[2] > 0.0)) {
     __syncthreads();
@@ -1371,46 +1518,23 @@ __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, in
 // The whole draw for one row (pair) by one workgroup: the one-sweep fast path
 // when `fast`, else or on its failure the exact two-sweep path (dyn: nch
 // doubles).  The fast sweep's items are kDrawG chunks each, and dynamic LDS
-// `dyn` holds, for its ni items (draw_fast_lds bytes), A, Bv, Lq, Lp: four
-// row totals per item, 4*ni doubles each; W: ni doubles; unc_n: ni ints;
-// unc_idx, unc_code: ni*kUncMax ints each.  sh.tab must hold the exp table.
+// `dyn` holds, for its ni items (draw_fast_lds bytes), W: ni doubles, then
+// the LdsItems arrays.  sh.tab must hold the exp table.
 // Returns the token (every thread), or -1 when no token has positive weight.
 template <int BLOCK, int DT, bool ET = false>
 __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast, double* dyn,
                                           DrawShared<BLOCK>& sh) {
   constexpr int E = 16 / Elt<DT>::bytes;
   constexpr int NW = BLOCK / kWave;
-  const int wv = uniform(static_cast<int>(threadIdx.x) / kWave), lane = lane_id();
+  const int wv = uniform(static_cast<int>(threadIdx.x) / kWave);
   const int nch = (R.V + kWave * E - 1) / (kWave * E);
   const int ni = (nch + kDrawG - 1) / kDrawG;  // sweep items
   int tok = -2;
   double Sq = 0.0, Sp = 0.0;
   if (fast) {
-    double* A = dyn;
-    double* Bv = A + 4 * ni;
-    double* Lq = Bv + 4 * ni;
-    double* Lp = Lq + 4 * ni;
-    double* W = Lp + 4 * ni;
-    int* unc_n = reinterpret_cast<int*>(W + ni);
-    int* unc_idx = unc_n + ni;
-    unsigned* unc_code = reinterpret_cast<unsigned*>(unc_idx + ni * kUncMax);
-    auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) {
-      if ((lane & 15) == 15) {  // the row totals
-        const int i = 4 * c + (lane >> 4);
-        A[i] = cs.A;
-        Bv[i] = cs.Bv;
-        Lq[i] = lq;
-        Lp[i] = lp;
-      }
-      if (lane == 0) {
-        unc_n[c] = cs.n_unc;
-#pragma unroll
-        for (int j = 0; j < kUncMax; ++j) {
-          unc_idx[c * kUncMax + j] = cs.unc[j];
-          unc_code[c * kUncMax + j] = cs.ucode[j];
-        }
-      }
-    };
+    double* W = dyn;  // the finish's item totals, then the sweep's item arrays
+    const LdsItems it(dyn + ni, ni);
+    auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) { it.emit(c, cs, lq, lp); };
     if (threadIdx.x == 0) {
       sh.next = NW;
       sh.sel[3] = 0;
@@ -1421,18 +1545,8 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
     else
       wave_sweep_claimed<DT, kModeBonus, kDrawG, ET>(R, wv, ni, nch, &sh.next, sh.tab, emit);
     __syncthreads();
-    // the exact normalisers: item parts in item order, then a fixed tree
-    double lsq = 0.0, lsp = 0.0;
-    for (int c = threadIdx.x; c < ni; c += BLOCK) {
-      lsq = lsq + sum_row_totals(Lq[4 * c], Lq[4 * c + 1], Lq[4 * c + 2], Lq[4 * c + 3]);
-      lsp = lsp + sum_row_totals(Lp[4 * c], Lp[4 * c + 1], Lp[4 * c + 2], Lp[4 * c + 3]);
-    }
-    Sq = block_sum<BLOCK>(lsq, sh.red);
-    Sp = block_sum<BLOCK>(lsp, sh.red);
-    tok = fast_finish<BLOCK, DT, false, ET, true, kDrawG>(
-        R, ni, Sq, Sp, Src<false, double>(A, 4 * ni), Src<false, double>(Bv, 4 * ni),
-        Src<false, int>(unc_n, ni), Src<false, int>(unc_idx, ni * kUncMax), W, u, sh,
-        DT == kBF16 && ET ? unc_code : nullptr);
+    item_normalisers<BLOCK>(it, ni, sh, Sq, Sp);
+    tok = fast_finish<BLOCK, DT, ET, kDrawG>(R, ni, Sq, Sp, it, W, u, sh);
   }
   if (tok == -3) {  // residual without mass: the bonus draw from q_n
     DrawRows Rb = R;
@@ -1551,6 +1665,155 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
   __syncthreads();  // sel[] is reused by the draw
   draw_sequence<BLOCK, DT>(b, n, tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
                            out_tokens, num_emitted, dyn, sh, true, DT == kBF16 && etab);
+}
+
+// ======================================================= split final draw
+//
+// The final draw with one sequence's sweep spread over P workgroups
+// ("parts"), for batches with too few sequences to fill the device one
+// workgroup per sequence, and to even out the residual and bonus draws'
+// different costs.  Every part runs the accept scan (wave 0, while the other
+// waves fill the exponential tables), sweeps its own contiguous range of
+// items and stores their results as GlobalItems records; the part that
+// finishes last -- counted on parts_done[b] -- reads every record back and
+// draws exactly as one workgroup does after its own sweep (the same sums in
+// the same order), so the token does not depend on P or on the block size.
+// Part 0 writes the scan's outputs; the last part writes out_tokens[b][n] and
+// num_emitted[b] and puts parts_done[b] back to 0 (it must be zero before the
+// first launch and is zero after every completed one).
+//
+// Dynamic LDS: with etab (bf16 rows), the table exp(z/T) both rows share
+// (kETab doubles), then max(ni, nch) doubles for the finish, then the LdsItems
+// arrays of the part's own items (at most ceil(ni/P)).  Rows that cannot
+// share the table (|m|/T > kSharedTableMax) compute their exponentials; the
+// per-row tables of the one-workgroup draw hold the same values
+// (row_tok_exp), so the bits agree.
+struct SplitDraw {
+  const void* tgt;
+  const void* dft;
+  const int32_t* tokens;
+  const float* uni;
+  const float* tstats;
+  const float* dstats;
+  int32_t* num_accepted;
+  int32_t* out_tokens;
+  float* probs;
+  int32_t* num_emitted;
+  unsigned* parts_done;  // [B]
+  double* items;         // [B][ni][kItemRec]
+  int K, V, P, ni, nch, etab;
+  double invT, yscale;
+};
+
+template <int BLOCK, int DT>
+__global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a) {
+  static_assert(BLOCK > kWave, "waves other than the first fill the tables");
+  constexpr int NW = BLOCK / kWave;
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
+  const int64_t b = blockIdx.x / static_cast<unsigned>(a.P);
+  const int part = static_cast<int>(blockIdx.x % static_cast<unsigned>(a.P));
+  const int K = a.K, V = a.V, tid = threadIdx.x;
+  const int64_t K1 = K + 1;
+  const bool etab = DT == kBF16 && a.etab != 0;
+  if (tid < kWave) {
+    const int n = verify_seq<DT, false>(b, a.tgt, a.dft, a.tokens, a.uni, a.tstats + 2 * b * K1,
+                                        a.dstats + 2 * b * K, K, V, a.invT, a.num_accepted,
+                                        a.out_tokens, a.probs, true, part == 0);
+    if (tid == 0) sh.sel[0] = n;
+  } else {
+    fill_exp2_table(sh.tab, kWave);
+    if (etab) fill_shared_exp_table<BLOCK>(dyn, a.yscale, kWave);
+  }
+  __syncthreads();
+  const int n = uniform(sh.sel[0]);
+  DrawRows R;
+  bool rows_ok = false;
+  if (n >= 0 && n <= K) {
+    const int64_t rq = b * K1 + n, rp = b * K + (n < K ? n : 0);
+    rows_ok = make_draw_rows<DT>(b, n, K, V, a.tgt, a.dft, a.tstats[2 * rq],
+                                 a.tstats[2 * rq + 1], a.dstats[2 * rp], a.dstats[2 * rp + 1],
+                                 a.yscale, R);
+  }
+  if (rows_ok && etab && draw_rows_share_table(R)) use_shared_table(R, dyn);
+  double* work = dyn + (etab ? kETab : 0);
+  const GlobalItems it(a.items + b * static_cast<int64_t>(a.ni) * kItemRec, a.ni);
+  if (rows_ok) {
+    const int s0 = static_cast<int>(static_cast<int64_t>(part) * a.ni / a.P);
+    const int s1 = static_cast<int>(static_cast<int64_t>(part + 1) * a.ni / a.P);
+    // this part's items in LDS (after the finish's W area), written out below
+    const LdsItems own(work + max(a.ni, a.nch), s1 - s0);
+    if (tid == 0) sh.next = s0 + NW;
+    __syncthreads();  // also orders the scan's sel[0] read before later uses of sel[]
+    const int wv = uniform(tid / kWave);
+    auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) {
+      own.emit(c - s0, cs, lq, lp);
+    };
+    if (R.et != nullptr) {
+      if (R.mode == kModeResidual)
+        wave_sweep_claimed<DT, kModeResidual, kDrawG, true>(R, s0 + wv, s1, a.nch, &sh.next,
+                                                            sh.tab, emit);
+      else
+        wave_sweep_claimed<DT, kModeBonus, kDrawG, true>(R, s0 + wv, s1, a.nch, &sh.next, sh.tab,
+                                                         emit);
+    } else {
+      if (R.mode == kModeResidual)
+        wave_sweep_claimed<DT, kModeResidual, kDrawG, false>(R, s0 + wv, s1, a.nch, &sh.next,
+                                                             sh.tab, emit);
+      else
+        wave_sweep_claimed<DT, kModeBonus, kDrawG, false>(R, s0 + wv, s1, a.nch, &sh.next,
+                                                          sh.tab, emit);
+    }
+    __syncthreads();
+    it.write_from(own, s0, s1 - s0);
+  }
+  // this part's records are complete (device-coherent) before it is counted
+  store_complete();
+  __syncthreads();
+  if (tid == 0) {
+    sh.sel[3] = 0;
+    sh.last = atomic_add_dev(&a.parts_done[b], 1u) == static_cast<unsigned>(a.P - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (sh.last == 0u) return;
+
+  // ------------------------------------- the last part: the sequence's draw
+  if (n < 0 || n > K || !rows_ok) {
+    if (tid == 0) {
+      if (n >= 0 && n <= K) a.out_tokens[b * K1 + n] = -1;
+      if (a.num_emitted) a.num_emitted[b] = 0;
+      atomic_store_dev(&a.parts_done[b], 0u);
+    }
+    return;
+  }
+  const double u = a.uni[b * K1 + K];
+  double Sq, Sp;
+  item_normalisers<BLOCK>(it, a.ni, sh, Sq, Sp);  // its barrier orders the sel[3] clear
+  int tok;
+  if (R.et != nullptr) {
+    tok = fast_finish<BLOCK, DT, true, kDrawG>(R, a.ni, Sq, Sp, it, work, u, sh);
+    if (tok == -3) {  // residual without mass: the bonus draw from q_n
+      DrawRows Rb = R;
+      Rb.mode = kModeBonus;
+      tok = slow_draw<BLOCK, DT, true>(Rb, a.nch, work, u, sh);
+    } else if (tok == -2) {
+      tok = slow_draw<BLOCK, DT, true>(R, a.nch, work, u, sh, true, Sq, Sp);
+    }
+  } else {
+    tok = fast_finish<BLOCK, DT, false, kDrawG>(R, a.ni, Sq, Sp, it, work, u, sh);
+    if (tok == -3) {
+      DrawRows Rb = R;
+      Rb.mode = kModeBonus;
+      tok = slow_draw<BLOCK, DT, false>(Rb, a.nch, work, u, sh);
+    } else if (tok == -2) {
+      tok = slow_draw<BLOCK, DT, false>(R, a.nch, work, u, sh, true, Sq, Sp);
+    }
+  }
+  if (tid == 0) {
+    a.out_tokens[b * K1 + n] = tok;
+    if (a.num_emitted) a.num_emitted[b] = tok >= 0 ? n + 1 : 0;
+    atomic_store_dev(&a.parts_done[b], 0u);
+  }
 }
 
 // ============================================================ draft sampling
@@ -2233,324 +2496,6 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     if (tid == 0) {
       stats_out[2 * r] = m;
       stats_out[2 * r + 1] = want ? static_cast<float>(sum) : __builtin_nanf("");
-    }
-  }
-}
-
-// ==================================================================== fused
-
-// The fused kernel streams its rows non-temporal as well (measured faster
-// even though its slices re-read two rows per sequence).
-constexpr int kFusedLoad = kLoadStream;
-//
-// One persistent launch for the whole verify.  Work items, handed out in a
-// fixed order by a device-wide counter:
-//   ROW(b, r)    stats of row r of sequence b (the 2K+1 target and draft rows)
-//   SCAN(b)      accept scan of sequence b, once all its rows have stats
-//   SLICE(b, s)  fast-path sweep of chunks [s*CPS, (s+1)*CPS) at position n_b
-// Item order: group g holds ROW(g, *), then SCAN(g - D1), then
-// SLICE(g - D2, *) (D2 > D1), so a sequence's scan and slices are normally
-// ready to run when they are taken, and residual sweeps (fp64 VALU work) run
-// on the same CUs as later rows' streaming (HBM work).  The workgroup that
-// finishes the last SLICE of a sequence draws its final token.
-//
-// Hand-offs between workgroups (possibly on different XCDs) use the sc1
-// loads and stores of device_common.hpp.  A ROW publishes {m, s} as one
-// 64-bit atomic word whose non-zero value is also its ready flag (s is never
-// +0 and NaN is canonical), so a row needs no wait of its own; SCAN polls its
-// sequence's words, clears them, runs the scan and publishes {n, stats at n}
-// then a ready word; SLICE polls that word, and its stores complete before it
-// counts itself on a per-sequence counter whose last increment elects the
-// finisher, which clears the counters.  Every poll waits on items already
-// taken by running workgroups that never wait on later items, so the launch
-// always drains; a poll that exceeds kSpinLimit sets the error word and gives
-// up (not expected; that sequence then has no final token).
-//
-// Workspace, flags first (zero before the first launch and again after each
-// completed launch, except the error word):
-//   ctl[kCtlItem] item counter, ctl[kCtlExit] exit counter, ctl[kCtlErr]
-//   error word; stat_word[B*(2K+1)] (target rows b*(K+1)+t, then draft
-//   rows); ready[B]; slices_done[B]
-// then data written before it is read within each launch:
-//   rec[B][8] = {n, mq, sq, mp, sp}, sq_part[B][S], sp_part[B][S],
-//   A[B][nch], Bv[B][nch], unc_n[B][nch], unc_idx[B][nch][kUncMax]
-
-enum : int { kCtlItem = 0, kCtlExit = 1, kCtlErr = 2, kCtlWords = 64 };
-
-struct FusedArgs {
-  const void* tgt;
-  const void* dft;
-  const int32_t* tokens;
-  const float* uni;
-  float* tstats;
-  float* dstats;
-  int32_t* num_accepted;
-  int32_t* out_tokens;
-  float* probs;
-  int32_t* num_emitted;
-  unsigned* ctl;
-  unsigned long long* stat_word;
-  unsigned* ready;
-  unsigned* slices_done;
-  int* rec;
-  double* sq_part;
-  double* sp_part;
-  double* A;
-  double* Bv;
-  int* unc_n;
-  int* unc_idx;
-  int B, K, V;
-  int S;    // slices per sequence
-  int nch;  // chunks per row
-  int D1, D2;
-  int nseg;               // item-order segments
-  int seg_g0[8];          // first group of each segment
-  int seg_size[8];        // items per group in each segment
-  unsigned seg_item0[8];  // first item of each segment
-  unsigned total_items;
-  float c2;
-  double invT, yscale;
-};
-
-constexpr unsigned kSpinLimit = 1u << 22;
-constexpr int kFusedMaxRows = 2 * 64 + 1;
-// Chunks in one slice: kFusedCPW for each wave of the workgroup.  Each wave
-// keeps one chunk's loads in flight ahead of the one it computes: deeper
-// prefetch costs registers this kernel does not have (measured slower).
-constexpr int kFusedCPW = 4;
-
-template <int BLOCK>
-struct FusedShared {
-  DrawShared<BLOCK> d;
-  float scan_stats[kFusedMaxRows][2];
-  // a slice's per-chunk results, written out together when the slice ends
-  // (on this architecture stores count against the same wait counter as
-  // loads, so stores issued chunk by chunk would hold up the next loads)
-  double sA[(BLOCK / kWave) * kFusedCPW], sB[(BLOCK / kWave) * kFusedCPW];
-  int sUn[(BLOCK / kWave) * kFusedCPW], sUi[(BLOCK / kWave) * kFusedCPW][kUncMax];
-  unsigned item, flag;
-};
-
-__device__ __forceinline__ unsigned long long pack_stats(float m, float s) {
-  if (__builtin_isnan(s)) s = __builtin_nanf("");
-  return static_cast<unsigned long long>(__float_as_uint(m)) |
-         (static_cast<unsigned long long>(__float_as_uint(s)) << 32);
-}
-
-// At most 128 VGPRs, so that four 256-thread workgroups share a CU and a
-// row's streaming and another item's fp64 sweep overlap on it.
-template <int BLOCK, int DT, int VPG>
-__global__ __launch_bounds__(BLOCK, 1024 / BLOCK) void fused_kernel(FusedArgs a) {
-  constexpr int NW = BLOCK / kWave;
-  __shared__ FusedShared<BLOCK> sh;
-  extern __shared__ double wbuf[];  // nch doubles: chunk totals of a final draw
-  const int tid = threadIdx.x, wv = tid / kWave, lane = lane_id();
-  const int K = a.K, V = a.V;
-  const int64_t K1 = K + 1;
-  const int rows_per = 2 * K + 1;
-  fill_exp2_table(sh.d.tab);
-  unsigned next_item = 0;
-  if (tid == 0) next_item = atomic_add_dev(&a.ctl[kCtlItem], 1u);
-
-  for (;;) {
-    __syncthreads();
-    if (tid == 0) sh.item = next_item;
-    __syncthreads();
-    const unsigned item = uniform(sh.item);
-    if (item >= a.total_items) break;
-    if (tid == 0) next_item = atomic_add_dev(&a.ctl[kCtlItem], 1u);  // used next iteration
-
-    // decode: segment, group, offset within the group
-    int seg = 0;
-    while (seg + 1 < a.nseg && item >= a.seg_item0[seg + 1]) ++seg;
-    const unsigned rel = item - a.seg_item0[seg];
-    const int g = a.seg_g0[seg] + static_cast<int>(rel / a.seg_size[seg]);
-    int off = static_cast<int>(rel % a.seg_size[seg]);
-    const int nrow = g < a.B ? rows_per : 0;
-    const bool has_scan = g >= a.D1 && g - a.D1 < a.B;
-
-    if (off < nrow) {
-      // ---------------------------------------------------------------- ROW
-      const int b = g, r = off;
-      const char* row;
-      float* out;
-      if (r < K1) {
-        const int64_t rr = static_cast<int64_t>(b) * K1 + r;
-        row = static_cast<const char*>(a.tgt) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
-        out = a.tstats + 2 * rr;
-      } else {
-        const int64_t rr = static_cast<int64_t>(b) * K + (r - K1);
-        row = static_cast<const char*>(a.dft) + rr * static_cast<int64_t>(V) * Elt<DT>::bytes;
-        out = a.dstats + 2 * rr;
-      }
-      float m, s;
-      row_stats<BLOCK, DT, VPG, kFusedLoad>(row, V, a.c2, sh.d.redf, sh.d.red, m, s);
-      if (tid == 0) {
-        out[0] = m;
-        out[1] = s;
-        __hip_atomic_store(&a.stat_word[static_cast<int64_t>(b) * rows_per + r], pack_stats(m, s),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      continue;
-    }
-    off -= nrow;
-
-    if (has_scan && off == 0) {
-      // --------------------------------------------------------------- SCAN
-      const int b = g - a.D1;
-      if (wv == 0) {
-        unsigned long long* words = a.stat_word + static_cast<int64_t>(b) * rows_per;
-        bool ok = true;
-        for (int r0 = 0; r0 < rows_per; r0 += kWave) {
-          const int r = r0 + lane;
-          unsigned long long w = 0;
-          unsigned spins = 0;
-          for (;;) {
-            if (r < rows_per)
-              w = __hip_atomic_load(&words[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool all = __all(r >= rows_per || w != 0ull);
-            if (all || spins >= kSpinLimit) break;
-            __builtin_amdgcn_s_sleep(2);
-            ++spins;
-          }
-          ok = ok && spins < kSpinLimit;
-          if (r < rows_per) {
-            sh.scan_stats[r][0] = __uint_as_float(static_cast<unsigned>(w));
-            sh.scan_stats[r][1] = __uint_as_float(static_cast<unsigned>(w >> 32));
-            __hip_atomic_store(&words[r], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        if (!ok) {
-          if (lane == 0) atomic_store_dev(&a.ctl[kCtlErr], 1u);
-          for (int r = lane; r < rows_per; r += kWave) sh.scan_stats[r][1] = __builtin_nanf("");
-        }
-        // target rows are scan_stats[0..K], draft rows scan_stats[K+1..2K]
-        const int n = verify_seq<DT, false>(b, a.tgt, a.dft, a.tokens, a.uni,
-                                            &sh.scan_stats[0][0], &sh.scan_stats[K1][0], K, V,
-                                            a.invT, a.num_accepted, a.out_tokens, a.probs, true);
-        if (lane == 0) {
-          int* rc = a.rec + 8 * static_cast<int64_t>(b);
-          st<true>(&rc[0], n);
-          if (n >= 0) {
-            st<true>(reinterpret_cast<float*>(&rc[1]), sh.scan_stats[n][0]);
-            st<true>(reinterpret_cast<float*>(&rc[2]), sh.scan_stats[n][1]);
-            st<true>(reinterpret_cast<float*>(&rc[3]), n < K ? sh.scan_stats[K1 + n][0] : 0.f);
-            st<true>(reinterpret_cast<float*>(&rc[4]), n < K ? sh.scan_stats[K1 + n][1] : 1.f);
-          }
-          store_complete();
-          atomic_store_dev(&a.ready[b], 1u);
-        }
-      }
-      continue;
-    }
-    if (has_scan) off -= 1;
-
-    // ---------------------------------------------------------------- SLICE
-    const int b = g - a.D2, sl = off;
-    if (tid == 0) {
-      unsigned spins = 0;
-      while (atomic_load_dev(&a.ready[b]) == 0u && spins < kSpinLimit) {
-        __builtin_amdgcn_s_sleep(2);
-        ++spins;
-      }
-      sh.flag = spins < kSpinLimit ? 1u : 0u;
-      if (!sh.flag) atomic_store_dev(&a.ctl[kCtlErr], 1u);
-    }
-    __syncthreads();
-    const bool ready = uniform(sh.flag) != 0;
-    const Src<true, int> rc(a.rec + 8 * static_cast<int64_t>(b), 8);
-    const int n = ready ? uniform(rc[0]) : -1;
-    const float mq = uniform(__int_as_float(rc[1])), sq = uniform(__int_as_float(rc[2]));
-    const float mp = uniform(__int_as_float(rc[3])), sp = uniform(__int_as_float(rc[4]));
-    DrawRows R;
-    bool rows_valid = false;
-    if (n >= 0 && n <= K)
-      rows_valid = make_draw_rows<DT>(b, n, K, V, a.tgt, a.dft, mq, sq, n < K ? mp : 0.f,
-                                      n < K ? sp : 1.f, a.yscale, R);
-    const int64_t base = static_cast<int64_t>(b) * a.nch;
-    if (rows_valid) {
-      double lsq = 0.0, lsp = 0.0;
-      constexpr int cps = NW * kFusedCPW;
-      const int cb = sl * cps;  // first chunk of the slice
-      const int c0 = cb + wv;
-      const int c1 = min(a.nch, cb + cps);
-      auto emit = [&](int c, const ChunkSums& cs) {
-        if (lane == 0) {
-          const int i = c - cb;
-          sh.sA[i] = cs.A;
-          sh.sB[i] = cs.Bv;
-          sh.sUn[i] = cs.n_unc;
-#pragma unroll
-          for (int j = 0; j < kUncMax; ++j) sh.sUi[i][j] = cs.unc[j];
-        }
-      };
-      if (R.mode == kModeResidual)
-        wave_sweep<DT, kModeResidual, 1>(R, c0, c1, NW, a.nch, sh.d.tab, lsq, lsp, emit);
-      else
-        wave_sweep<DT, kModeBonus, 1>(R, c0, c1, NW, a.nch, sh.d.tab, lsq, lsp, emit);
-      const double Sq = block_sum<BLOCK>(lsq, sh.d.red);  // its barriers also order the LDS above
-      const double Sp = block_sum<BLOCK>(lsp, sh.d.red);
-      if (tid < c1 - cb) {
-        const int64_t c = base + cb + tid;
-        st<true>(&a.A[c], sh.sA[tid]);
-        st<true>(&a.Bv[c], sh.sB[tid]);
-        st<true>(&a.unc_n[c], sh.sUn[tid]);
-#pragma unroll
-        for (int j = 0; j < kUncMax; ++j) st<true>(&a.unc_idx[c * kUncMax + j], sh.sUi[tid][j]);
-      }
-      if (tid == 0) {
-        st<true>(&a.sq_part[static_cast<int64_t>(b) * a.S + sl], Sq);
-        st<true>(&a.sp_part[static_cast<int64_t>(b) * a.S + sl], Sp);
-      }
-    }
-    store_complete();
-    __syncthreads();
-    if (tid == 0) sh.flag = atomic_add_dev(&a.slices_done[b], 1u);
-    __syncthreads();
-    if (uniform(sh.flag) != static_cast<unsigned>(a.S - 1)) continue;
-
-    // ------------------------------------------- last slice of b: final draw
-    int tok = -1;
-    if (rows_valid) {
-      const double u = a.uni[static_cast<int64_t>(b) * K1 + K];
-      // exact normalisers: the slices' parts, summed by the whole block
-      const Src<true, double> sqp(a.sq_part + static_cast<int64_t>(b) * a.S, a.S);
-      const Src<true, double> spp(a.sp_part + static_cast<int64_t>(b) * a.S, a.S);
-      double lq = 0.0, lp = 0.0;
-      for (int i = tid; i < a.S; i += BLOCK) {
-        lq = lq + sqp[i];
-        lp = lp + spp[i];
-      }
-      if (tid == 0) sh.d.sel[3] = 0;
-      const double Sq = block_sum<BLOCK>(lq, sh.d.red);  // its barriers order the clear
-      const double Sp = block_sum<BLOCK>(lp, sh.d.red);
-      tok = fast_finish<BLOCK, DT, true>(
-          R, a.nch, Sq, Sp, Src<true, double>(a.A + base, a.nch),
-          Src<true, double>(a.Bv + base, a.nch), Src<true, int>(a.unc_n + base, a.nch),
-          Src<true, int>(a.unc_idx + base * kUncMax, static_cast<int64_t>(a.nch) * kUncMax), wbuf,
-          u, sh.d);
-      if (tok == -3) {  // residual without mass: the bonus draw from q_n
-        DrawRows Rb = R;
-        Rb.mode = kModeBonus;
-        tok = slow_draw<BLOCK, DT>(Rb, a.nch, wbuf, u, sh.d);
-      } else if (tok == -2) {
-        tok = slow_draw<BLOCK, DT>(R, a.nch, wbuf, u, sh.d, true, Sq, Sp);
-      }
-    }
-    if (tid == 0) {
-      if (n >= 0 && n <= K) a.out_tokens[static_cast<int64_t>(b) * K1 + n] = tok;
-      if (a.num_emitted) a.num_emitted[b] = (tok >= 0) ? n + 1 : 0;
-      atomic_store_dev(&a.slices_done[b], 0u);
-      atomic_store_dev(&a.ready[b], 0u);
-    }
-  }
-
-  // Last workgroup out resets the item counters for the next launch.
-  if (tid == 0) {
-    const unsigned done = atomic_add_dev(&a.ctl[kCtlExit], 1u);
-    if (done == gridDim.x - 1) {
-      atomic_store_dev(&a.ctl[kCtlItem], 0u);
-      atomic_store_dev(&a.ctl[kCtlExit], 0u);
     }
   }
 }

@@ -19,12 +19,12 @@ MAX_FLAGGED_FRACTION = 1e-4
 PROB_RTOL = 1e-5
 
 
-PATHS = ("three_call", "two_call", "fused")
+PATHS = ("three_call", "two_call", "step")
 
 
 def gpu_verify(inp: dict, stream=None, path: str = "three_call", workspace=None) -> dict:
     """Run the HIP verify through the C ABI: the three calls, the two calls
-    (stats, then spec_verify_sample), or the fused call (with a fresh zeroed
+    (stats, then spec_verify_sample), or spec_verify_step (with a fresh zeroed
     workspace unless one is given)."""
     import torch
     from speculative_sampling_verification_softmax_amd import binding
@@ -34,20 +34,17 @@ def gpu_verify(inp: dict, stream=None, path: str = "three_call", workspace=None)
     elif path == "two_call":
         out = binding.verify_two_call(inp["target"], inp["draft"], inp["tokens"],
                                       inp["uniforms"], inp["T"], stream=stream)
-    elif path == "fused":
+    elif path == "step":
         B, K1, V = inp["target"].shape
         if workspace is None:
             workspace = binding.new_workspace(B, K1 - 1, V, inp["target"].dtype,
                                               inp["target"].device)
-        out = binding.verify_fused(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
-                                   inp["T"], workspace, stream=stream)
+        out = binding.verify_step(inp["target"], inp["draft"], inp["tokens"], inp["uniforms"],
+                                  inp["T"], workspace, stream=stream)
     else:
         raise ValueError(path)
     torch.cuda.synchronize()
-    res = {k: v.cpu().numpy() for k, v in out.items()}
-    if path == "fused":
-        assert binding.workspace_error(workspace) == 0, "a wait inside the fused kernel gave up"
-    return res
+    return {k: v.cpu().numpy() for k, v in out.items()}
 
 
 def oracle_verify(host: dict, seqs=None, nthreads: int = 0) -> dict:

@@ -44,6 +44,7 @@ def test_header_constants_match_binding():
     assert int(consts["SPEC_DTYPE_BF16"]) == binding.SPEC_DTYPE_BF16
     assert int(consts["SPEC_MAX_K"]) == binding.SPEC_MAX_K
     assert eval(consts["SPEC_MAX_V"]) == binding.SPEC_MAX_V
+    assert int(consts["SPEC_MAX_ROWS"]) == binding.SPEC_MAX_ROWS == (2**32 - 1) // 1024
 
 
 def test_status_strings():
@@ -112,20 +113,28 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
 def test_workspace_size_host_only():
     L = _lib()
-    L.spec_verify_workspace_size.restype = ctypes.c_size_t
-    n = L.spec_verify_workspace_size(256, 8, 128256, 1)
-    assert 1 << 20 < n < 8 << 20 and n % 256 == 0
-    assert L.spec_verify_workspace_size(256, 8, 128256, 0) > n  # fp32 chunks are shorter
-    assert L.spec_verify_workspace_size(0, 8, 100, 1) == 0
-    assert L.spec_verify_workspace_size(1, 0, 100, 1) == 0
-    assert L.spec_verify_workspace_size(1, 1, 100, 7) == 0
+    L.spec_verify_step_workspace_size.restype = ctypes.c_size_t
+    size = lambda *a: L.spec_verify_step_workspace_size(*a)
+    # from 32 sequences on, one workgroup per sequence: the counters only
+    assert size(256, 8, 128256, 1) == 1024
+    assert size(32, 4, 32000, 1) == 256
+    # fewer sequences split the draw: one record of 160 bytes per sweep item of
+    # 1024 bf16 / 512 fp32 tokens and sequence, after the counters
+    assert size(1, 4, 32000, 0) == 256 + (63 * 160 + 255) // 256 * 256
+    assert size(31, 4, 32000, 1) == 256 + 31 * 32 * 160
+    assert size(16, 4, 32000, 0) > size(16, 4, 32000, 1)  # fp32 items hold fewer tokens
+    assert size(0, 8, 100, 1) == 0
+    assert size(1, 0, 100, 1) == 0
+    assert size(1, 1, 100, 7) == 0
+    assert size(1, 65, 100, 1) == 0
+    assert size(4194303, 1, 100, 1) == 0  # 3 * B rows past one launch
 
 
 @pytest.mark.parametrize("case", ["null_ws", "small_ws", "misaligned_ws", "null_out", "bad_T"])
-def test_fused_rejects_bad_arguments(case):
+def test_step_rejects_bad_arguments(case):
     L = _lib()
-    L.spec_verify_workspace_size.restype = ctypes.c_size_t
-    need = L.spec_verify_workspace_size(2, 3, 100, 1)
+    L.spec_verify_step_workspace_size.restype = ctypes.c_size_t
+    need = L.spec_verify_step_workspace_size(2, 3, 100, 1)
     ws, nbytes, out, T = P * 256, need, P, 1.0
     if case == "null_ws":
         ws = None
@@ -137,9 +146,27 @@ def test_fused_rejects_bad_arguments(case):
         out = None
     elif case == "bad_T":
         T = -1.0
-    rc = L.spec_verify_fused(P, P, 1, P, P, 2, 3, 100, T, P, P, P, out, None, None, ws,
-                             ctypes.c_size_t(nbytes), None)
+    rc = L.spec_verify_step(P, P, 1, P, P, 2, 3, 100, T, P, P, P, out, None, None, ws,
+                            ctypes.c_size_t(nbytes), None)
     assert rc == 1
+
+
+@pytest.mark.parametrize("fn", ["stats", "verify_sample", "sample", "filter"])
+def test_launch_size_limit(fn):
+    """Shapes whose launch would exceed 2^32 - 1 threads are argument errors,
+    reported before anything is enqueued."""
+    L = _lib()
+    if fn == "stats":  # 2K+1 = 3 rows per sequence
+        assert L.spec_softmax_stats(P, P, 1, 1398102, 1, 4, ctypes.c_float(1.0), P, P, None) == 1
+        assert L.spec_softmax_stats(P, P, 1, 4194304, 1, 4, ctypes.c_float(1.0), P, P, None) == 1
+    elif fn == "verify_sample":
+        assert L.spec_verify_sample(P, P, 1, P, P, P, P, 1398102, 1, 4, ctypes.c_float(1.0), P, P,
+                                    None, None, None) == 1
+    elif fn == "sample":
+        assert L.spec_sample(P, 1, 4194304, 4, ctypes.c_float(1.0), P, P, P, None) == 1
+    else:
+        assert L.spec_filter(P, 1, 4194304, 4, ctypes.c_float(1.0), 2, ctypes.c_float(1.0), P,
+                             None, None, None) == 1
 
 
 @pytest.mark.parametrize("case", ["tgt", "tok", "am", "nacc", "out", "dtype", "K", "misaligned"])

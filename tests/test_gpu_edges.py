@@ -270,8 +270,8 @@ BOUNDARY_BF16 = [0x3C00, 0xBC00,   # +-2^-7: the first codes the residual kernel
 def test_bf16_table_boundary_codes(T):
     """bf16 rows made of the codes at and around the edges of the draw
     kernels' exponential table (2^-7 <= |z| < 2^6), -inf, zeros and
-    denormals: the three-call path (tabulated), the fused path (computed)
-    and the draft sampler all against the oracle.  The low temperatures put
+    denormals: every verify path (one-workgroup draws with the tables, the
+    step's split draw) and the draft sampler against the oracle.  The low temperatures put
     most table entries at or near 0 and the top codes' entries far apart."""
     rng = np.random.default_rng(int(T))
     B, K, V = 64, 3, 700
