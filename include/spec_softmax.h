@@ -70,6 +70,7 @@ extern "C" {
 #define SPEC_MAX_K 64
 #define SPEC_MAX_V (1 << 20)
 #define SPEC_MAX_ROWS 4194303 /* (2^32 - 1) / 1024 */
+#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20) /* spec_verify_step_noalloc's scratch */
 
 /*
  * spec_softmax_stats -- temperature softmax statistics of every row.
@@ -261,6 +262,34 @@ int spec_verify_step(const void* target_logits, const void* draft_logits, int dt
                      int32_t* num_accepted, int32_t* out_tokens, float* probs,
                      int32_t* num_emitted, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * spec_verify_step_noalloc -- spec_verify_step for callers that cannot
+ * allocate or pass device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments minus the
+ * workspace, same launches and the same bits; the workspace is instead a
+ * file-scope device array of SPEC_NOALLOC_SCRATCH_BYTES (8 MiB) inside the
+ * library, of which each GPU the library runs on holds its own copy until the
+ * process ends.  No hipMalloc, hipFree or allocating routine is called.
+ *   - The first call on a device looks the array up and clears it with one
+ *     fill kernel on `stream`, ahead of its own launches.
+ *   - Every call on a GPU shares that GPU's array (each completed call leaves
+ *     its counters zero for the next): calls that overlap on one GPU, on
+ *     different streams or from different threads, race and must not be
+ *     issued.
+ *   - A shape whose spec_verify_step_workspace_size exceeds the array returns
+ *     SPEC_ERR_UNSUPPORTED with nothing enqueued (only batches under 32
+ *     sequences use it: up to 31 sequences of about 800K fp32 or all bf16
+ *     vocabularies up to SPEC_MAX_V fit).
+ * Returns SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED or
+ * SPEC_ERR_LAUNCH (also if the array cannot be looked up).
+ */
+int spec_verify_step_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* uniforms,
+                             int B, int K, int V, float temperature,
+                             float* target_stats, float* draft_stats,
+                             int32_t* num_accepted, int32_t* out_tokens, float* probs,
+                             int32_t* num_emitted, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* spec_status_string(int status);

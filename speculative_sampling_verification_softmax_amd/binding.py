@@ -23,10 +23,12 @@ SPEC_OK = 0
 SPEC_MAX_K = 64
 SPEC_MAX_V = 1 << 20
 SPEC_MAX_ROWS = 4194303
+SPEC_NOALLOC_SCRATCH_BYTES = 8 << 20
+SPEC_ERR_UNSUPPORTED = 2
 
 EXPORTS = ("spec_softmax_stats", "spec_verify", "spec_residual_sample", "spec_status_string",
-           "spec_verify_step_workspace_size", "spec_verify_step", "spec_greedy_verify",
-           "spec_sample", "spec_filter", "spec_verify_sample")
+           "spec_verify_step_workspace_size", "spec_verify_step", "spec_verify_step_noalloc",
+           "spec_greedy_verify", "spec_sample", "spec_filter", "spec_verify_sample")
 
 _lib = None
 
@@ -57,6 +59,9 @@ def load(path: str = LIB_PATH):
     L.spec_verify_step.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                    vp, vp, ctypes.c_size_t, vp]
     L.spec_verify_step.restype = i32
+    L.spec_verify_step_noalloc.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, f32, vp, vp, vp,
+                                           vp, vp, vp, vp]
+    L.spec_verify_step_noalloc.restype = i32
     L.spec_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp]
     L.spec_greedy_verify.restype = i32
     L.spec_sample.argtypes = [vp, i32, i32, i32, f32, vp, vp, vp, vp]
@@ -294,6 +299,29 @@ def verify_step(target, draft, tokens, uniforms, T: float, workspace: torch.Tens
         None if ne is None else _dev(ne, "num_emitted", torch.int32, (B,)),
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream))
     _check(rc, "spec_verify_step")
+    return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=pr,
+                num_emitted=ne)
+
+
+def verify_step_noalloc(target, draft, tokens, uniforms, T: float, target_stats=None,
+                        draft_stats=None, num_accepted=None, out_tokens=None, probs=True,
+                        num_emitted=True, stream=None) -> dict:
+    """spec_verify_step_noalloc: spec_verify_step on the library's own static
+    scratch (no workspace; calls that overlap on one GPU race)."""
+    B, K, V = _shapes(target, draft)
+    ts, ds, n, out, pr, ne = _step_outputs(B, K, target.device, target_stats, draft_stats,
+                                           num_accepted, out_tokens, probs, num_emitted)
+    rc = load().spec_verify_step_noalloc(
+        _dev(target, "target"), _dev(draft, "draft"), _dtype_code(target),
+        _dev(tokens, "tokens", torch.int32, (B, K)),
+        _dev(uniforms, "uniforms", torch.float32, (B, K + 1)), B, K, V, float(T),
+        _dev(ts, "target_stats", torch.float32, (B, K + 1, 2)),
+        _dev(ds, "draft_stats", torch.float32, (B, K, 2)),
+        _dev(n, "num_accepted", torch.int32, (B,)),
+        _dev(out, "out_tokens", torch.int32, (B, K + 1)),
+        None if pr is None else _dev(pr, "probs", torch.float32, (B, K, 2)),
+        None if ne is None else _dev(ne, "num_emitted", torch.int32, (B,)), _stream(stream))
+    _check(rc, "spec_verify_step_noalloc")
     return dict(target_stats=ts, draft_stats=ds, num_accepted=n, out_tokens=out, probs=pr,
                 num_emitted=ne)
 

@@ -154,6 +154,47 @@ int launched() {
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 
+// ------------------------------------------------- no-allocation scratch
+// The device memory of spec_verify_step_noalloc: one file-scope array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends.  In host code the name `scratch` stands for the symbol only; the
+// copy's device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is ever used (kernel arguments,
+// the clearing below).
+constexpr size_t kScratchBytes = SPEC_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(1024) void zero_scratch_kernel(uint4* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's scratch address, set up by the first call on the device:
+// the symbol's address, then the whole array cleared by a fill kernel on
+// the caller's stream, ahead of the call's own kernels (the counters must
+// start at zero; every completed call leaves them zero again).  nullptr on
+// failure.
+void* scratch_for_current_device(hipStream_t s) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(zero_scratch_kernel, dim3(256), dim3(1024), 0, s, static_cast<uint4*>(p),
+                       kScratchBytes / sizeof(uint4));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
 // The two launches of spec_verify_step on an already checked call: row
 // stats, then the accept scan and final draw (split over Pd workgroups per
 // sequence when there are few sequences), with the counters and records in
@@ -468,6 +509,29 @@ int spec_verify_step(const void* target_logits, const void* draft_logits, int dt
                      temperature, target_stats, draft_stats, num_accepted, out_tokens, probs,
                      num_emitted, static_cast<char*>(workspace), L,
                      static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_step_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                             const int32_t* draft_tokens, const float* uniforms, int B, int K,
+                             int V, float temperature, float* target_stats, float* draft_stats,
+                             int32_t* num_accepted, int32_t* out_tokens, float* probs,
+                             int32_t* num_emitted, void* stream) {
+  int rc = check_verify(target_logits, draft_logits, dtype, B, K, V, temperature);
+  if (rc != SPEC_OK) return rc;
+  if (!draft_tokens || !uniforms || !target_stats || !draft_stats || !num_accepted || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (!aligned(draft_tokens, 4) || !aligned(uniforms, 4) || !aligned(target_stats, 4) ||
+      !aligned(draft_stats, 4) || !aligned(num_accepted, 4) || !aligned(out_tokens, 4) ||
+      !aligned(probs, 4) || !aligned(num_emitted, 4))
+    return SPEC_ERR_INVALID_ARG;
+  const StepLayout L = step_layout(B, K, V, dtype);
+  if (L.total > kScratchBytes) return SPEC_ERR_UNSUPPORTED;  // past the static scratch
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = scratch_for_current_device(s);
+  if (ws == nullptr) return SPEC_ERR_LAUNCH;
+  return launch_step(target_logits, draft_logits, dtype, draft_tokens, uniforms, B, K, V,
+                     temperature, target_stats, draft_stats, num_accepted, out_tokens, probs,
+                     num_emitted, static_cast<char*>(ws), L, s);
 }
 
 }  // extern "C"

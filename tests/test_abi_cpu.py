@@ -151,6 +151,29 @@ def test_step_rejects_bad_arguments(case):
     assert rc == 1
 
 
+@pytest.mark.parametrize("case", ["too_big", "null_tok", "bad_K", "misaligned"])
+def test_noalloc_rejects_before_touching_the_device(case):
+    """spec_verify_step_noalloc checks its arguments, then whether the shape's
+    workspace fits its static scratch, before it looks the scratch up or
+    launches anything."""
+    L = _lib()
+    B, K, V, dtype, tok, ne = 2, 3, 100, 1, P, None
+    if case == "too_big":  # 31 sequences of 2^20 fp32 tokens: 10 MB of item records
+        B, K, V, dtype = 31, 1, 1 << 20, 0
+    elif case == "null_tok":
+        tok = None
+    elif case == "bad_K":
+        K = 65
+    else:
+        ne = P + 2
+    rc = L.spec_verify_step_noalloc(P, P, dtype, tok, P, B, K, V, ctypes.c_float(1.0), P, P, P, P,
+                                    None, ne, None)
+    assert rc == (2 if case == "too_big" else 1)
+    L.spec_verify_step_workspace_size.restype = ctypes.c_size_t
+    if case == "too_big":
+        assert L.spec_verify_step_workspace_size(B, K, V, dtype) > binding.SPEC_NOALLOC_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("fn", ["stats", "verify_sample", "sample", "filter"])
 def test_launch_size_limit(fn):
     """Shapes whose launch would exceed 2^32 - 1 threads are argument errors,
