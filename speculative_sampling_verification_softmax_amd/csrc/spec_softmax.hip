@@ -154,6 +154,24 @@ int launched() {
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 
+// The row-stats launch every verify path uses (so that all of them get the
+// same bits): one workgroup per row; 1024 threads, two workgroups per CU, or
+// 512 threads when the rows number between 512 and 1024, so that they all
+// run in one round of the device's 256 CUs (four per CU) instead of two
+// rounds of latency-bound rows.
+template <int DT>
+void launch_stats_dt(const void* tgt, const void* dft, int64_t n_tgt, int64_t rows, int V, float c2,
+                     float* tstats, float* dstats, hipStream_t s) {
+  constexpr int VPG = DT == kBF16 ? SPEC_STATS_VPG_BF16 : SPEC_STATS_VPG_F32;
+  const dim3 grid(static_cast<unsigned>(rows));
+  if (rows > 512 && rows <= 1024)
+    hipLaunchKernelGGL((spec::stats_kernel<512, DT, VPG>), grid, dim3(512), 0, s, tgt, dft, n_tgt,
+                       V, c2, tstats, dstats);
+  else
+    hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, DT, VPG>), grid, dim3(kStatsBlock), 0, s,
+                       tgt, dft, n_tgt, V, c2, tstats, dstats);
+}
+
 // ------------------------------------------------- no-allocation scratch
 // The device memory of spec_verify_step_noalloc: one file-scope array, of
 // which every GPU the library runs on holds its own copy until the process
@@ -204,15 +222,13 @@ int launch_step_dt(const void* tgt, const void* dft, const int32_t* tokens, cons
                    int B, int K, int V, float T, float* tstats, float* dstats, int32_t* nacc,
                    int32_t* out, float* probs, int32_t* nemit, char* ws, const StepLayout& L,
                    hipStream_t s) {
-  constexpr int VPG = DT == kBF16 ? SPEC_STATS_VPG_BF16 : SPEC_STATS_VPG_F32;
   const int64_t n_tgt = static_cast<int64_t>(B) * (K + 1);
   const int64_t rows = n_tgt + static_cast<int64_t>(B) * K;
   const double invT = 1.0 / static_cast<double>(T);
   const double yscale = invT * spec::Exp64::kScale;
   const float c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(T));
   (void)hipGetLastError();
-  hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, DT, VPG>), dim3(static_cast<unsigned>(rows)),
-                     dim3(kStatsBlock), 0, s, tgt, dft, n_tgt, V, c2, tstats, dstats);
+  launch_stats_dt<DT>(tgt, dft, n_tgt, rows, V, c2, tstats, dstats, s);
   int rc = launched();
   if (rc != SPEC_OK) return rc;
   if (L.Pd > 1) {
@@ -287,14 +303,12 @@ int spec_softmax_stats(const void* target_logits, const void* draft_logits, int 
   const int64_t rows = n_tgt + static_cast<int64_t>(B) * K;
   const float c2 = static_cast<float>(1.4426950408889634074 / static_cast<double>(temperature));
   (void)hipGetLastError();
-  const dim3 grid(static_cast<unsigned>(rows)), block(kStatsBlock);
-  if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), grid, block, 0, s,
-                       target_logits, draft_logits, n_tgt, V, c2, target_stats, draft_stats);
-  } else {
-    hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>), grid, block, 0, s,
-                       target_logits, draft_logits, n_tgt, V, c2, target_stats, draft_stats);
-  }
+  if (dtype == SPEC_DTYPE_BF16)
+    launch_stats_dt<kBF16>(target_logits, draft_logits, n_tgt, rows, V, c2, target_stats,
+                           draft_stats, s);
+  else
+    launch_stats_dt<kF32>(target_logits, draft_logits, n_tgt, rows, V, c2, target_stats,
+                          draft_stats, s);
   return launched();
 }
 
