@@ -137,10 +137,12 @@ def _pmc_kernels(path: str) -> dict:
     return out
 
 
-def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
+def pmc_summary(d: str, path: str, workload: str, command: str, mode: str = "verify",
+                top_k: int = 50, top_p: float = 0.9) -> str:
     f = lambda sub: _pmc_kernels(os.path.join(d, sub, "run_counter_collection.csv"))
-    # pass directories: fetch, write (the stats kernel, any path)
-    suffix = ""
+    # pass directories: fetch, write (the stats kernel of the verify step), or
+    # fetch_filter, write_filter (--mode filter); fetch_copy, write_copy
+    suffix = "_filter" if mode == "filter" else ""
     fetch, write = f("fetch" + suffix), f("write" + suffix)
     copy_bytes = COPY_MIB << 20
     def calib(sub):  # mean counter of the calibration copies (torch's own copies are far smaller)
@@ -151,8 +153,16 @@ def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
     kf = copy_bytes / (cf * 1024)
     kw = copy_bytes / (cw * 1024)
     wl = synth.WORKLOADS[workload]
-    dom = "stats_kernel"
-    alg = stats_bytes(wl)
+    if mode == "filter":
+        dom = "filter_kernel"
+        rows = wl.B * (2 * wl.K + 1)
+        alg_total = 2 * rows * wl.V * wl.elt + rows * 4  # both calls: target and draft rows
+        # one launch filters the target rows, the other the draft rows
+        alg = alg_total  # reported per step (two launches); per launch below
+        path = f"filter (top-k {top_k}, top-p {top_p}, rows written)"
+    else:
+        dom = "stats_kernel"
+        alg = stats_bytes(wl)
     lines = [f"# HBM traffic per launch: {path} path, {workload} workload "
              f"(B={wl.B}, K={wl.K}, V={wl.V}, {wl.dtype}, T={wl.T})", "",
              "Commands (one MI355X, from the repository root; each pass is a run of its own):", "",
@@ -172,12 +182,17 @@ def pmc_summary(d: str, path: str, workload: str, command: str) -> str:
         rb, wb = fa * 1024 * kf, wa * 1024 * kw
         lines.append(f"| `{k}` | {len(fetch[k])} | {fa:.1f} | {wa:.1f} | {rb:.4g} | {wb:.4g} |")
         if dom in k:
-            rec = rb + wb
-    lines += ["", f"Algorithmic bytes of one `{dom}` launch: {alg}."]
+            if mode == "filter":  # per step: the target and the draft launch
+                rec = sum(fetch[k]) * 1024 * kf / len(fetch[k]) * 2 + \
+                    sum(write.get(k, [0.0])) * 1024 * kw / max(len(write.get(k, [0.0])), 1) * 2
+            else:
+                rec = rb + wb
+    what = "step (two launches)" if mode == "filter" else "launch"
+    lines += ["", f"Algorithmic bytes of one `{dom}` {what}: {alg}."]
     if rec is not None:
-        lines += [f"Measured HBM bytes per launch: {rec:.6g} ({rec / alg:.4f} of algorithmic).", "",
-                  f"traffic-record: kernel={dom} workload={workload} sources={kernel_sources_hash()} "
-                  f"bytes={rec:.0f}"]
+        lines += [f"Measured HBM bytes per {what}: {rec:.6g} ({rec / alg:.4f} of algorithmic).",
+                  "", f"traffic-record: kernel={dom} workload={workload} "
+                  f"sources={kernel_sources_hash()} bytes={rec:.0f}"]
     return "\n".join(lines) + "\n"
 
 
@@ -611,7 +626,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.pmc_summary:
-        print(pmc_summary(args.pmc_summary, args.path, args.workload, args.command), end="")
+        print(pmc_summary(args.pmc_summary, args.path, args.workload, args.command, args.mode,
+                          args.top_k, args.top_p), end="")
         return 0
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.command), end="")

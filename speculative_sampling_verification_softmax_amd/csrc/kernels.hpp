@@ -1356,9 +1356,9 @@ struct GlobalItems {
 };
 
 // The exact normalisers S_q, S_p of a finished fast sweep, to every thread:
-// wave 0 adds the items' parts, item c in lane c % 64 in item order, then a
-// butterfly -- the same order whatever the block size and however many
-// workgroups swept.  Contains a barrier.
+// wave 0 adds the items' parts, item c in lane c % 64 in item order, then
+// the lanes in wave_sum_rows' fixed order -- the same order whatever the
+// block size and however many workgroups swept.  Contains a barrier.
 template <int BLOCK, typename Items>
 __device__ __forceinline__ void item_normalisers(const Items& it, int ni, DrawShared<BLOCK>& sh,
                                                  double& Sq, double& Sp) {
@@ -1368,8 +1368,8 @@ __device__ __forceinline__ void item_normalisers(const Items& it, int ni, DrawSh
       lq = lq + it.lq(c);
       lp = lp + it.lp(c);
     }
-    lq = wave_sum(lq);
-    lp = wave_sum(lp);
+    lq = wave_sum_rows(lq);  // DPP row scans and four lane reads, no LDS round trips
+    lp = wave_sum_rows(lp);
     if (threadIdx.x == 0) {
       sh.norm[0] = lq;
       sh.norm[1] = lp;
@@ -2031,6 +2031,12 @@ __global__ __launch_bounds__(kWave) void greedy_scan_kernel(const int32_t* __res
 // of fp32 exp2 terms each below 2^-16, rounded once to the same units.
 
 constexpr int kFilterCap = 12288;
+constexpr int kFilterMapVecs = 16384;  // 256 KB rows: bf16 up to 131072 tokens
+// The 16-bit vector keys of the top-k first pass share the candidate array:
+// they fill its last kFilterMapVecs / 2 floats, clear of the per-thread
+// maxima the top-k window select keeps at its start.
+constexpr int kFilterKeyOff = kFilterCap - kFilterMapVecs / 2;
+static_assert(kFilterKeyOff >= 1024, "room for the per-thread maxima of a 1024-thread block");
 constexpr float kFilterWindow = 16.0f;
 constexpr double kMassScale = 4398046511104.0;  // 2^42: V * 2^42 < 2^63 for V <= 2^20
 
@@ -2081,24 +2087,25 @@ __device__ __forceinline__ void for_each_value(const char* row, int V, F f) {
   if (tid < V - G.tail0) f(logit_f32<DT>(row, G.tail0 + tid));
 }
 
-// g(x) over a row in groups: x is a float array (one value for the head and
-// tail elements, VPG vectors for the body); every thread makes the same calls
-// and entries past the row are -inf.
-template <int BLOCK, int DT, int VPG, typename G>
+// g(x, i0) over a row in groups: x is a float array (one value for the head
+// and tail elements, with i0 = -1; VPG vectors for the body, the thread's
+// vectors i0 + u*BLOCK); every thread makes the same calls and entries past
+// the row are -inf.  AUX: the body loads' cache policy (stream_body).
+template <int BLOCK, int DT, int VPG, int AUX = kLoadDefault, typename G>
 __device__ __forceinline__ void for_each_group(const char* row, int V, G g) {
   constexpr int EPV = 16 / Elt<DT>::bytes;
   const int tid = threadIdx.x;
   const RowGeom<DT> Gm(row, V);
   {
     const float x[1] = {tid < Gm.head ? logit_f32<DT>(row, tid) : -__builtin_huge_valf()};
-    g(x);
+    g(x, -1);
   }
-  stream_body<BLOCK, DT, VPG>(row + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes, Gm.nvec,
-                              [&](const float(&x)[VPG * EPV], int) { g(x); });
+  stream_body<BLOCK, DT, VPG, AUX>(row + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes, Gm.nvec,
+                                   [&](const float(&x)[VPG * EPV], int i0) { g(x, i0); });
   {
     const float x[1] = {tid < V - Gm.tail0 ? logit_f32<DT>(row, Gm.tail0 + tid)
                                            : -__builtin_huge_valf()};
-    g(x);
+    g(x, -1);
   }
 }
 
@@ -2174,6 +2181,9 @@ struct FilterShared {
   double sel_need;
   unsigned ncand;
   float cand[kFilterCap];
+  // one bit per 16-byte vector of the row body that holds a window value
+  // (rows of at most kFilterMapVecs vectors)
+  unsigned vmap[kFilterMapVecs / 32];
 };
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
@@ -2330,6 +2340,54 @@ __device__ __forceinline__ double finish_row(const char* row, char* orow, int V,
   return acc;
 }
 
+// The output row of a cut settled in LDS (input and output rows sharing their
+// offset within 16 bytes): each body vector marked in vmap is read and cut
+// (tokens below thr become -inf), every other body vector is written as
+// -inf without being read; the head and tail elements are read and cut.
+template <int BLOCK, int DT>
+__device__ __forceinline__ void write_marked_row(const char* row, char* orow, int V, float thr,
+                                                 const unsigned* vmap) {
+  using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
+  constexpr Bits kNegInf = DT == kBF16 ? Bits(0xFF80u) : Bits(0xFF800000u);
+  constexpr uint32_t kNegInfWord = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+  constexpr int EB = Elt<DT>::bytes;
+  const int tid = threadIdx.x;
+  const Bits* src = reinterpret_cast<const Bits*>(row);
+  Bits* dst = reinterpret_cast<Bits*>(orow);
+  auto one = [&](Bits b) -> Bits {
+    const float z = DT == kBF16 ? __uint_as_float(static_cast<uint32_t>(b) << 16)
+                                : __uint_as_float(static_cast<uint32_t>(b));
+    return z < thr ? kNegInf : b;
+  };
+  auto word = [&](uint32_t w) -> uint32_t {
+    if constexpr (DT == kBF16) {
+      return static_cast<uint32_t>(one(static_cast<Bits>(w & 0xFFFFu))) |
+             (static_cast<uint32_t>(one(static_cast<Bits>(w >> 16))) << 16);
+    } else {
+      return one(w);
+    }
+  };
+  const RowGeom<DT> G(row, V);
+  if (tid < G.head) dst[tid] = one(src[tid]);
+  if (tid < V - G.tail0) dst[G.tail0 + tid] = one(src[G.tail0 + tid]);
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u* vs = reinterpret_cast<const v4u*>(row + static_cast<int64_t>(G.head) * EB);
+  v4u* vd = reinterpret_cast<v4u*>(orow + static_cast<int64_t>(G.head) * EB);
+  v4u ninf;
+  ninf.x = ninf.y = ninf.z = ninf.w = kNegInfWord;
+  for (int i = tid; i < G.nvec; i += BLOCK) {
+    v4u o = ninf;
+    if ((vmap[i >> 5] >> (i & 31)) & 1u) {
+      const v4u v = vs[i];
+      o.x = word(v.x);
+      o.y = word(v.y);
+      o.z = word(v.z);
+      o.w = word(v.w);
+    }
+    __builtin_nontemporal_store(o, &vd[i]);
+  }
+}
+
 template <int BLOCK, int DT, int VPG>
 __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out, int V,
                                                        float c2, double yscale, int top_k,
@@ -2338,19 +2396,65 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   constexpr int NW = BLOCK / kWave;
   __shared__ FilterShared<BLOCK> sh;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  constexpr int EPV = 16 / Elt<DT>::bytes;
   const int64_t r = blockIdx.x;
   const char* row = static_cast<const char*>(in) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+  // whether the window pass can mark the body vectors that hold its values
+  const bool map_ok = RowGeom<DT>(row, V).nvec <= kFilterMapVecs;
   fill_exp2_table(sh.tab);
   if (tid == 0) sh.ncand = 0u;
+
+  const bool use_k = top_k > 0, use_p = top_p < 1.0f;
+  // Top-k with k <= BLOCK: the window needs only the row's largest values, so
+  // the first pass also keeps each body vector's largest key (its top 16
+  // bits) in LDS, and the window pass reads just the vectors whose key
+  // reaches the window.  Otherwise the window pass reads the whole row again.
+  const bool skip = use_k && top_k <= BLOCK && map_ok;
+  constexpr int KS = DT == kF32 ? 16 : 0;  // key bits dropped
+  unsigned short* vkey = reinterpret_cast<unsigned short*>(sh.cand + kFilterKeyOff);
+  const RowGeom<DT> Gm(row, V);
 
   // max, min and NaN
   float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
   unsigned long long nanm = 0;
-  for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
-    mx = fmaxf(mx, x);
-    mn = fminf(mn, x);
-    nanm |= __ballot(x != x);
-  });
+  if (skip) {
+    // streamed once (non-temporal); padding entries are -inf and enter
+    // neither the minimum nor the keys
+    for_each_group<BLOCK, DT, VPG, kLoadStream>(row, V, [&](const auto& x, int i0) {
+      constexpr int N = sizeof(x) / sizeof(float);
+      if (N == 1) {  // a head or tail element (its minimum is taken below)
+        mx = fmaxf(mx, x[0]);
+        nanm |= __ballot(x[0] != x[0]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < N / EPV; ++u) {
+          float vm = x[u * EPV], vn = x[u * EPV];
+          bool nan = x[u * EPV] != x[u * EPV];
+#pragma unroll
+          for (int e = 1; e < EPV; ++e) {
+            vm = fmaxf(vm, x[u * EPV + e]);
+            vn = fminf(vn, x[u * EPV + e]);
+            nan = nan || x[u * EPV + e] != x[u * EPV + e];
+          }
+          nanm |= __ballot(nan);
+          mx = fmaxf(mx, vm);
+          const int vi = i0 + u * BLOCK;
+          if (vi < Gm.nvec) {
+            mn = fminf(mn, vn);
+            vkey[vi] = static_cast<unsigned short>(order_key<DT>(vm) >> KS);
+          }
+        }
+      }
+    });
+    if (tid < Gm.head) mn = fminf(mn, logit_f32<DT>(row, tid));
+    if (tid < V - Gm.tail0) mn = fminf(mn, logit_f32<DT>(row, Gm.tail0 + tid));
+  } else {
+    for_each_value<BLOCK, DT, VPG>(row, V, [&](float x) {
+      mx = fmaxf(mx, x);
+      mn = fminf(mn, x);
+      nanm |= __ballot(x != x);
+    });
+  }
   const float m = block_max<BLOCK>(mx, sh.redf);
   const float lo = -block_max<BLOCK>(-mn, sh.redf);
   if (lane == 0) sh.redu[wv] = nanm != 0ull ? 1u : 0u;
@@ -2358,7 +2462,6 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   bool bad = !__builtin_isfinite(m);
   for (int w = 0; w < NW; ++w) bad = bad || sh.redu[w] != 0u;
 
-  const bool use_k = top_k > 0, use_p = top_p < 1.0f;
   float zlo = m - kFilterWindow / c2;
   unsigned thr_key = 0;
   bool in_lds = false;  // the selects ran over the window's values in LDS
@@ -2375,37 +2478,116 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   }
   if (!bad && (use_k || use_p)) {
     // the window: values >= zlo go to LDS (one slot range per wave and
-    // group, taken with one LDS atomic); for the nucleus without top-k the
-    // fp32 mass below the window is summed on the way
+    // group, taken with one LDS atomic), and the body vectors that hold them
+    // are marked; for the nucleus without top-k the fp32 mass below the
+    // window is summed on the way
     const bool masses = use_p && !use_k;
     float rest = 0.0f;
-    for_each_group<BLOCK, DT, VPG>(row, V, [&](const auto& x) {
-      constexpr int N = sizeof(x) / sizeof(float);
-      unsigned c = 0u;
+    if (skip) {
+      // the map from the keys: bit t of word w marks body vector 32w + t when
+      // its key reaches zlo's (the dropped low key bits only widen the set,
+      // so every value >= zlo lies in a marked vector)
+      const unsigned zk = order_key<DT>(zlo) >> KS;
+      const int nw = (Gm.nvec + 31) >> 5;
+      constexpr int WPT = (kFilterMapVecs / 32 + BLOCK - 1) / BLOCK;  // map words per thread
+      unsigned bits[WPT];
 #pragma unroll
-      for (int e = 0; e < N; ++e) c += x[e] >= zlo ? 1u : 0u;
-      if (masses) {
+      for (int j = 0; j < WPT; ++j) {
+        const int w = tid + j * BLOCK;
+        unsigned b = 0u;
+        if (w < nw) {
+          const uint4* kv = reinterpret_cast<const uint4*>(vkey + 32 * w);
 #pragma unroll
-        for (int e = 0; e < N; ++e) {
-          const float t = __builtin_amdgcn_exp2f((x[e] - m) * c2);
-          rest += x[e] >= zlo ? 0.0f : t;
+          for (int q = 0; q < 4; ++q) {
+            const uint4 k4 = kv[q];
+            const unsigned kw[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+              const int t = 8 * q + h;
+              const unsigned key = (kw[h >> 1] >> (16 * (h & 1))) & 0xFFFFu;
+              b |= (32 * w + t < Gm.nvec && key >= zk) ? 1u << t : 0u;
+            }
+          }
+          sh.vmap[w] = b;
+        }
+        bits[j] = b;
+      }
+      __syncthreads();  // every key is read before candidates overwrite them
+      // values >= zlo of the head and tail elements and of the marked
+      // vectors, appended with one LDS atomic per element or vector
+      auto put = [&](const float* x, int nx) {
+        unsigned c = 0u;
+        for (int e = 0; e < nx; ++e) c += x[e] >= zlo ? 1u : 0u;
+        if (c != 0u) {
+          unsigned pos = atomicAdd(&sh.ncand, c);
+          for (int e = 0; e < nx; ++e)
+            if (x[e] >= zlo) {
+              if (pos < static_cast<unsigned>(kFilterCap)) sh.cand[pos] = x[e];
+              ++pos;
+            }
+        }
+      };
+      if (tid < Gm.head) {
+        const float x = logit_f32<DT>(row, tid);
+        put(&x, 1);
+      }
+      if (tid < V - Gm.tail0) {
+        const float x = logit_f32<DT>(row, Gm.tail0 + tid);
+        put(&x, 1);
+      }
+      const char* body = row + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        unsigned b = bits[j];
+        while (b != 0u) {
+          const int vi = 32 * (tid + j * BLOCK) + __builtin_ctz(b);
+          b &= b - 1u;
+          float xv[EPV];
+          unpack16<DT>(*reinterpret_cast<const uint4*>(body + static_cast<int64_t>(vi) * 16), xv);
+          put(xv, EPV);
         }
       }
-      if (__ballot(c != 0u) != 0ull) {
-        const unsigned incl = wave_incl_scan_u32(c);
-        const unsigned total =
-            static_cast<unsigned>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
-        unsigned base = 0u;
-        if (lane == 0) base = atomicAdd(&sh.ncand, total);
-        unsigned pos = uniform(base) + incl - c;
+    } else {
+      for (int i = tid; i < kFilterMapVecs / 32; i += BLOCK) sh.vmap[i] = 0u;
+      __syncthreads();
+      for_each_group<BLOCK, DT, VPG>(row, V, [&](const auto& x, int i0) {
+        constexpr int N = sizeof(x) / sizeof(float);
+        unsigned c = 0u;
 #pragma unroll
-        for (int e = 0; e < N; ++e)
-          if (x[e] >= zlo) {
-            if (pos < static_cast<unsigned>(kFilterCap)) sh.cand[pos] = x[e];
-            ++pos;
+        for (int e = 0; e < N; ++e) c += x[e] >= zlo ? 1u : 0u;
+        if (masses) {
+#pragma unroll
+          for (int e = 0; e < N; ++e) {
+            const float t = __builtin_amdgcn_exp2f((x[e] - m) * c2);
+            rest += x[e] >= zlo ? 0.0f : t;
           }
-      }
-    });
+        }
+        if (N > 1 && map_ok && c != 0u) {
+#pragma unroll
+          for (int u = 0; u < N / EPV; ++u) {
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) any = any || x[u * EPV + e] >= zlo;
+            const int vi = i0 + u * BLOCK;
+            if (any) atomicOr(&sh.vmap[vi >> 5], 1u << (vi & 31));
+          }
+        }
+        if (__ballot(c != 0u) != 0ull) {
+          const unsigned incl = wave_incl_scan_u32(c);
+          const unsigned total =
+              static_cast<unsigned>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
+          unsigned base = 0u;
+          if (lane == 0) base = atomicAdd(&sh.ncand, total);
+          unsigned pos = uniform(base) + incl - c;
+#pragma unroll
+          for (int e = 0; e < N; ++e)
+            if (x[e] >= zlo) {
+              if (pos < static_cast<unsigned>(kFilterCap)) sh.cand[pos] = x[e];
+              ++pos;
+            }
+        }
+      });
+    }
     const double rest_all = masses ? block_sum<BLOCK>(static_cast<double>(rest), sh.redd) : 0.0;
     __syncthreads();
     const unsigned n = sh.ncand;
@@ -2473,8 +2655,16 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   const bool s_lds = want && in_lds && cut;
   char* orow = write ? static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes
                      : nullptr;
+  // When the cut was settled in LDS, every kept token lies in the window, so
+  // a body vector that held no window value is all -inf in the output and
+  // need not be read again: only the marked vectors (and the head and tail
+  // elements) are.
+  const bool marked = write && in_lds && cut && map_ok &&
+                      ((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) == 0;
   double part = 0.0;
-  if (write && want && !s_lds) {
+  if (marked) {
+    write_marked_row<BLOCK, DT>(row, orow, V, thr, sh.vmap);
+  } else if (write && want && !s_lds) {
     part = finish_row<BLOCK, DT, true, true>(row, orow, V, cut, thr, m, c2);
   } else if (write) {
     (void)finish_row<BLOCK, DT, true, false>(row, orow, V, cut, thr, m, c2);

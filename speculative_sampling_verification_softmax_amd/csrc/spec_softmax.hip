@@ -28,6 +28,11 @@ using spec::kF32;
 #ifndef SPEC_FILTER_VPG_BF16
 #define SPEC_FILTER_VPG_BF16 4
 #endif
+// 512 threads: two filter workgroups share a CU, so one row's selects overlap
+// another row's streaming
+#ifndef SPEC_FILTER_BLOCK
+#define SPEC_FILTER_BLOCK 512
+#endif
 #ifndef SPEC_FILTER_VPG_F32
 #define SPEC_FILTER_VPG_F32 4
 #endif
@@ -483,15 +488,14 @@ int spec_filter(const void* logits, int dtype, int R, int V, float temperature, 
   const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kBF16, SPEC_FILTER_VPG_BF16>), dim3(R),
-                       dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
-                       thresholds, row_stats);
-  } else {
-    hipLaunchKernelGGL((spec::filter_kernel<kStatsBlock, kF32, SPEC_FILTER_VPG_F32>), dim3(R),
-                       dim3(kStatsBlock), 0, s, logits, filtered, V, c2, yscale, k, p,
-                       thresholds, row_stats);
-  }
+  if (dtype == SPEC_DTYPE_BF16)
+    hipLaunchKernelGGL((spec::filter_kernel<SPEC_FILTER_BLOCK, kBF16, SPEC_FILTER_VPG_BF16>),
+                       dim3(R), dim3(SPEC_FILTER_BLOCK), 0, s, logits, filtered, V, c2, yscale, k,
+                       p, thresholds, row_stats);
+  else
+    hipLaunchKernelGGL((spec::filter_kernel<SPEC_FILTER_BLOCK, kF32, SPEC_FILTER_VPG_F32>),
+                       dim3(R), dim3(SPEC_FILTER_BLOCK), 0, s, logits, filtered, V, c2, yscale, k,
+                       p, thresholds, row_stats);
   return launched();
 }
 

@@ -184,6 +184,25 @@ def test_rows_outside_the_window(case):
     check_filter(z, T, k, p, case)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_k_at_the_block_size(dtype):
+    """top_k up to the filter's block size (512 threads) takes the window from
+    the per-thread maxima and re-reads only the vectors whose largest key
+    reaches it; top_k one past it re-reads the whole row.  Both around the
+    switch, plus constant rows (every vector marked, the window over LDS) and
+    rows with -inf runs (already filtered rows), including a ragged head."""
+    z = zipf_rows(20, 32000, dtype, seed=51)
+    z[3, :] = 1.5
+    z[4, 100:20000] = float("-inf")
+    z[5, ::3] = float("-inf")
+    for k, p in [(512, 1.0), (513, 1.0), (512, 0.6), (2, 0.99)]:
+        check_filter(z, 0.9, k, p, f"block-size {dtype} k={k} p={p}")
+    big = torch.empty(20 * 32000 + 5, dtype=z.dtype, device="cuda")
+    view = big[5:].view(20, 32000)  # rows off 16-byte boundaries
+    view.copy_(z)
+    check_filter(view, 0.9, 300, 0.95, f"block-size ragged {dtype}")
+
+
 def test_repeatable():
     from speculative_sampling_verification_softmax_amd import binding
     z = zipf_rows(64, 32000, "f32", seed=41)
