@@ -113,9 +113,12 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def find_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a matching traffic-record line in profiles/."""
+def find_traffic(kernel: str, workload: str, setting: str | None = None):
+    """HBM bytes per launch (per step for the filter's two calls) from a
+    matching traffic-record line in profiles/."""
     want = {"kernel": kernel, "workload": workload, "sources": kernel_sources_hash()}
+    if setting is not None:
+        want["setting"] = setting
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(f) as fh:
             for line in fh:
@@ -125,6 +128,10 @@ def find_traffic(kernel: str, workload: str):
                 if all(kv.get(k) == v for k, v in want.items()):
                     return float(kv["bytes"])
     return None
+
+
+def filter_setting(top_k: int, top_p: float) -> str:
+    return f"k{top_k}-p{top_p:g}"
 
 
 def _pmc_kernels(path: str) -> dict:
@@ -190,8 +197,9 @@ def pmc_summary(d: str, path: str, workload: str, command: str, mode: str = "ver
     what = "step (two launches)" if mode == "filter" else "launch"
     lines += ["", f"Algorithmic bytes of one `{dom}` {what}: {alg}."]
     if rec is not None:
+        setting = f" setting={filter_setting(top_k, top_p)}" if mode == "filter" else ""
         lines += [f"Measured HBM bytes per {what}: {rec:.6g} ({rec / alg:.4f} of algorithmic).",
-                  "", f"traffic-record: kernel={dom} workload={workload} "
+                  "", f"traffic-record: kernel={dom} workload={workload}{setting} "
                   f"sources={kernel_sources_hash()} bytes={rec:.0f}"]
     return "\n".join(lines) + "\n"
 
@@ -442,11 +450,16 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if args.mode == "greedy" else "f64",
         "data": "synthetic",
-        "config": {"workload": wl.name, "mode": args.mode, "B": B, "K": K, "V": V,
-                   "logits": wl.dtype, "T": wl.T, "seed": args.seed},
+        "config": dict({"workload": wl.name, "mode": args.mode, "B": B, "K": K, "V": V,
+                        "logits": wl.dtype, "T": wl.T, "seed": args.seed},
+                       **({"top_k": args.top_k, "top_p": args.top_p}
+                          if args.mode in ("filter", "filtered") else {})),
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "launch_us": call_ms * 1e3, "bytes_per_launch": alg},
+                     "traffic": (find_traffic("filter_kernel", wl.name,
+                                              filter_setting(args.top_k, args.top_p))
+                                 if args.mode == "filter" else None),
+                     "launch_us": call_ms * 1e3, "bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }
 
@@ -588,6 +601,72 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
             "peak_GBps": HBM_PEAK_GBPS, "reads": res, "stats_kernel": sk}
 
 
+def summary_from(files: list, command: str) -> str:
+    """Markdown tables for profiles/ from the JSON lines earlier runs printed
+    (one file per run: the verify paths and workloads, the filter settings
+    and other entry points, the K sweep, the read ceiling)."""
+    recs = []
+    for f in files:
+        with open(f) as fh:
+            recs.append(json.loads([l for l in fh.read().splitlines() if l.startswith("{")][-1]))
+    mode = recs[0]["config"].get("mode", "verify")
+    out = ["Commands (one MI355X, from the repository root; each a run of its own, its JSON line "
+           "saved to the file named):", "", "```", command, "```", ""]
+    f3 = lambda x: "—" if x is None else f"{x:.3g}"
+    if mode == "verify":
+        out += ["| workload | path | µs per step | sequences/s | GB/s over the step (% of peak) | "
+                "stats µs (event pair) | `roofline.frac` | cold step µs | parity (draws, "
+                "flagged, failures) |", "|---|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            c, rf, par = r["config"], r["roofline"], r.get("parity") or {}
+            cold = r.get("ms_per_step_cold")
+            colds = "—" if cold is None else f"{cold * 1e3:.1f}"
+            out.append(f"| {c['workload']} | {c['path']} | {r['ms_per_step'] * 1e3:.1f} | "
+                       f"{r['value']:.4g} | {r['achieved_GBps']:.0f} ({r['pct_of_peak']:.1f} %) | "
+                       f"{rf['launch_us']:.1f} | {rf['frac']:.3f} | {colds} | "
+                       f"{par.get('draws', '—')}, {par.get('flagged', '—')}, "
+                       f"{par.get('failures', '—')} |")
+        out += ["", "`cold step`: median with a 1 GiB write between steps (evicts the 256 MB MALL; "
+                "taken only for logits under 512 MB)."]
+    elif mode == "ksweep":
+        r = recs[0]
+        out += [r["metric"] + ".", "",
+                "| K | µs per step | emitted per sequence (mean ± std) | oracle expectation "
+                "(± batch-mean std. error) | µs per emitted token | GB/s |",
+                "|---|---|---|---|---|---|"]
+        for k in r["sweep"]:
+            exp = (f"{k['emitted_expected']:.3f} (± {k['emitted_mean_stderr']:.3f})"
+                   if "emitted_expected" in k else "—")
+            out.append(f"| {k['K']} | {k['us_per_step']:.1f} | {k['emitted_mean']:.3f} ± "
+                       f"{k['emitted_std']:.3f} | {exp} | {k['us_per_emitted_token']:.1f} | "
+                       f"{k['GBps']:.0f} |")
+    elif mode == "read-ceiling":
+        r = recs[0]
+        out += [r["metric"] + ".", "", "| shape | workgroups | µs | GB/s | % of 8 TB/s |",
+                "|---|---|---|---|---|"]
+        for x in r["reads"]:
+            out.append(f"| {x['shape']} | {x['workgroups']} | {x['us']:.1f} | {x['GBps']:.0f} | "
+                       f"{100 * x['GBps'] / HBM_PEAK_GBPS:.1f} |")
+        sk = r["stats_kernel"]
+        out += ["", f"`spec_softmax_stats` on the same workload's rows: {sk['us']:.1f} µs, "
+                f"{sk['GBps']:.0f} GB/s, {100 * sk['of_best_read']:.1f} % of the best plain read."]
+    else:
+        out += ["| call | setting | µs per step | throughput | GB/s over the algorithmic bytes | "
+                "`roofline.frac` | measured traffic | CPU oracle |",
+                "|---|---|---|---|---|---|---|---|"]
+        for r in recs:
+            c, rf, cb = r["config"], r["roofline"], r.get("cpu_baseline")
+            setting = (f"top-k {c['top_k']}, top-p {c['top_p']}" if "top_k" in c else "—")
+            tr = rf.get("traffic")
+            trs = "—" if tr is None else f"{tr / rf['bytes_per_launch']:.3f}× algorithmic"
+            cbs = "—" if not cb else f3(cb["value"]) + " " + cb["unit"]
+            out.append(f"| {c['mode']} | {setting} | {r['ms_per_step'] * 1e3:.1f} | "
+                       f"{r['value']:.4g} {r['unit']} | {rf['achieved']:.0f} | {rf['frac']:.3f} | "
+                       f"{trs} | {cbs} |")
+    out += ["", f"Kernel sources: {kernel_sources_hash()}."]
+    return "\n".join(out) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -618,6 +697,9 @@ def main() -> int:
                          "(a known-size reference for HBM byte counters) and exit")
     ap.add_argument("--pmc-summary", default=None, metavar="DIR",
                     help="print the markdown summary of rocprofv3 --pmc output under DIR and exit")
+    ap.add_argument("--summary-from", nargs="+", default=None, metavar="JSON",
+                    help="print the markdown table of the JSON lines saved from earlier runs "
+                         "(with --command: the commands that made them) and exit")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="print the markdown table of rocprofv3 --kernel-trace --stats output "
                          "under DIR and exit")
@@ -628,6 +710,9 @@ def main() -> int:
     if args.pmc_summary:
         print(pmc_summary(args.pmc_summary, args.path, args.workload, args.command, args.mode,
                           args.top_k, args.top_p), end="")
+        return 0
+    if args.summary_from:
+        print(summary_from(args.summary_from, args.command), end="")
         return 0
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.command), end="")
@@ -767,7 +852,8 @@ def main() -> int:
         log(f"[bench] parity: {par}")
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "headline" else
+        f"verified seqs/sec + achieved HBM GB/s (% of peak), B={B} K={K} V={wl.V} {wl.dtype}",
         "value": seqs_per_s,
         "unit": "seqs/s",
         "n_gpus": 1,
