@@ -546,8 +546,9 @@ def ksweep(args, base: synth.Workload) -> dict:
 def read_ceiling(args, wl: synth.Workload) -> dict:
     """What a kernel that only reads gets from HBM on this part: the probe of
     libspec_probe.so (16-byte non-temporal loads, as the stats kernel issues)
-    over a buffer of the workload's logit bytes, in three shapes, and the
-    stats kernel itself on the workload's rows; event-timed per launch."""
+    over a buffer of the workload's logit bytes, in four shapes, one of them
+    again with the default cache policy, and the stats kernel itself on the
+    workload's rows; event-timed per launch."""
     import ctypes
     from speculative_sampling_verification_softmax_amd import build as hip_build
     probe = ctypes.CDLL(hip_build.PROBE_LIB)
@@ -564,7 +565,9 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
     for name, mode, groups in [("grid-stride, 8 loads in flight", 0, rows),
                                ("grid-stride, 4 loads in flight", 1, rows),
                                ("grid-stride, 8 loads in flight, 1024 workgroups", 0, 1024),
-                               ("one row per workgroup, 4 loads in flight", 2, rows)]:
+                               ("one row per workgroup, 4 loads in flight", 2, rows),
+                               ("one row per workgroup, 4 loads in flight, default loads", 3,
+                                rows)]:
         def call(ev=None):
             if ev is not None:
                 ev[0].record(stream)
@@ -616,16 +619,19 @@ def summary_from(files: list, command: str) -> str:
     if mode == "verify":
         out += ["| workload | path | µs per step | sequences/s | GB/s over the step (% of peak) | "
                 "stats µs (event pair) | `roofline.frac` | cold step µs | parity (draws, "
-                "flagged, failures) |", "|---|---|---|---|---|---|---|---|---|"]
+                "flagged, failures) | CPU oracle, sequences/s (threads) |",
+                "|---|---|---|---|---|---|---|---|---|---|"]
         for r in recs:
             c, rf, par = r["config"], r["roofline"], r.get("parity") or {}
             cold = r.get("ms_per_step_cold")
             colds = "—" if cold is None else f"{cold * 1e3:.1f}"
+            cb, cb1 = r.get("cpu_baseline"), r.get("cpu_baseline_1thread")
+            cpus = "; ".join(f"{f3(c['value'])} ({c['cores']})" for c in (cb, cb1) if c) or "—"
             out.append(f"| {c['workload']} | {c['path']} | {r['ms_per_step'] * 1e3:.1f} | "
                        f"{r['value']:.4g} | {r['achieved_GBps']:.0f} ({r['pct_of_peak']:.1f} %) | "
                        f"{rf['launch_us']:.1f} | {rf['frac']:.3f} | {colds} | "
                        f"{par.get('draws', '—')}, {par.get('flagged', '—')}, "
-                       f"{par.get('failures', '—')} |")
+                       f"{par.get('failures', '—')} | {cpus} |")
         out += ["", "`cold step`: median with a 1 GiB write between steps (evicts the 256 MB MALL; "
                 "taken only for logits under 512 MB)."]
     elif mode == "ksweep":

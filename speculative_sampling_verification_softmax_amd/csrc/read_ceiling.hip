@@ -2,7 +2,8 @@
 // streaming reads of a device buffer with the access pattern of the stats
 // kernel (16-byte non-temporal loads), so that the rate the stats kernel
 // reaches can be compared with what this part delivers to a kernel that does
-// nothing but read.  Built as its own library (libspec_probe.so) and loaded
+// nothing but read (and, one shape, the same reads with the default cache
+// policy).  Built as its own library (libspec_probe.so) and loaded
 // by the benchmark only.
 #include <hip/hip_runtime.h>
 
@@ -48,10 +49,15 @@ __global__ __launch_bounds__(1024) void read_grid_stride(const uint4* __restrict
   }
 }
 
+__device__ __forceinline__ uint4 load_cached(const uint4* p) { return *p; }
+
 // One row per workgroup, as the stats kernel streams: groups of 4 vectors
-// per thread, the next group's loads issued before the current one is used.
+// per thread, the next group's loads issued before the current one is used;
+// NT: non-temporal loads (as the stats kernel), else the default policy.
+template <bool NT>
 __global__ __launch_bounds__(1024) void read_rows(const uint4* __restrict__ p, size_t row_vec,
                                                   unsigned* __restrict__ sink) {
+  auto load = [](const uint4* q) { return NT ? load_nt(q) : load_cached(q); };
   const uint4* row = p + static_cast<size_t>(blockIdx.x) * row_vec;
   constexpr int G = 4;
   const size_t step = static_cast<size_t>(blockDim.x) * G;
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(1024) void read_rows(const uint4* __restrict__ p, s
   bool have = i + (G - 1) * blockDim.x < row_vec;
   if (have)
 #pragma unroll
-    for (int g = 0; g < G; ++g) v[g] = load_nt(row + i + g * blockDim.x);
+    for (int g = 0; g < G; ++g) v[g] = load(row + i + g * blockDim.x);
   while (have) {
     uint4 cur[G];
 #pragma unroll
@@ -70,11 +76,11 @@ __global__ __launch_bounds__(1024) void read_rows(const uint4* __restrict__ p, s
     have = i + (G - 1) * blockDim.x < row_vec;
     if (have)
 #pragma unroll
-      for (int g = 0; g < G; ++g) v[g] = load_nt(row + i + g * blockDim.x);
+      for (int g = 0; g < G; ++g) v[g] = load(row + i + g * blockDim.x);
 #pragma unroll
     for (int g = 0; g < G; ++g) acc ^= fold4(cur[g]);
   }
-  for (; i < row_vec; i += blockDim.x) acc ^= fold4(load_nt(row + i));
+  for (; i < row_vec; i += blockDim.x) acc ^= fold4(load(row + i));
   __shared__ unsigned red[16];
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
@@ -97,6 +103,7 @@ extern "C" {
 //   mode 0: grid-stride, 8 loads in flight per thread, `groups` workgroups
 //   mode 1: grid-stride, 4 loads in flight per thread
 //   mode 2: one row of bytes/groups bytes per workgroup (a multiple of 16)
+//   mode 3: as mode 2 with default (cached) loads
 // sink: device memory of at least `groups` words.  Returns 0, or 1 for bad
 // arguments, 3 for a failed launch.
 int spec_probe_read(const void* p, size_t bytes, int mode, int groups, unsigned* sink,
@@ -111,9 +118,12 @@ int spec_probe_read(const void* p, size_t bytes, int mode, int groups, unsigned*
     hipLaunchKernelGGL(read_grid_stride<8>, dim3(groups), dim3(1024), 0, s, v, nvec, sink);
   } else if (mode == 1) {
     hipLaunchKernelGGL(read_grid_stride<4>, dim3(groups), dim3(1024), 0, s, v, nvec, sink);
-  } else if (mode == 2) {
+  } else if (mode == 2 || mode == 3) {
     if (nvec % static_cast<size_t>(groups) != 0) return 1;
-    hipLaunchKernelGGL(read_rows, dim3(groups), dim3(1024), 0, s, v, nvec / groups, sink);
+    if (mode == 2)
+      hipLaunchKernelGGL(read_rows<true>, dim3(groups), dim3(1024), 0, s, v, nvec / groups, sink);
+    else
+      hipLaunchKernelGGL(read_rows<false>, dim3(groups), dim3(1024), 0, s, v, nvec / groups, sink);
   } else {
     return 1;
   }
