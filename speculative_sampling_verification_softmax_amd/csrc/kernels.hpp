@@ -2180,7 +2180,9 @@ struct FilterShared {
   int sel_bin;
   double sel_need;
   unsigned ncand;
-  float cand[kFilterCap];
+  // 16-byte aligned: the top-k first pass's vector keys, kept in its upper
+  // part, are read back 16 bytes at a time
+  alignas(16) float cand[kFilterCap];
   // one bit per 16-byte vector of the row body that holds a window value
   // (rows of at most kFilterMapVecs vectors)
   unsigned vmap[kFilterMapVecs / 32];
