@@ -9,9 +9,11 @@ HBM.  --path two_call (default) runs it as spec_softmax_stats then
 spec_verify_sample on one stream; --path three_call as spec_softmax_stats,
 spec_verify, spec_residual_sample; --path step as spec_verify_step (the same
 two launches, with rows and sequences split over several workgroups when
-the batch is small).  W untimed steps, then K timed steps bracketed by
-device synchronisation, with nothing else on the stream.  Prints one JSON
-line on stdout; progress goes to stderr.
+the batch is small).  At least W untimed steps, continued until 0.1 s of
+device time has passed (the part's clocks ramp up over tens of milliseconds
+of load after idle; "warmup_run" reports the steps actually run), then K
+timed steps bracketed by device synchronisation, with nothing else on the
+stream.  Prints one JSON line on stdout; progress goes to stderr.
 
 Reported:
   value          verified sequences per second (B / seconds per step)
@@ -271,15 +273,33 @@ def cpu_baseline(inp: dict, wl: synth.Workload, max_seqs: int, gpu_out: dict,
     return base, one, parity
 
 
+SETTLE_S = 0.1
+WARMUP_RUN = {"steps": 0, "s": 0.0}
+
+
 def timed(step, steps: int, warmup: int, stream) -> tuple[float, float]:
     """(ms per step over the timed region, mean ms of the event pair that a
     step records around its main call).  The timed region holds `steps`
     steps and nothing else; the call's duration comes from `steps` further
-    steps that record the pair."""
+    steps that record the pair.
+
+    Warm-up: at least `warmup` untimed steps, and more until SETTLE_S seconds
+    of device time have passed.  After idle the part's clocks take tens of
+    milliseconds of load to come up (the first steps of a headline step run
+    ~3x slower), so a warm-up of a few steps would time the ramp rather than
+    the steady state a serving loop sees.  WARMUP_RUN records the steps and
+    seconds actually run (reported in the JSON line)."""
     torch.cuda.synchronize()
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < SETTLE_S:
         step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()  # wall time follows the device
     torch.cuda.synchronize()
+    WARMUP_RUN["steps"] = n
+    WARMUP_RUN["s"] = time.perf_counter() - t0
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -447,7 +467,8 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
     log(f"[bench] {args.mode}: {ms * 1e3:.1f} us/step, call {call_ms * 1e3:.1f} us")
     return {
         "metric": metric, "value": units / (ms * 1e-3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "warmup_run": dict(WARMUP_RUN),
+        "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32" if args.mode == "greedy" else "f64",
         "data": "synthetic",
         "config": dict({"workload": wl.name, "mode": args.mode, "B": B, "K": K, "V": V,
@@ -865,6 +886,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": dict(WARMUP_RUN),
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
