@@ -185,7 +185,11 @@ int spec_greedy_verify(const void* target_logits, int dtype, const int32_t* draf
  * the same exact inverse CDF in ascending token id as the bonus draw.
  *   logits      [R][V], dtype as above
  *   uniforms    [R] in [0, 1)
- *   row_stats   out [R][2] {m, s} as for spec_softmax_stats (computed here)
+ *   row_stats   out [R][2] {m, s}: the same quantities as spec_softmax_stats
+ *               writes (m exact; s within its rounding: bf16 rows whose
+ *               draw fits in LDS are read once, and their s comes from the
+ *               draw's own fp64 sum, more precise than the fp32 terms of
+ *               spec_softmax_stats, so the two can differ in the last bits)
  *   tokens      out [R]: x_r, or -1 for a row that defines no distribution
  * Returns SPEC_OK, SPEC_ERR_INVALID_ARG or SPEC_ERR_LAUNCH.
  */

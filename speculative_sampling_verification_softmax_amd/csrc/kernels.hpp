@@ -883,7 +883,12 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
       a = a + eq;
     }
   }
+  unsigned long long any_unc = 0ull;
   if (MODE == kModeResidual) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) any_unc |= unc_m[e];
+  }
+  if (MODE == kModeResidual && any_unc != 0ull) {  // one scalar test for the chunk; rare
     const int x0 = c * (kWave * E) + lane_id() * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -938,12 +943,32 @@ __device__ __forceinline__ void chunk_acc(const DrawRows& R, int c,
   chunk_accumulate<DT, MODE, H>(R, c, lookup, lsq, lsp, a, bb, out);
 }
 
+// What a one-pass sweep of a row also gathers for its statistics: the
+// lane's largest value and the largest |code| of its bf16 words (above
+// 0x7F80: a NaN).
+struct RowTrack {
+  float zmax = -__builtin_huge_valf();
+  unsigned mag = 0u;  // two 16-bit maxima, one per half-word
+};
+
 // chunk_accumulate from the raw words of bf16 rows with the exponential tables.
-template <int MODE>
+// TRACK: also fold the q row's codes into *trk.
+template <int MODE, bool TRACK = false>
 __device__ __forceinline__ void chunk_acc_words(const DrawRows& R, int c, const uint4& wq,
                                                 const uint4& wp, const double* tab, double& lsq,
                                                 double& lsp, double& a, double& bb,
-                                                ChunkSums& out) {
+                                                ChunkSums& out, RowTrack* trk = nullptr) {
+  if constexpr (TRACK) {
+    const unsigned q4[4] = {wq.x, wq.y, wq.z, wq.w};
+    u16x2 mg = __builtin_bit_cast(u16x2, trk->mag);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      trk->zmax = fmaxf(trk->zmax, fmaxf(__uint_as_float(q4[k] << 16),
+                                         __uint_as_float(q4[k] & 0xFFFF0000u)));
+      mg = __builtin_elementwise_max(mg, __builtin_bit_cast(u16x2, q4[k] & 0x7FFF7FFFu));
+    }
+    trk->mag = __builtin_bit_cast(unsigned, mg);
+  }
   const unsigned w8[8] = {wq.x, wq.y, wq.z, wq.w, wp.x, wp.y, wp.z, wp.w};
   auto lookup = [&](int e, double (&eq)[8], double (&ep)[8]) {
     const unsigned qw[4] = {w8[0], w8[1], w8[2], w8[3]};
@@ -1462,10 +1487,11 @@ __device__ __forceinline__ int fast_finish(const DrawRows& R, int ni, double Sq,
 // each other.  Every sum is formed per item -- a, bb and the normaliser parts
 // lq, lp, each reduced to four row totals -- and emit(s, cs, lq, lp) stores
 // them by item, so no result depends on which wave took which item.
-template <int DT, int MODE, int G, bool ET, typename Emit>
+template <int DT, int MODE, int G, bool ET, typename Emit, bool TRACK = false>
 __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, int ni, int nsub,
                                                    unsigned* next, const double* tab,
-                                                   Emit emit) {
+                                                   Emit emit, RowTrack* trk = nullptr) {
+  static_assert(!TRACK || (DT == kBF16 && ET), "row tracking rides on the bf16 table path");
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
   RawChunk buf;
@@ -1497,7 +1523,7 @@ __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, in
           }
           full = has_next && chunk_full<DT>(R, cn);
           if (full) chunk_issue<DT, MODE>(R, cn, buf);
-          chunk_acc_words<MODE>(R, c, wq, wp, tab, lq, lp, a, bb, cs);
+          chunk_acc_words<MODE, TRACK>(R, c, wq, wp, tab, lq, lp, a, bb, cs, trk);
         } else {
           float zq[E], zp[E];
           chunk_values<DT, MODE>(R, c, full, buf, zq, zp);
@@ -1867,6 +1893,95 @@ __global__ __launch_bounds__(BLOCK) void sample_kernel(const void* __restrict__ 
   const int tok = R.et != nullptr ? draw_block<BLOCK, DT, true>(R, uni[r], fast, work, sh)
                                   : draw_block<BLOCK, DT, false>(R, uni[r], fast, work, sh);
   if (threadIdx.x == 0) tokens[r] = tok;
+}
+
+// One read per row (bf16 rows whose table and fast-sweep arrays fit in LDS):
+// the bonus sweep over a table of exp(z/T) also tracks the row's
+// maximum and any NaN, so the row's statistics come from the sweep's own
+// sums -- s = S * exp(-m/T) with S = sum_x exp(z_x/T) formed in fp64 (the
+// quantity stats_kernel forms from fp32 terms, here more precise) -- and
+// the draw uses the same item sums.  A row whose maximum is too large for
+// that table (|m|/T > kSharedTableMax) is drawn again from a table of its
+// own, with the maximum subtracted.  Rows that define no distribution get token -1 and s = NaN, as
+// with stats_kernel and sample_kernel.
+template <int BLOCK>
+__global__ __launch_bounds__(BLOCK) void sample_onepass_kernel(const void* __restrict__ logits,
+                                                               const float* __restrict__ uni,
+                                                               int V, double yscale,
+                                                               float* __restrict__ stats_out,
+                                                               int32_t* __restrict__ tokens) {
+  constexpr int DT = kBF16;
+  constexpr int NW = BLOCK / kWave;
+  extern __shared__ double dyn[];
+  __shared__ DrawShared<BLOCK> sh;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  DrawRows R;
+  R.qrow = static_cast<const char*>(logits) + r * static_cast<int64_t>(V) * Elt<DT>::bytes;
+  R.prow = R.qrow;
+  R.V = V;
+  R.mode = kModeBonus;
+  R.aligned = (reinterpret_cast<uintptr_t>(R.qrow) & 15) == 0;
+  R.yscale = yscale;
+  R.mq = 0.0;
+  R.mp = 0.0;
+  R.cq = 1.0;
+  R.cp = 1.0;
+  R.et = nullptr;
+  R.etp = nullptr;
+  R.k_hi = uniform_margin(true);
+  R.k_lo = uniform_margin(false);
+  R.rho = 1.0;
+  fill_exp2_table(sh.tab);
+  if (tid == 0) {
+    sh.next = NW;
+    sh.sel[3] = 0;
+  }
+  __syncthreads();
+  // the table of exp(z/T) (maximum 0, factor 1), from the fp64 exponential
+  // the other codes and the per-row tables use
+  fill_row_exp_tables<BLOCK>(dyn, 1, R, sh.tab);
+  __syncthreads();
+  R.et = dyn;
+  R.etp = dyn;
+  double* work = dyn + kETab;
+  const int nch = (V + kWave * 8 - 1) / (kWave * 8);
+  const int ni = (nch + kDrawG - 1) / kDrawG;
+  const LdsItems it(work + ni, ni);
+  auto emit = [&](int c, const ChunkSums& cs, double lq, double lp) { it.emit(c, cs, lq, lp); };
+  RowTrack trk;
+  wave_sweep_claimed<DT, kModeBonus, kDrawG, true, decltype(emit), true>(
+      R, uniform(tid / kWave), ni, nch, &sh.next, sh.tab, emit, &trk);
+  // the row's maximum and NaN flag (block_max's barriers also end the sweep)
+  const float m = block_max<BLOCK>(trk.zmax, sh.redf);
+  const bool nan = (trk.mag & 0xFFFFu) > 0x7F80u || (trk.mag >> 16) > 0x7F80u;
+  const bool bad = block_max<BLOCK>(nan ? 1.0f : 0.0f, sh.redf) > 0.0f || !__builtin_isfinite(m);
+  const double invT = yscale / Exp64::kScale;
+  const double u = uni[r];
+  int tok = -1;
+  double srow = __builtin_nan("");
+  if (!bad && fabs(static_cast<double>(m)) * invT <= kSharedTableMax) {
+    tok = fast_finish<BLOCK, DT, true, kDrawG>(R, ni, 1.0, 1.0, it, work, u, sh);
+    srow = sh.seld[2] * exp(-static_cast<double>(m) * invT);  // S_w = sum_x exp(z_x/T)
+  } else if (!bad) {
+    // a table of the row's own: exp((z - m)/T); its sweep's total is s itself
+    R.mq = m;
+    R.et = nullptr;
+    R.etp = nullptr;
+    R.k_hi = uniform_margin(true);
+    R.k_lo = uniform_margin(false);
+    fill_row_exp_tables<BLOCK>(dyn, 1, R, sh.tab);
+    __syncthreads();
+    R.et = dyn;
+    R.etp = dyn;
+    tok = draw_block<BLOCK, DT, true>(R, u, 1, work, sh);
+    srow = sh.seld[2];
+  }
+  if (tid == 0) {
+    tokens[r] = tok;
+    stats_out[2 * r] = m;
+    stats_out[2 * r + 1] = static_cast<float>(srow);
+  }
 }
 
 // ================================================================== greedy

@@ -448,6 +448,14 @@ int spec_sample(const void* logits, int dtype, int R, int V, float temperature,
   const double yscale = (1.0 / static_cast<double>(temperature)) * spec::Exp64::kScale;
   const DrawLds d = draw_lds(num_chunks(V, dtype), dtype, 1);
   (void)hipGetLastError();
+  if (dtype == SPEC_DTYPE_BF16 && d.fast && d.etab) {
+    // one read per row: the statistics come out of the draw's own sweep
+    // 512 threads (78 VGPRs, ~52 KB of LDS): three rows share a CU, so one
+    // row's table fill and finish overlap the others' sweeps
+    hipLaunchKernelGGL((spec::sample_onepass_kernel<512>), dim3(R), dim3(512), d.bytes, s, logits,
+                       uniforms, V, yscale, row_stats, tokens);
+    return launched();
+  }
   if (dtype == SPEC_DTYPE_BF16) {
     hipLaunchKernelGGL((spec::stats_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>), dim3(R),
                        dim3(kStatsBlock), 0, s, logits, logits, static_cast<int64_t>(R), V, c2,

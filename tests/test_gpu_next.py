@@ -179,6 +179,40 @@ def test_sample_masks_and_invalid_rows():
     assert out[0] == 123 and out[1] == -1 and out[2] == -1 and out[3] % 2 == 1
 
 
+@pytest.mark.parametrize("T", [1.0, 0.05])
+def test_sample_bf16_one_pass_edges(T):
+    """bf16 rows take one read: the row's maximum and NaNs are tracked in the
+    draw's own sweep over the shared exp(z/T) table.  Rows whose maximum is
+    too large for that table (|m|/T > 300: shifted by +-400, or T = 0.05 with
+    logits up to ~20) are drawn again from a table of their own; NaN of
+    either sign, +inf and all -inf rows define no distribution."""
+    R, V = 12, 3000
+    g = torch.Generator(device="cuda").manual_seed(77)
+    z = torch.randn(R, V, device="cuda", generator=g) * 4
+    z[1] += 400.0
+    z[2] -= 400.0
+    z[3, 17] = float("nan")
+    z[4, 2999] = -float("nan")
+    z[5, 5] = float("inf")
+    z[6, :] = float("-inf")
+    z[7, :] = float("-inf")
+    z[7, 1234] = 3.0          # a single allowed token
+    z[8, ::3] = float("-inf")
+    z[9, :] = 2.5             # all equal
+    zb = z.to(torch.bfloat16)
+    check_sample(zb, T, 31, f"bf16 one-pass T={T}")
+    big = torch.empty(R * V + 3, dtype=torch.bfloat16, device="cuda")
+    view = big[3:].view(R, V)  # rows off 16-byte boundaries
+    view.copy_(zb)
+    check_sample(view, T, 32, f"bf16 one-pass unaligned T={T}")
+    from speculative_sampling_verification_softmax_amd import binding
+    out = binding.sample(zb, torch.full((R,), 0.5, device="cuda"), T)
+    tok = out["tokens"].cpu().numpy()
+    st = out["row_stats"].cpu().numpy()
+    assert list(tok[3:7]) == [-1, -1, -1, -1] and tok[7] == 1234
+    assert np.all(np.isnan(st[3:7, 1])) and not np.any(np.isnan(st[[0, 1, 2, 7, 8, 9], 1]))
+
+
 def test_sample_law_chi_square():
     """The draws follow softmax(z/T): chi-square of 2e5 draws on one row."""
     from scipy import special
