@@ -568,8 +568,9 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
     """What a kernel that only reads gets from HBM on this part: the probe of
     libspec_probe.so (16-byte non-temporal loads, as the stats kernel issues)
     over a buffer of the workload's logit bytes, in four shapes, one of them
-    again with the default cache policy, and the stats kernel itself on the
-    workload's rows; event-timed per launch."""
+    again with the default cache policy; a device copy of the same bytes (the
+    ceiling of a call that reads and writes every row once); and the stats
+    kernel itself on the workload's rows; event-timed per launch."""
     import ctypes
     from speculative_sampling_verification_softmax_amd import build as hip_build
     probe = ctypes.CDLL(hip_build.PROBE_LIB)
@@ -602,7 +603,21 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
         res.append({"shape": name, "workgroups": groups, "us": ms * 1e3,
                     "GBps": nbytes / (ms * 1e-3) / 1e9})
         log(f"[bench] read ceiling, {name}: {ms * 1e3:.1f} us, {res[-1]['GBps']:.0f} GB/s")
-    del buf
+    # a device copy of the same bytes (torch's copy kernel): the ceiling of a
+    # call that reads every row once and writes it once, as the filter does
+    dst = torch.empty_like(buf)
+
+    def copy(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dst.copy_(buf)
+        if ev is not None:
+            ev[1].record(stream)
+    ms, _ = timed(copy, args.steps, args.warmup, stream)
+    res.append({"shape": "device copy (torch), read + write", "workgroups": None,
+                "us": ms * 1e3, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9})
+    log(f"[bench] device copy: {ms * 1e3:.1f} us, {res[-1]['GBps']:.0f} GB/s read + write")
+    del buf, dst
     torch.cuda.empty_cache()
     inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
     ts = torch.empty((wl.B, wl.K + 1, 2), dtype=torch.float32, device="cuda")
@@ -616,7 +631,7 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
             ev[1].record(stream)
     ms, _ = timed(stats, args.steps, args.warmup, stream)
     sk = {"us": ms * 1e3, "GBps": stats_bytes(wl) / (ms * 1e-3) / 1e9}
-    sk["of_best_read"] = sk["GBps"] / max(r["GBps"] for r in res)
+    sk["of_best_read"] = sk["GBps"] / max(r["GBps"] for r in res if r["workgroups"] is not None)
     log(f"[bench] stats_kernel: {ms * 1e3:.1f} us, {sk['GBps']:.0f} GB/s "
         f"({100 * sk['of_best_read']:.1f} % of the best plain read)")
     return {"metric": f"streaming read ceiling over {nbytes} bytes (the {wl.name} logits)",
@@ -672,7 +687,8 @@ def summary_from(files: list, command: str) -> str:
         out += [r["metric"] + ".", "", "| shape | workgroups | µs | GB/s | % of 8 TB/s |",
                 "|---|---|---|---|---|"]
         for x in r["reads"]:
-            out.append(f"| {x['shape']} | {x['workgroups']} | {x['us']:.1f} | {x['GBps']:.0f} | "
+            wg = "—" if x["workgroups"] is None else x["workgroups"]
+            out.append(f"| {x['shape']} | {wg} | {x['us']:.1f} | {x['GBps']:.0f} | "
                        f"{100 * x['GBps'] / HBM_PEAK_GBPS:.1f} |")
         sk = r["stats_kernel"]
         out += ["", f"`spec_softmax_stats` on the same workload's rows: {sk['us']:.1f} µs, "
