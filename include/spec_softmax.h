@@ -241,10 +241,10 @@ size_t spec_verify_step_workspace_size(int B, int K, int V, int dtype);
  * spec_verify_step -- the whole verify step (what spec_softmax_stats followed
  * by spec_verify_sample computes: alg. 2 steps 2-4, sec. 4.2, "Decoding
  * transforms" and the Pitfalls readings cited above) in two launches.  With
- * fewer than 32 sequences, too few to occupy the device one workgroup per
+ * 64 sequences or fewer, too few to occupy the device one workgroup per
  * sequence, each sequence's final draw is split over several workgroups
  * that sweep parts of its row(s) and hand their sums to the one that
- * finishes last; from 32 sequences on it is spec_softmax_stats followed by
+ * finishes last; from 65 sequences on it is spec_softmax_stats followed by
  * spec_verify_sample.  The outputs are the same bits as those two calls give
  * (the split draw forms the same sums in the same order).
  *   inputs         as for the calls above (target, draft, tokens, uniforms)
@@ -282,9 +282,9 @@ int spec_verify_step(const void* target_logits, const void* draft_logits, int dt
  *     different streams or from different threads, race and must not be
  *     issued.
  *   - A shape whose spec_verify_step_workspace_size exceeds the array returns
- *     SPEC_ERR_UNSUPPORTED with nothing enqueued (only batches under 32
- *     sequences use it: up to 31 sequences of about 800K fp32 or all bf16
- *     vocabularies up to SPEC_MAX_V fit).
+ *     SPEC_ERR_UNSUPPORTED with nothing enqueued (only batches of 64
+ *     sequences or fewer use it: 64 sequences of up to about 800K bf16 or
+ *     400K fp32 tokens fit, 32 of any bf16 vocabulary up to SPEC_MAX_V).
  * Returns SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED or
  * SPEC_ERR_LAUNCH (also if the array cannot be looked up).
  */

@@ -39,12 +39,12 @@ using spec::kF32;
 constexpr int kStatsBlock = SPEC_STATS_BLOCK;
 constexpr int kResidBlock = 1024;
 // The split final draw of spec_verify_step: block size, the largest batch it
-// is used for (from 32 sequences on, one 1024-thread workgroup per sequence
-// draws as fast: a sequence's sweep is then throughput-bound on its CU, and
-// splitting it only adds the hand-off), the workgroups it aims for and the
-// most parts per sequence.
+// is used for (past 64 sequences, floor(256/B) parts per sequence leave too
+// few workgroups per part's hand-off to pay: one 1024-thread workgroup per
+// sequence draws as fast or faster), the workgroups it aims for and the most
+// parts per sequence.
 constexpr int kSplitDrawBlock = 512;
-constexpr int kSplitDrawMaxB = 31;
+constexpr int kSplitDrawMaxB = 64;
 constexpr int kStepDrawWGs = 256;
 constexpr int kMaxParts = 64;
 // Dynamic LDS of a draw workgroup (the bf16 exponential tables when they fit
@@ -140,7 +140,7 @@ StepLayout step_layout(int B, int K, int V, int dtype) {
   L.ni = (L.nch + spec::kDrawG - 1) / spec::kDrawG;
   L.Pd = 1;
   if (B <= kSplitDrawMaxB) {
-    L.Pd = std::min(std::min(L.ni, kMaxParts), (kStepDrawWGs + B - 1) / B);
+    L.Pd = std::min(std::min(L.ni, kMaxParts), kStepDrawWGs / B);  // at most 256 workgroups
     // a part's item records must fit its LDS next to the table and W
     while (L.Pd < L.ni && split_draw_lds(L.ni, L.nch, L.Pd, dtype) > kSplitDrawMaxLds) ++L.Pd;
   }

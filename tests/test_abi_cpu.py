@@ -115,13 +115,19 @@ def test_workspace_size_host_only():
     L = _lib()
     L.spec_verify_step_workspace_size.restype = ctypes.c_size_t
     size = lambda *a: L.spec_verify_step_workspace_size(*a)
-    # from 32 sequences on, one workgroup per sequence: the counters only
+    # from 65 sequences on, one workgroup per sequence: the counters only
     assert size(256, 8, 128256, 1) == 1024
-    assert size(32, 4, 32000, 1) == 256
-    # fewer sequences split the draw: one record of 160 bytes per sweep item of
+    assert size(65, 4, 32000, 1) == 512
+    # 64 or fewer split the draw: one record of 160 bytes per sweep item of
     # 1024 bf16 / 512 fp32 tokens and sequence, after the counters
     assert size(1, 4, 32000, 0) == 256 + (63 * 160 + 255) // 256 * 256
     assert size(31, 4, 32000, 1) == 256 + 31 * 32 * 160
+    assert size(64, 4, 32000, 1) == 256 + 64 * 32 * 160
+    # the no-allocation array's limits as its declaration states them
+    cap = binding.SPEC_NOALLOC_SCRATCH_BYTES
+    assert size(64, 1, 800000, 1) <= cap < size(64, 1, 900000, 1)
+    assert size(64, 1, 400000, 0) <= cap < size(64, 1, 450000, 0)
+    assert size(32, 1, 1 << 20, 1) <= cap
     assert size(16, 4, 32000, 0) > size(16, 4, 32000, 1)  # fp32 items hold fewer tokens
     assert size(0, 8, 100, 1) == 0
     assert size(1, 0, 100, 1) == 0
