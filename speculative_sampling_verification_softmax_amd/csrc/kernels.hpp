@@ -207,20 +207,24 @@ __device__ __forceinline__ void stream_body(const char* body, int nvec, F f) {
   }
   if (nfull * STEP < nvec) {  // one partial group: vectors past nvec read as -inf
     const int i0 = nfull * STEP + tid;
+    // every load issued before any is used (one round trip, not VPG): a lane
+    // whose vector lies past nvec loads the row's last vector instead (its
+    // offset entirely in the range-checked vector operand) and drops it
+    uint4 v[VPG];
+#pragma unroll
+    for (int u = 0; u < VPG; ++u) {
+      const int vi = min(i0 + u * BLOCK, nvec - 1);
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(rs, vi * 16, 0, AUX);
+      v[u] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
     float x[VPG * EPV];
 #pragma unroll
     for (int u = 0; u < VPG; ++u) {
       float xu[EPV];
-      if (i0 + u * BLOCK < nvec) {
-        const auto w =
-            __builtin_amdgcn_raw_buffer_load_b128(rs, vo, (nfull * STEP + u * BLOCK) * 16, AUX);
-        unpack16<DT>(make_uint4(w[0], w[1], w[2], w[3]), xu);
-      } else {
+      unpack16<DT>(v[u], xu);
+      const bool in = i0 + u * BLOCK < nvec;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) xu[e] = -__builtin_huge_valf();
-      }
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = xu[e];
+      for (int e = 0; e < EPV; ++e) x[u * EPV + e] = in ? xu[e] : -__builtin_huge_valf();
     }
     f(x, i0);
   }
