@@ -413,7 +413,7 @@ constexpr int kDrawG = 2;  // chunks per item of the fast sweep
 
 // Dynamic LDS of the fast sweep for a row of nch chunks: per item, the
 // finish's total W, then four row totals of each of A, Bv, Lq, Lp, unc_n,
-// kUncMax unc_idx and kUncMax unc_code (LdsItems).
+// kUncMax unc_q and kUncMax unc_p (LdsItems).
 constexpr size_t draw_fast_lds(int nch) {
   return static_cast<size_t>((nch + kDrawG - 1) / kDrawG) *
          (17 * sizeof(double) + (1 + 2 * kUncMax) * sizeof(int));
@@ -833,8 +833,9 @@ __device__ __forceinline__ void lane_weights(const DrawRows& R, int c, double iq
 struct ChunkSums {
   double A, Bv;
   int n_unc;
-  int unc[kUncMax];
-  unsigned ucode[kUncMax];  // bf16 words path: the token's q code | p code << 16
+  // the uncertain tokens' two logits as fp32 bit patterns (bf16 rows: the
+  // code in the high half), so that resolving them reads no row again
+  unsigned uq[kUncMax], up[kUncMax];
 };
 
 // An empty uncertain list.
@@ -842,23 +843,26 @@ __device__ __forceinline__ void chunk_sums_init(ChunkSums& out) {
   out.n_unc = 0;
 #pragma unroll
   for (int j = 0; j < kUncMax; ++j) {
-    out.unc[j] = -1;
-    out.ucode[j] = 0u;
+    out.uq[j] = 0u;
+    out.up[j] = 0u;
   }
 }
 
 // Fast-path arithmetic of one chunk.  lookup(e, eq, ep) gives the exponentials
 // of the lane's tokens e .. e+H-1 of the q row (and the p row for a residual).
 // Adds every token's e_q, e_p to the lane's lsq, lsp, the clearly positive
-// ones to a, bb, and the chunk's uncertain tokens to out's list -- with their
-// two bf16 codes when words (the lane's 4+4 raw words of a bf16 chunk) is set.
+// ones to a, bb, and the chunk's uncertain tokens to out's list with their two
+// logits, taken from words (the lane's 4+4 raw words of a bf16 chunk) when it
+// is set, else from the lane's values zqv, zpv.
 // A bonus draw needs no normaliser (its weights are e_q, the draw is
 // scale-free): there every e_q goes to a alone and lsq, lsp stay as they are.
 template <int DT, int MODE, int H, typename Lookup>
 __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Lookup lookup,
                                                  double& lsq, double& lsp, double& a, double& bb,
                                                  ChunkSums& out,
-                                                 const unsigned* words = nullptr) {
+                                                 const unsigned* words = nullptr,
+                                                 const float* zqv = nullptr,
+                                                 const float* zpv = nullptr) {
   constexpr int E = 16 / Elt<DT>::bytes;
   unsigned long long unc_m[E];  // per token slot: the lanes whose token is uncertain
   double eqh[H], eph[H];
@@ -893,24 +897,26 @@ __device__ __forceinline__ void chunk_accumulate(const DrawRows& R, int c, Looku
     for (int e = 0; e < E; ++e) any_unc |= unc_m[e];
   }
   if (MODE == kModeResidual && any_unc != 0ull) {  // one scalar test for the chunk; rare
-    const int x0 = c * (kWave * E) + lane_id() * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       unsigned long long m = unc_m[e];
       while (m) {  // wave-uniform; rare
         const int src = __ffsll(static_cast<long long>(m)) - 1;
-        const int idx = __shfl(x0, src, kWave) + e;
-        unsigned code = 0u;
+        unsigned bq, bp;
         if (words != nullptr) {  // token e sits in word e/2, lower id in the low half
           const unsigned wq = static_cast<unsigned>(__shfl(static_cast<int>(words[e / 2]), src, kWave));
           const unsigned wp = static_cast<unsigned>(__shfl(static_cast<int>(words[4 + e / 2]), src, kWave));
-          code = (e & 1) ? ((wq >> 16) | (wp & 0xFFFF0000u)) : ((wq & 0xFFFFu) | (wp << 16));
+          bq = (e & 1) ? (wq & 0xFFFF0000u) : (wq << 16);
+          bp = (e & 1) ? (wp & 0xFFFF0000u) : (wp << 16);
+        } else {
+          bq = static_cast<unsigned>(__shfl(static_cast<int>(__float_as_uint(zqv[e])), src, kWave));
+          bp = static_cast<unsigned>(__shfl(static_cast<int>(__float_as_uint(zpv[e])), src, kWave));
         }
 #pragma unroll
         for (int j = 0; j < kUncMax; ++j)
           if (j == out.n_unc) {
-            out.unc[j] = idx;
-            out.ucode[j] = code;
+            out.uq[j] = bq;
+            out.up[j] = bp;
           }
         out.n_unc += 1;
         m &= m - 1;
@@ -944,7 +950,7 @@ __device__ __forceinline__ void chunk_acc(const DrawRows& R, int c,
     row_exp_n<DT, ET, false, H>(R, zq + e, tab, eq);
     if (MODE == kModeResidual) row_exp_n<DT, ET, true, H>(R, zp + e, tab, ep);
   };
-  chunk_accumulate<DT, MODE, H>(R, c, lookup, lsq, lsp, a, bb, out);
+  chunk_accumulate<DT, MODE, H>(R, c, lookup, lsq, lsp, a, bb, out, nullptr, zq, zp);
 }
 
 // What a one-pass sweep of a row also gathers for its statistics: the
@@ -1256,26 +1262,26 @@ __device__ __forceinline__ int slow_draw(DrawRows R, int nch, double* W, double 
 //
 // What the fast sweep leaves per item: the sums A, Bv of the clearly positive
 // tokens' e_q and e_p, the normaliser parts Lq, Lp, and the uncertain tokens
-// (count, token ids, and their two bf16 codes on the table path).  Each sum is
+// (count and their two logits' fp32 bit patterns).  Each sum is
 // kept as the four in-row scan totals of the wave that swept the item (lanes
 // 15, 31, 47, 63) and added in sum_row_totals' order where it is read, so no
 // result depends on which wave, or which workgroup, swept which item.
 
 // In the LDS of the one workgroup that sweeps and draws: A, Bv, Lq, Lp as
-// arrays of 4*ni doubles, then unc_n[ni], unc_idx[ni*kUncMax],
-// unc_code[ni*kUncMax].
+// arrays of 4*ni doubles, then unc_n[ni], unc_q[ni*kUncMax],
+// unc_p[ni*kUncMax].
 struct LdsItems {
   double* A;
   double* Bv;
   double* Lq;
   double* Lp;
   int* unc_n;
-  int* unc_idx;
-  unsigned* unc_code;
+  unsigned* unc_q;
+  unsigned* unc_p;
   __device__ __forceinline__ LdsItems(double* base, int ni)
       : A(base), Bv(base + 4 * ni), Lq(base + 8 * ni), Lp(base + 12 * ni),
-        unc_n(reinterpret_cast<int*>(base + 16 * ni)), unc_idx(unc_n + ni),
-        unc_code(reinterpret_cast<unsigned*>(unc_idx + ni * kUncMax)) {}
+        unc_n(reinterpret_cast<int*>(base + 16 * ni)),
+        unc_q(reinterpret_cast<unsigned*>(unc_n + ni)), unc_p(unc_q + ni * kUncMax) {}
   // cs.A, cs.Bv, lq, lp: in-row scans (chunk_reduce with RS); the uncertain
   // list is the same in every lane.
   __device__ __forceinline__ void emit(int s, const ChunkSums& cs, double lq, double lp) const {
@@ -1291,8 +1297,8 @@ struct LdsItems {
       unc_n[s] = cs.n_unc;
 #pragma unroll
       for (int j = 0; j < kUncMax; ++j) {
-        unc_idx[s * kUncMax + j] = cs.unc[j];
-        unc_code[s * kUncMax + j] = cs.ucode[j];
+        unc_q[s * kUncMax + j] = cs.uq[j];
+        unc_p[s * kUncMax + j] = cs.up[j];
       }
     }
   }
@@ -1309,10 +1315,8 @@ struct LdsItems {
     return sum_row_totals(Lp[4 * c], Lp[4 * c + 1], Lp[4 * c + 2], Lp[4 * c + 3]);
   }
   __device__ __forceinline__ int n_unc(int c) const { return unc_n[c]; }
-  __device__ __forceinline__ int unc(int c, int j) const { return unc_idx[c * kUncMax + j]; }
-  __device__ __forceinline__ unsigned code(int c, int j) const {
-    return unc_code[c * kUncMax + j];
-  }
+  __device__ __forceinline__ unsigned uq(int c, int j) const { return unc_q[c * kUncMax + j]; }
+  __device__ __forceinline__ unsigned up(int c, int j) const { return unc_p[c * kUncMax + j]; }
 };
 
 // Bytes of the LDS item arrays for ni items.
@@ -1322,8 +1326,8 @@ constexpr size_t lds_items_bytes(int ni) {
 
 // In device memory, for a sequence whose sweep is split over several
 // workgroups: one record of kItemRec doubles per item -- doubles 4r..4r+3 hold
-// row r's totals of A, Bv, Lq, Lp, then the ints unc_n, unc_idx[kUncMax],
-// unc_code[kUncMax] -- written with sc1 stores by the workgroup that swept the
+// row r's totals of A, Bv, Lq, Lp, then the 32-bit words unc_n, unc_q[kUncMax],
+// unc_p[kUncMax] -- written with sc1 stores by the workgroup that swept the
 // item and read with sc1 loads by the workgroup that draws, possibly on
 // another XCD (device_common.hpp).  `rec` must be uniform.
 constexpr int kItemRec = 20;  // doubles per record (160 bytes)
@@ -1351,14 +1355,14 @@ struct GlobalItems {
         const double* src = f == 0 ? L.A : f == 1 ? L.Bv : f == 2 ? L.Lq : L.Lp;
         v = src[4 * i + r];
       } else {
-        // int words 32 + 2(w-16), +1: unc_n, unc_idx[..], unc_code[..], 0 padding
+        // int words 32 + 2(w-16), +1: unc_n, unc_q[..], unc_p[..], 0 padding
         int lo_hi[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int q = 2 * (w - 16) + h;
           lo_hi[h] = q == 0 ? L.unc_n[i]
-                   : q <= kUncMax ? L.unc_idx[i * kUncMax + q - 1]
-                   : q <= 2 * kUncMax ? static_cast<int>(L.unc_code[i * kUncMax + q - 1 - kUncMax])
+                   : q <= kUncMax ? static_cast<int>(L.unc_q[i * kUncMax + q - 1])
+                   : q <= 2 * kUncMax ? static_cast<int>(L.unc_p[i * kUncMax + q - 1 - kUncMax])
                    : 0;
         }
         v = __hiloint2double(lo_hi[1], lo_hi[0]);
@@ -1378,9 +1382,56 @@ struct GlobalItems {
     return I[static_cast<int64_t>(c) * (2 * kItemRec) + 32 + k];
   }
   __device__ __forceinline__ int n_unc(int c) const { return word(c, 0); }
-  __device__ __forceinline__ int unc(int c, int j) const { return word(c, 1 + j); }
-  __device__ __forceinline__ unsigned code(int c, int j) const {
+  __device__ __forceinline__ unsigned uq(int c, int j) const {
+    return static_cast<unsigned>(word(c, 1 + j));
+  }
+  __device__ __forceinline__ unsigned up(int c, int j) const {
     return static_cast<unsigned>(word(c, 1 + kUncMax + j));
+  }
+};
+
+// GlobalItems whose item threadIdx.x (when below ni) has its fields for the
+// finish (A, Bv and the uncertain tokens) loaded on construction.  The part
+// that finishes a split draw builds it before item_normalisers, so that these
+// loads travel with the normaliser parts' instead of a round trip later; the
+// row totals are kept as loaded and added where they are read, in
+// sum_row_totals' order, so every value is the one GlobalItems gives.
+struct GlobalItemsAhead : GlobalItems {
+  double ra[4], rb[4];
+  int nu;
+  unsigned wq[kUncMax], wp[kUncMax];
+  __device__ __forceinline__ GlobalItemsAhead(const GlobalItems& g, int ni) : GlobalItems(g) {
+    const int c = threadIdx.x;
+    if (c < ni) {
+      const int64_t o = static_cast<int64_t>(c) * kItemRec;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ra[r] = D[o + 4 * r];
+        rb[r] = D[o + 4 * r + 1];
+      }
+      nu = GlobalItems::n_unc(c);
+#pragma unroll
+      for (int j = 0; j < kUncMax; ++j) {
+        wq[j] = GlobalItems::uq(c, j);
+        wp[j] = GlobalItems::up(c, j);
+      }
+    }
+  }
+  __device__ __forceinline__ bool mine(int c) const { return c == static_cast<int>(threadIdx.x); }
+  __device__ __forceinline__ double a(int c) const {
+    return mine(c) ? sum_row_totals(ra[0], ra[1], ra[2], ra[3]) : GlobalItems::a(c);
+  }
+  __device__ __forceinline__ double bv(int c) const {
+    return mine(c) ? sum_row_totals(rb[0], rb[1], rb[2], rb[3]) : GlobalItems::bv(c);
+  }
+  __device__ __forceinline__ int n_unc(int c) const {
+    return mine(c) ? nu : GlobalItems::n_unc(c);
+  }
+  __device__ __forceinline__ unsigned uq(int c, int j) const {
+    return mine(c) ? wq[j] : GlobalItems::uq(c, j);
+  }
+  __device__ __forceinline__ unsigned up(int c, int j) const {
+    return mine(c) ? wp[j] : GlobalItems::up(c, j);
   }
 };
 
@@ -1435,18 +1486,8 @@ __device__ __forceinline__ int fast_finish(const DrawRows& R, int ni, double Sq,
 #pragma unroll
       for (int j = 0; j < kUncMax; ++j) {
         if (j < nu) {
-          // the token's stored logits: the codes the sweep kept (bf16 table
-          // path, exact), else read back from the rows
-          float zq, zp;
-          if constexpr (DT == kBF16 && ET) {
-            const unsigned cw = it.code(c, j);
-            zq = __uint_as_float(cw << 16);
-            zp = __uint_as_float(cw & 0xFFFF0000u);
-          } else {
-            const int x = it.unc(c, j);
-            zq = logit_f32<DT>(R.qrow, x);
-            zp = logit_f32<DT>(R.prow, x);
-          }
+          // the token's two logits as the sweep kept them (exact)
+          const float zq = __uint_as_float(it.uq(c, j)), zp = __uint_as_float(it.up(c, j));
           const double eq = row_exp<DT, ET, false>(R, zq, sh.tab);
           const double ep = row_exp<DT, ET, true>(R, zp, sh.tab);
           const double d = eq * iq - ep * ip;
@@ -1817,11 +1858,12 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
     return;
   }
   const double u = a.uni[b * K1 + K];
+  const GlobalItemsAhead ita(it, a.ni);
   double Sq, Sp;
-  item_normalisers<BLOCK>(it, a.ni, sh, Sq, Sp);  // its barrier orders the sel[3] clear
+  item_normalisers<BLOCK>(ita, a.ni, sh, Sq, Sp);  // its barrier orders the sel[3] clear
   int tok;
   if (R.et != nullptr) {
-    tok = fast_finish<BLOCK, DT, true, kDrawG>(R, a.ni, Sq, Sp, it, work, u, sh);
+    tok = fast_finish<BLOCK, DT, true, kDrawG>(R, a.ni, Sq, Sp, ita, work, u, sh);
     if (tok == -3) {  // residual without mass: the bonus draw from q_n
       DrawRows Rb = R;
       Rb.mode = kModeBonus;
@@ -1830,7 +1872,7 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
       tok = slow_draw<BLOCK, DT, true>(R, a.nch, work, u, sh, true, Sq, Sp);
     }
   } else {
-    tok = fast_finish<BLOCK, DT, false, kDrawG>(R, a.ni, Sq, Sp, it, work, u, sh);
+    tok = fast_finish<BLOCK, DT, false, kDrawG>(R, a.ni, Sq, Sp, ita, work, u, sh);
     if (tok == -3) {
       DrawRows Rb = R;
       Rb.mode = kModeBonus;
