@@ -247,6 +247,66 @@ def test_empty_residual_after_a_clean_fast_sweep(dtype):
     assert np.all(o["draw_kind"][::3] == 2)
 
 
+def _distinct_values(rng, V, dtype):
+    """V distinct logits, shuffled: evenly spaced fp32 values, or distinct
+    bf16 codes (1 + m/128) * 2**e for e in -6..3, both signs."""
+    if dtype == "f32":
+        vals = np.linspace(-5.0, 5.0, V)
+    else:
+        mags = np.array([(1 + m / 128) * 2.0 ** e for e in range(-6, 4) for m in range(128)])
+        vals = np.concatenate([mags, -mags])
+        assert V <= vals.size
+        vals = rng.choice(vals, V, replace=False)
+    return rng.permutation(vals).astype(np.float32)
+
+
+def _permutation_fixing(rng, V, fixed):
+    """A permutation of range(V) whose only fixed points are `fixed`."""
+    fixed = np.asarray(sorted(set(int(f) for f in fixed)), np.int64)
+    rest = np.setdiff1d(np.arange(V), fixed)
+    img = rng.permutation(rest)
+    for i in np.nonzero(img == rest)[0]:  # break accidental fixed points
+        j = (i + 1) % rest.size
+        img[i], img[j] = img[j], img[i]
+    perm = np.arange(V)
+    perm[rest] = img
+    assert np.array_equal(np.sort(np.nonzero(perm == np.arange(V))[0]), fixed)
+    return perm
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_uncertain_tokens_resolved_from_the_records(dtype):
+    """Draft rows that permute their target row's distinct values, leaving a
+    few tokens in place: p and q are the same distribution over the same
+    values, so the fixed tokens have q = p (their residual sign is within
+    rounding: uncertain, resolved exactly once the normalisers are known) and
+    every other token differs clearly.  One fixed token per sweep item, two in
+    the first item (the most the fast path resolves), or three there (the
+    exact two-sweep path); some sequences fix the row's top token.  Modified
+    rejection sampling, the residual max(0, q - p) normalised ("Algorithm:
+    Speculative Sampling (SpS)", alg. 2)."""
+    rng = np.random.default_rng(23)
+    B, K = 12, 3
+    V, item = (3000, 512) if dtype == "f32" else (2560, 1024)
+    tgt = np.empty((B, K + 1, V), np.float32)
+    dft = np.empty((B, K, V), np.float32)
+    for b in range(B):
+        for t in range(K + 1):
+            tgt[b, t] = _distinct_values(rng, V, dtype)
+        for t in range(K):
+            fixed = [int(rng.integers(i, min(V, i + item))) for i in range(0, V, item)]
+            extra = b % 3  # 0, 1 or 2 more fixed tokens in the first item
+            while len(set(fixed)) < (V + item - 1) // item + extra:
+                fixed.append(int(rng.integers(0, item)))
+            if b % 4 == 0:
+                fixed.append(int(np.argmax(tgt[b, t])))
+            perm = _permutation_fixing(rng, V, fixed)
+            dft[b, t] = tgt[b, t][perm]
+    tok = _tokens_from(rng, dft, 1.0)
+    g, o = _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0, dtype), f"uncertain {dtype}")
+    assert np.sum((o["num_accepted"] >= 0) & (o["num_accepted"] < K)) >= B // 2
+
+
 def test_binding_rejects_bad_tensors():
     inp = synth.make_inputs("tiny", seed=0, device="cuda")
     with pytest.raises(ValueError):
