@@ -564,6 +564,120 @@ def ksweep(args, base: synth.Workload) -> dict:
             "sweep": out}
 
 
+STAMP_TICK_US = 0.01  # the device's real-time counter runs at 100 MHz
+SPLIT_DRAW_MAX_B = 64  # spec_verify_step splits the final draw up to this batch
+
+
+def _phase_stats(x) -> dict:
+    x = np.asarray(x, dtype=np.float64)
+    if x.size == 0:
+        return {"n": 0}
+    return {"n": int(x.size), "median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+            "p90": float(np.percentile(x, 90)), "max": float(x.max())}
+
+
+def phases(args, wl: synth.Workload) -> dict:
+    """Where a step's time goes, from libspec_phases.so (the library built with
+    the kernels' phase timestamps): `--steps` steps back to back, then the
+    stamps the last one left, seven times over.  Per stats workgroup its
+    duration; per draw workgroup the time between its phase boundaries (the
+    kernel source lists them at its SPEC_STAMP points).  Times in µs."""
+    import ctypes
+    from speculative_sampling_verification_softmax_amd import build as hip_build
+    L = binding.load(hip_build.PHASES_LIB)
+    L.spec_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    L.spec_phase_stamps.restype = ctypes.c_int
+    L.spec_phase_clear.argtypes = []
+    L.spec_phase_clear.restype = ctypes.c_int
+    inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
+    B, K, V = wl.B, wl.K, wl.V
+    rows = B * (2 * K + 1)
+    split = args.path == "step" and B <= SPLIT_DRAW_MAX_B
+    if args.path == "step":
+        ws = binding.new_workspace(B, K, V, inp["target"].dtype, "cuda")
+        step = lambda: binding.verify_step(inp["target"], inp["draft"], inp["tokens"],
+                                           inp["uniforms"], wl.T, ws)
+    elif args.path == "two_call":
+        step = lambda: binding.verify_two_call(inp["target"], inp["draft"], inp["tokens"],
+                                               inp["uniforms"], wl.T)
+    else:
+        raise SystemExit("--mode phases times the two_call or step path")
+    if rows > 8192 or B > 8192:
+        raise SystemExit("--mode phases records at most 8192 workgroups per launch")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SETTLE_S:  # clocks up, as in timed()
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    tick = STAMP_TICK_US
+    acc: dict = {}
+
+    def add(key, vals):
+        acc.setdefault(key, []).extend(np.asarray(vals, dtype=np.float64).tolist())
+
+    reps = 7
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        if L.spec_phase_clear() != 0:
+            raise RuntimeError("spec_phase_clear failed")
+        for _ in range(args.steps):
+            out = step()
+        torch.cuda.synchronize()
+        sr = np.zeros((8192, 2), np.uint64)
+        sd = np.zeros((8192, 8), np.uint64)
+        if L.spec_phase_stamps(sr.ctypes.data, sr.nbytes, 0) or \
+                L.spec_phase_stamps(sd.ctypes.data, sd.nbytes, 1):
+            raise RuntimeError("spec_phase_stamps failed")
+        st = sr[:rows].astype(np.int64)
+        t_first = st[:, 0].min()
+        st_us = (st - t_first) * tick
+        add("stats: workgroup duration", st_us[:, 1] - st_us[:, 0])
+        add("stats: last workgroup start", [st_us[:, 0].max()])
+        add("stats: span (first start to last end)", [st_us[:, 1].max()])
+        nacc = out["num_accepted"].cpu().numpy()
+        if split:
+            P = int(np.count_nonzero(sd[:, 0])) // B
+            d = sd[:B * P].astype(np.int64)
+            du = (d - t_first) * tick
+            add("draw: first start after stats end", [du[:, 0].min() - st_us[:, 1].max()])
+            add("draw: workgroup start spread", [du[:, 0].max() - du[:, 0].min()])
+            sw = d[:, 2] > 0
+            add("part: scan and tables", du[:, 1] - du[:, 0])
+            add("part: sweep of its items", du[sw, 2] - du[sw, 1])
+            add("part: records stored", du[sw, 3] - du[sw, 2])
+            fin = d[:, 4] >= d[:, 3]  # stamped by the finishing part in this step
+            add("finisher: counted last", du[fin, 4] - du[fin, 3])
+            add("finisher: normalisers", du[fin, 5] - du[fin, 4])
+            add("finisher: finish and output", du[fin, 6] - du[fin, 5])
+            add("draw: end (from the stats' first start)", [du[fin, 6].max()])
+            add("parts per sequence", [P])
+        else:
+            d = sd[:B].astype(np.int64)
+            du = (d - t_first) * tick
+            ok = np.all(np.diff(d[:, :7], axis=1) >= 0, axis=1) & (d[:, 0] > 0)
+            add("draw: first start after stats end", [du[:, 0].min() - st_us[:, 1].max()])
+            add("draw: workgroup start spread", [du[:, 0].max() - du[:, 0].min()])
+            for kind, sel in (("residual", ok & (nacc >= 0) & (nacc < K)),
+                              ("bonus", ok & (nacc == K))):
+                add(f"{kind}: scan and tables", du[sel, 1] - du[sel, 0])
+                add(f"{kind}: wave 0's sweep", du[sel, 2] - du[sel, 1])
+                add(f"{kind}: waiting for the other waves", du[sel, 3] - du[sel, 2])
+                add(f"{kind}: normalisers", du[sel, 4] - du[sel, 3])
+                add(f"{kind}: finish (item totals, crossing, in-chunk draw)",
+                    du[sel, 5] - du[sel, 4])
+                add(f"{kind}: output", du[sel, 6] - du[sel, 5])
+                add(f"{kind}: workgroup duration", du[sel, 6] - du[sel, 0])
+            add("draw: end (from the stats' first start)", [du[ok, 6].max()])
+    return {"metric": f"phase timestamps of one step ({args.path}), {wl.name}: B={B} K={K} V={V} "
+                      f"{wl.dtype}",
+            "unit": "us", "data": "synthetic",
+            "config": {"mode": "phases", "workload": wl.name, "B": B, "K": K, "V": V,
+                       "logits": wl.dtype, "T": wl.T, "path": args.path,
+                       "draw": "split" if split else "one workgroup per sequence",
+                       "steps": args.steps, "repeats": reps},
+            "phases": {k: _phase_stats(v) for k, v in acc.items()}}
+
+
 def read_ceiling(args, wl: synth.Workload) -> dict:
     """What a kernel that only reads gets from HBM on this part: the probe of
     libspec_probe.so (16-byte non-temporal loads, as the stats kernel issues)
@@ -682,6 +796,19 @@ def summary_from(files: list, command: str) -> str:
             out.append(f"| {k['K']} | {k['us_per_step']:.1f} | {k['emitted_mean']:.3f} ± "
                        f"{k['emitted_std']:.3f} | {exp} | {k['us_per_emitted_token']:.1f} | "
                        f"{k['GBps']:.0f} |")
+    elif mode == "phases":
+        for r in recs:
+            c = r["config"]
+            out += [f"**{c['workload']}** (B={c['B']}, K={c['K']}, V={c['V']}, {c['logits']}), "
+                    f"path `{c['path']}`, draw: {c['draw']}; the last of {c['steps']} steps back "
+                    f"to back, {c['repeats']} times; µs.", "",
+                    "| phase | median | p10 | p90 | max | samples |", "|---|---|---|---|---|---|"]
+            for k, v in r["phases"].items():
+                if v["n"] == 0:
+                    continue
+                out.append(f"| {k} | {v['median']:.2f} | {v['p10']:.2f} | {v['p90']:.2f} | "
+                           f"{v['max']:.2f} | {v['n']} |")
+            out.append("")
     elif mode == "read-ceiling":
         r = recs[0]
         out += [r["metric"] + ".", "", "| shape | workgroups | µs | GB/s | % of 8 TB/s |",
@@ -721,7 +848,7 @@ def main() -> int:
                     help="override the workload's batch size B (0: the workload's own)")
     ap.add_argument("--mode", default="verify",
                     choices=["verify", "greedy", "sample", "filter", "filtered", "ksweep",
-                             "read-ceiling"],
+                             "read-ceiling", "phases"],
                     help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
                          "sweep K")
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
@@ -781,10 +908,13 @@ def main() -> int:
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         return 2
 
-    binding.load()
     wl = synth.WORKLOADS[args.workload]
     if args.batch > 0:  # another batch size on the same rows' recipe
         wl = synth.workload(args.workload, B=args.batch)
+    if args.mode == "phases":  # loads the phase-stamped build instead of the library
+        print(json.dumps(phases(args, wl)), flush=True)
+        return 0
+    binding.load()
     if args.mode == "ksweep":
         print(json.dumps(ksweep(args, wl)), flush=True)
         return 0

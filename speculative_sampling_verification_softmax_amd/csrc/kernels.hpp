@@ -18,6 +18,33 @@
 
 namespace spec {
 
+// ============================================================= phase stamps
+//
+// Measurement builds only (-DSPEC_PHASE_STAMPS, libspec_phases.so): thread 0
+// of workgroup g < kStampWGs records the device's 100 MHz real-time counter
+// as it passes phase k, in stamps_rows[g][k] (stats_kernel: 0 start, 1 end)
+// or stamps_draw[g][k] (the draw kernels' phases, listed where they are
+// taken).  Every launch overwrites its workgroups' entries.  A time taken
+// early and stored late (SPEC_STAMP_NOW, SPEC_STAMP_AT) stays in scalar
+// registers meanwhile, so the streaming loop keeps its vector registers.  In
+// the library the macros expand to nothing.
+#ifdef SPEC_PHASE_STAMPS
+constexpr int kStampWGs = 8192;
+__device__ unsigned long long stamps_rows[kStampWGs][2];
+__device__ unsigned long long stamps_draw[kStampWGs][8];
+#define SPEC_STAMP_NOW() __builtin_amdgcn_s_memrealtime()
+#define SPEC_STAMP_AT(arr, k, t)                            \
+  do {                                                      \
+    if (threadIdx.x == 0 && blockIdx.x < ::spec::kStampWGs) \
+      ::spec::arr[blockIdx.x][k] = (t);                     \
+  } while (0)
+#define SPEC_STAMP(arr, k) SPEC_STAMP_AT(arr, k, SPEC_STAMP_NOW())
+#else
+#define SPEC_STAMP_NOW() 0ull
+#define SPEC_STAMP_AT(arr, k, t) ((void)(t))
+#define SPEC_STAMP(arr, k) ((void)0)
+#endif
+
 // ================================================================ row stats
 //
 // HBM-bound streaming reduction of one row.  The row is split into an
@@ -278,6 +305,7 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ t
                                                       float* __restrict__ dstats) {
   __shared__ float red_f[BLOCK / kWave];
   __shared__ double red_d[BLOCK / kWave];
+  [[maybe_unused]] const unsigned long long t_start = SPEC_STAMP_NOW();
   int64_t r = blockIdx.x;
   const char* row;
   float* out;
@@ -295,6 +323,8 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(const void* __restrict__ t
     out[0] = m;
     out[1] = s;
   }
+  SPEC_STAMP_AT(stamps_rows, 0, t_start);
+  SPEC_STAMP(stamps_rows, 1);
 }
 
 // =================================================================== verify
@@ -1615,9 +1645,13 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
       wave_sweep_claimed<DT, kModeResidual, kDrawG, ET>(R, wv, ni, nch, &sh.next, sh.tab, emit);
     else
       wave_sweep_claimed<DT, kModeBonus, kDrawG, ET>(R, wv, ni, nch, &sh.next, sh.tab, emit);
+    SPEC_STAMP(stamps_draw, 2);  // wave 0's last item done
     __syncthreads();
+    SPEC_STAMP(stamps_draw, 3);  // every wave's
     item_normalisers<BLOCK>(it, ni, sh, Sq, Sp);
+    SPEC_STAMP(stamps_draw, 4);
     tok = fast_finish<BLOCK, DT, ET, kDrawG>(R, ni, Sq, Sp, it, W, u, sh);
+    SPEC_STAMP(stamps_draw, 5);
   }
   if (tok == -3) {  // residual without mass: the bonus draw from q_n
     DrawRows Rb = R;
@@ -1687,6 +1721,7 @@ __device__ __forceinline__ void draw_sequence(int64_t b, int n, const void* tgt,
     out_tokens[b * K1 + n] = tok;
     if (num_emitted) num_emitted[b] = tok >= 0 ? n + 1 : 0;
   }
+  SPEC_STAMP(stamps_draw, 6);
 }
 
 // One workgroup per sequence (the spec_residual_sample path): the final draw
@@ -1722,6 +1757,8 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
   extern __shared__ double dyn[];
   __shared__ DrawShared<BLOCK> sh;
   const int64_t b = blockIdx.x;
+  // stamps: 0 start, 1 scan and tables done, then draw_block's 2-5 and 6 at the end
+  SPEC_STAMP(stamps_draw, 0);
   if (threadIdx.x < kWave) {
     const int n = verify_seq<DT, false>(b, tgt, dft, tokens, uni, tstats + 2 * b * (K + 1),
                                         dstats + 2 * b * K, K, V, invT, num_accepted,
@@ -1732,6 +1769,7 @@ __global__ __launch_bounds__(BLOCK) void verify_draw_kernel(
     if (DT == kBF16 && etab) fill_shared_exp_table<BLOCK>(dyn, yscale, kWave);
   }
   __syncthreads();
+  SPEC_STAMP(stamps_draw, 1);
   const int n = uniform(sh.sel[0]);
   __syncthreads();  // sel[] is reused by the draw
   draw_sequence<BLOCK, DT>(b, n, tgt, dft, uni, tstats, dstats, K, V, yscale, fast, etab,
@@ -1787,6 +1825,9 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
   const int K = a.K, V = a.V, tid = threadIdx.x;
   const int64_t K1 = K + 1;
   const bool etab = DT == kBF16 && a.etab != 0;
+  // stamps: 0 start, 1 scan and tables done, 2 sweep done, 3 records stored;
+  // the finishing part: 4 counted last, 5 normalisers, 6 end
+  SPEC_STAMP(stamps_draw, 0);
   if (tid < kWave) {
     const int n = verify_seq<DT, false>(b, a.tgt, a.dft, a.tokens, a.uni, a.tstats + 2 * b * K1,
                                         a.dstats + 2 * b * K, K, V, a.invT, a.num_accepted,
@@ -1797,6 +1838,7 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
     if (etab) fill_shared_exp_table<BLOCK>(dyn, a.yscale, kWave);
   }
   __syncthreads();
+  SPEC_STAMP(stamps_draw, 1);
   const int n = uniform(sh.sel[0]);
   DrawRows R;
   bool rows_ok = false;
@@ -1836,11 +1878,13 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
                                                           sh.tab, emit);
     }
     __syncthreads();
+    SPEC_STAMP(stamps_draw, 2);
     it.write_from(own, s0, s1 - s0);
   }
   // this part's records are complete (device-coherent) before it is counted
   store_complete();
   __syncthreads();
+  SPEC_STAMP(stamps_draw, 3);
   if (tid == 0) {
     sh.sel[3] = 0;
     sh.last = atomic_add_dev(&a.parts_done[b], 1u) == static_cast<unsigned>(a.P - 1) ? 1u : 0u;
@@ -1857,10 +1901,12 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
     }
     return;
   }
+  SPEC_STAMP(stamps_draw, 4);
   const double u = a.uni[b * K1 + K];
   const GlobalItemsAhead ita(it, a.ni);
   double Sq, Sp;
   item_normalisers<BLOCK>(ita, a.ni, sh, Sq, Sp);  // its barrier orders the sel[3] clear
+  SPEC_STAMP(stamps_draw, 5);
   int tok;
   if (R.et != nullptr) {
     tok = fast_finish<BLOCK, DT, true, kDrawG>(R, a.ni, Sq, Sp, ita, work, u, sh);
@@ -1886,6 +1932,7 @@ __global__ __launch_bounds__(BLOCK, 4) void verify_draw_split_kernel(SplitDraw a
     if (a.num_emitted) a.num_emitted[b] = tok >= 0 ? n + 1 : 0;
     atomic_store_dev(&a.parts_done[b], 0u);
   }
+  SPEC_STAMP(stamps_draw, 6);
 }
 
 // ============================================================ draft sampling

@@ -560,4 +560,32 @@ int spec_verify_step_noalloc(const void* target_logits, const void* draft_logits
                      num_emitted, static_cast<char*>(ws), L, s);
 }
 
+#ifdef SPEC_PHASE_STAMPS
+// Measurement builds only (libspec_phases.so): copy the phase stamps the
+// kernels recorded to host memory -- which 0: stats_kernel's [8192][2], 1:
+// the draw kernels' [8192][8], both uint64 -- or zero them.  Synchronous;
+// call them with no launch of this library in flight.
+int spec_phase_stamps(void* host, size_t bytes, int which) {
+  const size_t have = which == 0 ? sizeof(spec::stamps_rows) : sizeof(spec::stamps_draw);
+  if (host == nullptr || (which != 0 && which != 1) || bytes > have) return SPEC_ERR_INVALID_ARG;
+  const hipError_t e =
+      which == 0 ? hipMemcpyFromSymbol(host, HIP_SYMBOL(spec::stamps_rows), bytes, 0,
+                                       hipMemcpyDeviceToHost)
+                 : hipMemcpyFromSymbol(host, HIP_SYMBOL(spec::stamps_draw), bytes, 0,
+                                       hipMemcpyDeviceToHost);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
+int spec_phase_clear(void) {
+  static unsigned long long zr[spec::kStampWGs][2];  // zero (static storage)
+  static unsigned long long zd[spec::kStampWGs][8];
+  if (hipMemcpyToSymbol(HIP_SYMBOL(spec::stamps_rows), zr, sizeof(zr), 0,
+                        hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(spec::stamps_draw), zd, sizeof(zd), 0,
+                        hipMemcpyHostToDevice) != hipSuccess)
+    return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}
+#endif
+
 }  // extern "C"

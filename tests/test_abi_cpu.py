@@ -37,6 +37,25 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_phase_stamps_only_in_the_measurement_build():
+    """libspec_phases.so (the kernels with their phase timestamps) exports the
+    stamp readers as well as every declared entry point; the library itself
+    has none of them and rejects nothing differently."""
+    from speculative_sampling_verification_softmax_amd import build
+    if not os.path.exists(build.PHASES_LIB):
+        build.build()
+    lib = _lib()
+    assert not hasattr(lib, "spec_phase_stamps") and not hasattr(lib, "spec_phase_clear")
+    ph = ctypes.CDLL(build.PHASES_LIB)
+    for name in declared_functions() + ["spec_phase_stamps", "spec_phase_clear"]:
+        assert hasattr(ph, name), name
+    ph.spec_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    buf = (ctypes.c_uint64 * 16)()
+    assert ph.spec_phase_stamps(None, 8, 0) == 1  # SPEC_ERR_INVALID_ARG
+    assert ph.spec_phase_stamps(buf, 8, 2) == 1  # SPEC_ERR_INVALID_ARG
+    assert ph.spec_phase_stamps(buf, 8192 * 2 * 8 + 8, 0) == 1  # SPEC_ERR_INVALID_ARG
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict(re.findall(r"#define\s+(SPEC_\w+)\s+(\S+(?:\s*<<\s*\d+\))?)", text))
