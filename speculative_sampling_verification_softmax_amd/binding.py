@@ -42,6 +42,14 @@ def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """A library with this header's entry points (the library itself, or its
+    measurement build) loaded from `path`, its signatures declared; load()
+    keeps the one the wrappers call."""
     if not os.path.exists(path):
         raise SpecError(f"{path} is missing: build it with "
                         "`python -m speculative_sampling_verification_softmax_amd.build`")
@@ -73,7 +81,6 @@ def load(path: str = LIB_PATH):
     L.spec_filter.restype = i32
     L.spec_status_string.argtypes = [i32]
     L.spec_status_string.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

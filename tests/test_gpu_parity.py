@@ -182,6 +182,51 @@ def test_step_smaller_batch_after_larger_on_same_workspace():
         parity.assert_parity(parity.compare(g, o, inp["T"]), f"step B={B}")
 
 
+@pytest.mark.parametrize("path,B", [("two_call", 16), ("step", 16), ("step", 1)])
+def test_phase_stamped_build_matches_the_library(path, B):
+    """libspec_phases.so (the kernels with their phase timestamps compiled in,
+    which bench.py --mode phases times) gives the library's outputs bit for
+    bit, and its stamps are in phase order in every workgroup."""
+    import ctypes
+    from speculative_sampling_verification_softmax_amd import binding
+    from speculative_sampling_verification_softmax_amd import build as hip_build
+    wl = "small" if B > 1 else "batch1"
+    inp = synth.make_inputs(wl, seed=29, device="cuda", B=B)
+    K, V = inp["tokens"].shape[1], inp["target"].shape[2]
+    ws = binding.new_workspace(B, K, V, inp["target"].dtype, "cuda")
+    say(f"[phases] {wl} B={B} {path}: library, then the stamped build")
+    a = parity.gpu_verify(inp, path=path, workspace=ws)
+    ph = binding.open_library(hip_build.PHASES_LIB)
+    ph.spec_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    main = binding.load()
+    binding._lib = ph
+    try:
+        torch.cuda.synchronize()
+        assert ph.spec_phase_clear() == 0
+        b = parity.gpu_verify(inp, path=path, workspace=ws)
+        torch.cuda.synchronize()
+        rows = np.zeros((8192, 2), np.uint64)
+        draw = np.zeros((8192, 8), np.uint64)
+        assert ph.spec_phase_stamps(rows.ctypes.data, rows.nbytes, 0) == 0
+        assert ph.spec_phase_stamps(draw.ctypes.data, draw.nbytes, 1) == 0
+    finally:
+        binding._lib = main
+    for k in a:
+        assert a[k].tobytes() == b[k].tobytes(), k
+    R = B * (2 * K + 1)
+    r = rows[:R].astype(np.int64)
+    assert np.all(r[:, 0] > 0) and np.all(r[:, 1] >= r[:, 0]) and not np.any(rows[R:])
+    nwg = int(np.count_nonzero(draw[:, 0]))
+    d = draw[:nwg].astype(np.int64)
+    if path == "step":  # the split draw: parts per sequence, then the finishing part's stamps
+        assert nwg % B == 0 and nwg > B
+        assert np.all(np.diff(d[:, :4], axis=1) >= 0)
+        fin = d[:, 4] > 0
+        assert fin.sum() == B and np.all(np.diff(d[fin][:, 3:7], axis=1) >= 0)
+    else:  # one workgroup per sequence, every phase stamped in order
+        assert nwg == B and np.all(np.diff(d[:, :7], axis=1) >= 0)
+
+
 @pytest.mark.parametrize("wl", ["small", "headline"])
 def test_two_call_equals_three_call_bit_for_bit(wl):
     """spec_verify_sample runs the same accept and draw arithmetic as spec_verify
