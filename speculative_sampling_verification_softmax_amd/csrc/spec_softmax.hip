@@ -140,7 +140,13 @@ StepLayout step_layout(int B, int K, int V, int dtype) {
   L.ni = (L.nch + spec::kDrawG - 1) / spec::kDrawG;
   L.Pd = 1;
   if (B <= kSplitDrawMaxB) {
-    L.Pd = std::min(std::min(L.ni, kMaxParts), kStepDrawWGs / B);  // at most 256 workgroups
+    // As many parts as leave half the CUs busy, or one item per wave of a
+    // part (8 waves) when that is more; at most one workgroup per CU
+    // (measured: past 128 workgroups, parts of fewer than 8 items cost more
+    // in scans, tables and records than their shorter sweeps save).
+    const int per_wave = (L.ni + kSplitDrawBlock / spec::kWave - 1) / (kSplitDrawBlock / spec::kWave);
+    const int want = std::max(kStepDrawWGs / 2 / B, per_wave);
+    L.Pd = std::max(1, std::min(std::min(L.ni, kMaxParts), std::min(kStepDrawWGs / B, want)));
     // a part's item records must fit its LDS next to the table and W
     while (L.Pd < L.ni && split_draw_lds(L.ni, L.nch, L.Pd, dtype) > kSplitDrawMaxLds) ++L.Pd;
   }
