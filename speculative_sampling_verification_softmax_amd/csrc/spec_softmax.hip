@@ -427,8 +427,11 @@ int spec_greedy_verify(const void* target_logits, int dtype, const int32_t* draf
   const int64_t rows = static_cast<int64_t>(B) * (K + 1);
   (void)hipGetLastError();
   if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL((spec::argmax_kernel<kStatsBlock, kBF16, SPEC_STATS_VPG_BF16>),
-                       dim3(static_cast<unsigned>(rows)), dim3(kStatsBlock), 0, s, target_logits,
+    // bf16 rows in 512-thread workgroups, four per CU: the rows' last round
+    // leaves fewer slots idle (measured ~1 % faster at B=256 K=8, ~4 % at
+    // B=64 K=4 V=32000 than 1024 threads)
+    hipLaunchKernelGGL((spec::argmax_kernel<512, kBF16, SPEC_STATS_VPG_BF16>),
+                       dim3(static_cast<unsigned>(rows)), dim3(512), 0, s, target_logits,
                        V, target_argmax);
   } else {
     hipLaunchKernelGGL((spec::argmax_kernel<kStatsBlock, kF32, SPEC_STATS_VPG_F32>),
