@@ -681,8 +681,8 @@ def phases(args, wl: synth.Workload) -> dict:
 def read_ceiling(args, wl: synth.Workload) -> dict:
     """What a kernel that only reads gets from HBM on this part: the probe of
     libspec_probe.so (16-byte non-temporal loads, as the stats kernel issues)
-    over a buffer of the workload's logit bytes, in four shapes, one of them
-    again with the default cache policy; a device copy of the same bytes (the
+    over a buffer of the workload's logit bytes, in five shapes (one of them
+    again with the default cache policy); a device copy of the same bytes (the
     ceiling of a call that reads and writes every row once); and the stats
     kernel itself on the workload's rows; event-timed per launch."""
     import ctypes
@@ -702,6 +702,7 @@ def read_ceiling(args, wl: synth.Workload) -> dict:
                                ("grid-stride, 4 loads in flight", 1, rows),
                                ("grid-stride, 8 loads in flight, 1024 workgroups", 0, 1024),
                                ("one row per workgroup, 4 loads in flight", 2, rows),
+                               ("one row per 512-thread workgroup, 4 loads in flight", 4, rows),
                                ("one row per workgroup, 4 loads in flight, default loads", 3,
                                 rows)]:
         def call(ev=None):

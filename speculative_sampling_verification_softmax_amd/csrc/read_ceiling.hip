@@ -104,6 +104,7 @@ extern "C" {
 //   mode 1: grid-stride, 4 loads in flight per thread
 //   mode 2: one row of bytes/groups bytes per workgroup (a multiple of 16)
 //   mode 3: as mode 2 with default (cached) loads
+//   mode 4: as mode 2 with 512-thread workgroups (1024 threads otherwise)
 // sink: device memory of at least `groups` words.  Returns 0, or 1 for bad
 // arguments, 3 for a failed launch.
 int spec_probe_read(const void* p, size_t bytes, int mode, int groups, unsigned* sink,
@@ -118,10 +119,11 @@ int spec_probe_read(const void* p, size_t bytes, int mode, int groups, unsigned*
     hipLaunchKernelGGL(read_grid_stride<8>, dim3(groups), dim3(1024), 0, s, v, nvec, sink);
   } else if (mode == 1) {
     hipLaunchKernelGGL(read_grid_stride<4>, dim3(groups), dim3(1024), 0, s, v, nvec, sink);
-  } else if (mode == 2 || mode == 3) {
+  } else if (mode == 2 || mode == 3 || mode == 4) {
     if (nvec % static_cast<size_t>(groups) != 0) return 1;
-    if (mode == 2)
-      hipLaunchKernelGGL(read_rows<true>, dim3(groups), dim3(1024), 0, s, v, nvec / groups, sink);
+    if (mode == 2 || mode == 4)
+      hipLaunchKernelGGL(read_rows<true>, dim3(groups), dim3(mode == 4 ? 512 : 1024), 0, s, v,
+                         nvec / groups, sink);
     else
       hipLaunchKernelGGL(read_rows<false>, dim3(groups), dim3(1024), 0, s, v, nvec / groups, sink);
   } else {
