@@ -1665,9 +1665,9 @@ __device__ __forceinline__ int draw_block(const DrawRows& R, double u, int fast,
 
 // The final draw of sequence b with accepted count n, by the whole
 // workgroup: writes out_tokens[b][n] and num_emitted[b].  Dynamic LDS `dyn`:
-// the fast layout (A, Bv: nch doubles each; unc_n: nch ints; unc_idx:
-// nch*kUncMax ints) when `fast` is set, otherwise nch doubles for the slow
-// path; with `etab` (bf16) the two rows' exponential tables come first.
+// the fast layout (draw_fast_lds: per item its total W, then the LdsItems
+// arrays) when `fast` is set, otherwise nch doubles for the slow path; with
+// `etab` (bf16) the two rows' exponential tables come first.
 // n must be uniform across the workgroup.  tab_ready: sh.tab is already
 // filled (and a barrier has passed since); shared_ready: so is the shared
 // exponential table at dyn (fill_shared_exp_table).

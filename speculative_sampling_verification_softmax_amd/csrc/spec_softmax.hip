@@ -39,9 +39,9 @@ using spec::kF32;
 constexpr int kStatsBlock = SPEC_STATS_BLOCK;
 constexpr int kResidBlock = 1024;
 // The split final draw of spec_verify_step: block size, the largest batch it
-// is used for (past 64 sequences, floor(256/B) parts per sequence leave too
-// few workgroups per part's hand-off to pay: one 1024-thread workgroup per
-// sequence draws as fast or faster), the workgroups it aims for and the most
+// is used for (past 64 sequences the at most floor(256/B) parts per sequence
+// save less than their hand-off costs: one 1024-thread workgroup per sequence
+// draws as fast or faster), the most workgroups it launches and the most
 // parts per sequence.
 constexpr int kSplitDrawBlock = 512;
 constexpr int kSplitDrawMaxB = 64;
