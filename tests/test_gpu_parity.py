@@ -128,6 +128,36 @@ def test_ragged_shapes(V, K, dtype, B, path):
     parity.assert_parity(rep, f"V={V} K={K} {dtype}")
 
 
+# Row counts B*(2K+1) around the stats launch's workgroup-size switches (1024 threads up to 512
+# rows; 512 threads past 512 rows; fp32 back to 1024 threads past 1024 rows) and batches around
+# the split draw's part rule (fewer parts once B*P would reach every CU), K = 1: rows = 3B.
+LAUNCH_SHAPES = [(170, "bf16"), (171, "bf16"), (341, "bf16"), (342, "bf16"),
+                 (170, "f32"), (171, "f32"), (341, "f32"), (342, "f32")]
+
+
+@pytest.mark.parametrize("B,dtype", LAUNCH_SHAPES)
+def test_stats_launch_shapes(B, dtype):
+    wl = synth.workload("batch1", V=3001, K=1, dtype=dtype, B=B, T=0.9, name=f"rows{3 * B}")
+    rep = run_case(wl, seed=B, path="two_call")
+    parity.assert_parity(rep, f"{3 * B} rows {dtype}")
+
+
+@pytest.mark.parametrize("B", [2, 8, 9, 16, 17, 33, 64])
+def test_split_draw_part_counts(B):
+    """spec_verify_step at batches where the number of parts per sequence
+    changes (headline-length rows, 126 sweep items), against the oracle and
+    bit for bit against the two calls."""
+    wl = synth.workload("headline", B=B, K=2, V=128256, name=f"parts{B}")
+    inp = synth.make_inputs(wl, seed=100 + B, device="cuda")
+    say(f"[parts] B={B}: step vs two calls vs oracle")
+    a = parity.gpu_verify(inp, path="two_call")
+    b = parity.gpu_verify(inp, path="step")
+    for k in a:
+        assert a[k].tobytes() == b[k].tobytes(), k
+    o = parity.oracle_verify(synth.to_host_arrays(inp))
+    parity.assert_parity(parity.compare(b, o, inp["T"]), f"parts B={B}")
+
+
 def test_repeatable_and_stream_independent():
     inp = synth.make_inputs("small", seed=5, device="cuda")
     torch.cuda.synchronize()
