@@ -681,6 +681,7 @@ __device__ __forceinline__ void row_exp_n(const DrawRows& R, const float* z, con
 // lower token id in the low half), with the index arithmetic done on both
 // halves at once in 16-bit lanes.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 static_assert(kETabSign == 1u << 11 && kETabN < kETabSign, "sign bit 15 -> entry bit 11");
 
@@ -983,12 +984,26 @@ __device__ __forceinline__ void chunk_acc(const DrawRows& R, int c,
   chunk_accumulate<DT, MODE, H>(R, c, lookup, lsq, lsp, a, bb, out, nullptr, zq, zp);
 }
 
-// What a one-pass sweep of a row also gathers for its statistics: the
-// lane's largest value and the largest |code| of its bf16 words (above
-// 0x7F80: a NaN).
+// What a one-pass sweep of a row also gathers for its statistics, on the
+// bf16 codes themselves (two per word, one packed 16-bit operation each): the
+// largest code read as a signed 16-bit integer -- the largest non-negative
+// value when there is one --, the smallest code read as unsigned -- then the
+// negative value of least magnitude, the largest --, and the largest |code|
+// (above 0x7F80: a NaN).  Integer extrema need none of the canonicalising
+// moves the compiler puts before a float max.
 struct RowTrack {
-  float zmax = -__builtin_huge_valf();
-  unsigned mag = 0u;  // two 16-bit maxima, one per half-word
+  unsigned smax = 0x80008000u;  // i16x2 max of the codes
+  unsigned umin = 0xFF80FF80u;  // u16x2 min of the codes, from -inf's code
+  unsigned mag = 0u;            // u16x2 max of |code|
+  // The lane's largest value (-inf when it read nothing).
+  __device__ __forceinline__ float value() const {
+    const i16x2 sm = __builtin_bit_cast(i16x2, smax);
+    const u16x2 um = __builtin_bit_cast(u16x2, umin);
+    const int p = max(static_cast<int>(sm.x), static_cast<int>(sm.y));
+    const unsigned n = min(static_cast<unsigned>(um.x), static_cast<unsigned>(um.y));
+    const unsigned code = p >= 0 ? static_cast<unsigned>(p) : n;
+    return __uint_as_float(code << 16);
+  }
 };
 
 // chunk_accumulate from the raw words of bf16 rows with the exponential tables.
@@ -1001,12 +1016,16 @@ __device__ __forceinline__ void chunk_acc_words(const DrawRows& R, int c, const 
   if constexpr (TRACK) {
     const unsigned q4[4] = {wq.x, wq.y, wq.z, wq.w};
     u16x2 mg = __builtin_bit_cast(u16x2, trk->mag);
+    i16x2 sm = __builtin_bit_cast(i16x2, trk->smax);
+    u16x2 um = __builtin_bit_cast(u16x2, trk->umin);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      trk->zmax = fmaxf(trk->zmax, fmaxf(__uint_as_float(q4[k] << 16),
-                                         __uint_as_float(q4[k] & 0xFFFF0000u)));
+      sm = __builtin_elementwise_max(sm, __builtin_bit_cast(i16x2, q4[k]));
+      um = __builtin_elementwise_min(um, __builtin_bit_cast(u16x2, q4[k]));
       mg = __builtin_elementwise_max(mg, __builtin_bit_cast(u16x2, q4[k] & 0x7FFF7FFFu));
     }
+    trk->smax = __builtin_bit_cast(unsigned, sm);
+    trk->umin = __builtin_bit_cast(unsigned, um);
     trk->mag = __builtin_bit_cast(unsigned, mg);
   }
   const unsigned w8[8] = {wq.x, wq.y, wq.z, wq.w, wp.x, wp.y, wp.z, wp.w};
@@ -2046,7 +2065,7 @@ __global__ __launch_bounds__(BLOCK) void sample_onepass_kernel(const void* __res
   wave_sweep_claimed<DT, kModeBonus, kDrawG, true, decltype(emit), true>(
       R, uniform(tid / kWave), ni, nch, &sh.next, sh.tab, emit, &trk);
   // the row's maximum and NaN flag (block_max's barriers also end the sweep)
-  const float m = block_max<BLOCK>(trk.zmax, sh.redf);
+  const float m = block_max<BLOCK>(trk.value(), sh.redf);
   const bool nan = (trk.mag & 0xFFFFu) > 0x7F80u || (trk.mag >> 16) > 0x7F80u;
   const bool bad = block_max<BLOCK>(nan ? 1.0f : 0.0f, sh.redf) > 0.0f || !__builtin_isfinite(m);
   const double invT = yscale / Exp64::kScale;
