@@ -770,10 +770,13 @@ struct RawChunk {
   uint4 q, p;
 };
 
+// Whether chunk c lies whole inside aligned rows.  32-bit arithmetic (chunks
+// past the row's end are never asked about, and V <= 2^20), so that the test
+// stays on the scalar unit: there is no 64-bit scalar compare for order.
 template <int DT>
 __device__ __forceinline__ bool chunk_full(const DrawRows& R, int c) {
   constexpr int CH = kWave * (16 / Elt<DT>::bytes);
-  return R.aligned && static_cast<int64_t>(c + 1) * CH <= R.V;
+  return R.aligned && (c + 1) * CH <= R.V;
 }
 
 // Issue the loads of a full chunk (both rows together).
