@@ -1591,6 +1591,56 @@ __device__ __forceinline__ void wave_sweep_claimed(const DrawRows& R, int s0, in
   static_assert(!TRACK || (DT == kBF16 && ET), "row tracking rides on the bf16 table path");
   constexpr int E = 16 / Elt<DT>::bytes;
   const int lane = lane_id();
+  if constexpr (DT == kBF16 && ET && G == 2) {
+    // Two buffers, one per chunk of an item: the second chunk's loads go to
+    // b1 while the first is computed from b0, and the next item's first
+    // chunk to b0 once its words are used, so no chunk's words are copied
+    // out of a buffer that is about to be reloaded.
+    RawChunk b0, b1;
+    int s = s0;
+    bool full0 = s < ni && chunk_full<DT>(R, 2 * s);
+    if (full0) chunk_issue<DT, MODE>(R, 2 * s, b0);
+    while (s < ni) {
+      unsigned claimed = 0;
+      if (lane == 0) claimed = atomicAdd(next, 1u);
+      const int sn = static_cast<int>(uniform(claimed));  // the item after this one
+      ChunkSums cs;
+      chunk_sums_init(cs);
+      double a = 0.0, bb = 0.0, lq = 0.0, lp = 0.0;
+      const int c0 = 2 * s, c1 = c0 + 1;  // c0 < nsub: every item has a chunk
+      const bool has1 = c1 < nsub;
+      uint4 wq = b0.q, wp = b0.p;
+      if (!full0) {
+        float zq[E], zp[E];
+        chunk_values<DT, MODE>(R, c0, false, b0, zq, zp);
+        wq = pack_bf16_words(zq);
+        if (MODE == kModeResidual) wp = pack_bf16_words(zp);
+      }
+      const bool full1 = has1 && chunk_full<DT>(R, c1);
+      if (full1) chunk_issue<DT, MODE>(R, c1, b1);
+      chunk_acc_words<MODE, TRACK>(R, c0, wq, wp, tab, lq, lp, a, bb, cs, trk);
+      full0 = sn < ni && chunk_full<DT>(R, 2 * sn);
+      if (has1) {
+        uint4 vq = b1.q, vp = b1.p;
+        if (!full1) {
+          float zq[E], zp[E];
+          chunk_values<DT, MODE>(R, c1, false, b1, zq, zp);
+          vq = pack_bf16_words(zq);
+          if (MODE == kModeResidual) vp = pack_bf16_words(zp);
+        }
+        if (full0) chunk_issue<DT, MODE>(R, 2 * sn, b0);
+        chunk_acc_words<MODE, TRACK>(R, c1, vq, vp, tab, lq, lp, a, bb, cs, trk);
+      } else if (full0) {
+        chunk_issue<DT, MODE>(R, 2 * sn, b0);
+      }
+      chunk_reduce<MODE, true>(a, bb, cs);
+      const double lqr = MODE == kModeResidual ? wave_scan_rows(lq) : 0.0;
+      const double lpr = MODE == kModeResidual ? wave_scan_rows(lp) : 0.0;
+      emit(s, cs, lqr, lpr);
+      s = sn;
+    }
+    return;
+  }
   RawChunk buf;
   int s = s0;
   bool full = s < ni && chunk_full<DT>(R, G * s);
