@@ -47,6 +47,11 @@ per step, the mean and spread of the tokens emitted per sequence, the time per
 emitted token and the oracle's closed-form expectation; one JSON line with a
 "sweep" list.
 
+    python bench.py --mode overlap
+
+the step over batch slices on two streams (one slice's draw beside the next
+slice's stats), for several slice plans, next to the one-stream step.
+
     python bench.py --mode read-ceiling
 
 what a kernel that only reads gets from HBM here (the probe library's plain
@@ -564,6 +569,97 @@ def ksweep(args, base: synth.Workload) -> dict:
             "sweep": out}
 
 
+def overlap_plans(B: int) -> list:
+    """Slice plans for --mode overlap: (slice sizes summing to B, whether the
+    last slice runs as spec_verify_step, whose draw splits each sequence over
+    several workgroups when the slice holds at most SPLIT_DRAW_MAX_B)."""
+    def sizes(*fr):
+        s = [max(1, int(round(B * f))) for f in fr]
+        s[-1] = B - sum(s[:-1])
+        return s
+    plans = [(sizes(0.5, 0.5), False), (sizes(0.25, 0.25, 0.25, 0.25), False),
+             (sizes(0.375, 0.375, 0.25), True), (sizes(0.5625, 0.3125, 0.125), True)]
+    return [(s, last) for s, last in plans if min(s) > 0 and sum(s) == B and len(s) <= B]
+
+
+def overlap(args, wl: synth.Workload) -> dict:
+    """The step over batch slices on two streams: each slice's stats on the
+    step's stream, its accept scan and draw (spec_verify_sample) on a second
+    stream once that slice's stats are done, so that one slice draws while the
+    next streams; the last slice's draw on the first stream after its stats
+    (or the whole last slice as spec_verify_step).  Sequences are independent,
+    so every plan's outputs equal the one-stream step's; the record says
+    whether they did and the time per step of each plan beside the plain
+    two-call step's."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority, like every stream here
+    inp = synth.make_inputs(wl, seed=args.seed, device="cuda")
+    tgt, dft, tok, uni, T = inp["target"], inp["draft"], inp["tokens"], inp["uniforms"], wl.T
+    B, K, V, dev = wl.B, wl.K, wl.V, tgt.device
+
+    def outputs():
+        return dict(ts=torch.empty((B, K + 1, 2), dtype=torch.float32, device=dev),
+                    ds=torch.empty((B, K, 2), dtype=torch.float32, device=dev),
+                    n=torch.empty(B, dtype=torch.int32, device=dev),
+                    out=torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                    pr=torch.empty((B, K, 2), dtype=torch.float32, device=dev),
+                    ne=torch.empty(B, dtype=torch.int32, device=dev))
+
+    def scan_draw(a, b, o, st):
+        binding.verify_sample(tgt[a:b], dft[a:b], tok[a:b], uni[a:b], o["ts"][a:b],
+                              o["ds"][a:b], T, o["n"][a:b], o["out"][a:b], o["pr"][a:b],
+                              o["ne"][a:b], stream=st)
+
+    def make(sizes, last_step):
+        bounds = list(zip(np.cumsum([0] + sizes[:-1]).tolist(), np.cumsum(sizes).tolist()))
+        evs = [torch.cuda.Event() for _ in bounds]
+        ws = (binding.new_workspace(sizes[-1], K, V, tgt.dtype, dev) if last_step else None)
+
+        def run(o, ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            for i, (a, b) in enumerate(bounds):
+                last = i == len(bounds) - 1
+                if last and last_step:
+                    binding.verify_step(tgt[a:b], dft[a:b], tok[a:b], uni[a:b], T, ws,
+                                        o["ts"][a:b], o["ds"][a:b], o["n"][a:b], o["out"][a:b],
+                                        o["pr"][a:b], o["ne"][a:b], stream=stream)
+                    continue
+                binding.softmax_stats(tgt[a:b], dft[a:b], T, o["ts"][a:b], o["ds"][a:b],
+                                      stream=stream)
+                if last:
+                    scan_draw(a, b, o, stream)
+                else:
+                    evs[i].record(stream)
+                    side.wait_event(evs[i])
+                    scan_draw(a, b, o, side)
+            if len(bounds) > 1:
+                stream.wait_stream(side)
+            if ev is not None:
+                ev[1].record(stream)
+        return run
+
+    ref = outputs()
+    plans = [("one stream (two calls)", [B], False, make([B], False))]
+    plans += [(" + ".join(map(str, s)) + (", last as spec_verify_step" if ls else ""), s, ls,
+               make(s, ls)) for s, ls in overlap_plans(B)]
+    plans[0][3](ref)
+    torch.cuda.synchronize()
+    res = []
+    for name, sizes, ls, run in plans:
+        o = outputs()
+        ms, _ = timed(lambda ev=None: run(o, ev), args.steps, args.warmup, stream)
+        same = all(torch.equal(o[k], ref[k]) for k in ref)
+        res.append({"plan": name, "slices": sizes, "last_as_step": ls, "us_per_step": ms * 1e3,
+                    "outputs_equal_one_stream": bool(same)})
+        log(f"[bench] overlap {name}: {ms * 1e3:.1f} us/step, outputs equal: {same}")
+    return {"metric": f"verify step time over batch slices on two streams, B={B} K={K} V={V} "
+                      f"{wl.dtype} T={wl.T}",
+            "unit": "us per step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic", "config": {"workload": wl.name, "mode": "overlap"},
+            "plans": res}
+
+
 STAMP_TICK_US = 0.01  # the device's real-time counter runs at 100 MHz
 SPLIT_DRAW_MAX_B = 64  # spec_verify_step splits the final draw up to this batch
 
@@ -810,6 +906,13 @@ def summary_from(files: list, command: str) -> str:
                 out.append(f"| {k} | {v['median']:.2f} | {v['p10']:.2f} | {v['p90']:.2f} | "
                            f"{v['max']:.2f} | {v['n']} |")
             out.append("")
+    elif mode == "overlap":
+        r = recs[0]
+        out += [r["metric"] + ".", "", "| slices | µs per step | outputs equal the one-stream "
+                "step's |", "|---|---|---|"]
+        for x in r["plans"]:
+            out.append(f"| {x['plan']} | {x['us_per_step']:.1f} | "
+                       f"{'yes' if x['outputs_equal_one_stream'] else 'NO'} |")
     elif mode == "read-ceiling":
         r = recs[0]
         out += [r["metric"] + ".", "", "| shape | workgroups | µs | GB/s | % of 8 TB/s |",
@@ -849,7 +952,7 @@ def main() -> int:
                     help="override the workload's batch size B (0: the workload's own)")
     ap.add_argument("--mode", default="verify",
                     choices=["verify", "greedy", "sample", "filter", "filtered", "ksweep",
-                             "read-ceiling", "phases"],
+                             "read-ceiling", "phases", "overlap"],
                     help="verify (the headline step), time spec_greedy_verify / spec_sample, or "
                          "sweep K")
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
@@ -921,6 +1024,9 @@ def main() -> int:
         return 0
     if args.mode == "read-ceiling":
         print(json.dumps(read_ceiling(args, wl)), flush=True)
+        return 0
+    if args.mode == "overlap":
+        print(json.dumps(overlap(args, wl)), flush=True)
         return 0
     log(f"[bench] generating {wl.name}: B={wl.B} K={wl.K} V={wl.V} {wl.dtype} T={wl.T}")
     inp = synth.make_inputs(wl, seed=args.seed, device="cuda")

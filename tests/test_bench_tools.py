@@ -145,3 +145,28 @@ def test_summaries_from_json_lines(tmp_path):
     out = bench.summary_from([str(g)], "cmd")
     assert "| part: sweep of its items | 1.76 | 1.70 | 1.80 | 1.84 | 441 |" in out
     assert "empty" not in out
+
+
+def test_overlap_plans_cover_the_batch():
+    for B in (1, 2, 3, 17, 64, 100, 256):
+        plans = bench.overlap_plans(B)
+        for sizes, last_step in plans:
+            assert sum(sizes) == B and min(sizes) > 0
+    sizes = {tuple(s): ls for s, ls in bench.overlap_plans(256)}
+    assert sizes == {(128, 128): False, (64, 64, 64, 64): False, (96, 96, 64): True,
+                     (144, 80, 32): True}
+    # the split-row tail: a last slice that spec_verify_step draws over several workgroups
+    assert all(s[-1] <= bench.SPLIT_DRAW_MAX_B for s, ls in bench.overlap_plans(256) if ls)
+
+
+def test_overlap_summary(tmp_path):
+    rec = {"metric": "verify step time over batch slices", "config": {"mode": "overlap"},
+           "plans": [{"plan": "one stream (two calls)", "us_per_step": 193.9,
+                      "outputs_equal_one_stream": True},
+                     {"plan": "128 + 128", "us_per_step": 209.5,
+                      "outputs_equal_one_stream": False}]}
+    f = tmp_path / "o.json"
+    f.write_text(json.dumps(rec) + "\n")
+    out = bench.summary_from([str(f)], "cmd")
+    assert "| one stream (two calls) | 193.9 | yes |" in out
+    assert "| 128 + 128 | 209.5 | NO |" in out
