@@ -2297,6 +2297,10 @@ __global__ __launch_bounds__(kWave) void greedy_scan_kernel(const int32_t* __res
 // The thresholds of real rows lie close to the row maximum, so after a first
 // pass for the maximum a second pass collects into LDS the values of a window
 // at the top of the row, and the selects run over those few values.  The
+// nucleus without top-k on bf16 rows usually does both in one read: it
+// stages every body vector whose largest value lies near the block's running
+// maximum (a superset of a window, since that maximum only grows toward the
+// row's) and sums the mass of the other vectors.  The
 // window is [L, m] with L the k-th largest of the per-thread maxima for top-k
 // (k <= block size: at least k values lie at or above it), and otherwise the
 // values within kFilterWindow powers of two of probability below the
@@ -2318,6 +2322,15 @@ constexpr int kFilterMapVecs = 16384;  // 256 KB rows: bf16 up to 131072 tokens
 constexpr int kFilterKeyOff = kFilterCap - kFilterMapVecs / 2;
 static_assert(kFilterKeyOff >= 1024, "room for the per-thread maxima of a 1024-thread block");
 constexpr float kFilterWindow = 16.0f;
+// The one-read nucleus pass stages whole body vectors (16 bytes each, their
+// indices as 16-bit words behind them) in the candidate array, against a
+// shallower window: rows whose cut lies deeper fall back to the window pass.
+constexpr float kFilterWindowOne = 12.0f;
+constexpr int kStageCap = 2720;
+// Above this top_p the cut of a typical row lies deeper than that window, and
+// the two-read path (maximum, then the deeper window) is taken at once.
+constexpr float kFilterOneReadMaxP = 0.97f;
+static_assert(kStageCap * 18 <= kFilterCap * 4, "staged vectors and their indices fit");
 constexpr double kMassScale = 4398046511104.0;  // 2^42: V * 2^42 < 2^63 for V <= 2^20
 
 // Order-preserving key of a stored value; -0 is taken as +0 so that equal
@@ -2460,6 +2473,7 @@ struct FilterShared {
   int sel_bin;
   double sel_need;
   unsigned ncand;
+  unsigned mkey;  // the one-read nucleus pass: order key of the running maximum
   // 16-byte aligned: the top-k first pass's vector keys, kept in its upper
   // part, are read back 16 bytes at a time
   alignas(16) float cand[kFilterCap];
@@ -2670,6 +2684,45 @@ __device__ __forceinline__ void write_marked_row(const char* row, char* orow, in
   }
 }
 
+// The output row of a bf16 cut settled over the one-read pass's staged
+// vectors (input and output rows sharing their offset within 16 bytes): no
+// body vector is read again.  Every vector not marked in vmap is written as
+// -inf, and each marked one (a staged vector holding a kept token) is written
+// cut from its staged copy; the head and tail elements are read and cut.
+template <int BLOCK>
+__device__ __forceinline__ void write_staged_row(const char* row, char* orow, int V, float thr,
+                                                 const unsigned* vmap, const uint4* stage,
+                                                 const unsigned short* sidx, int n_stage) {
+  const int tid = threadIdx.x;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(row);
+  uint16_t* dst = reinterpret_cast<uint16_t*>(orow);
+  auto one = [&](uint32_t b) -> uint32_t {
+    return __uint_as_float(b << 16) < thr ? 0xFF80u : b;
+  };
+  auto word = [&](uint32_t w) -> uint32_t { return one(w & 0xFFFFu) | (one(w >> 16) << 16); };
+  const RowGeom<kBF16> G(row, V);
+  if (tid < G.head) dst[tid] = static_cast<uint16_t>(one(src[tid]));
+  if (tid < V - G.tail0) dst[G.tail0 + tid] = static_cast<uint16_t>(one(src[G.tail0 + tid]));
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u* vd = reinterpret_cast<v4u*>(orow + static_cast<int64_t>(G.head) * 2);
+  v4u ninf;
+  ninf.x = ninf.y = ninf.z = ninf.w = 0xFF80FF80u;
+  for (int i = tid; i < G.nvec; i += BLOCK)
+    if (((vmap[i >> 5] >> (i & 31)) & 1u) == 0u) __builtin_nontemporal_store(ninf, &vd[i]);
+  for (int j = tid; j < n_stage; j += BLOCK) {
+    const unsigned vi = sidx[j];
+    if (vi < static_cast<unsigned>(G.nvec) && ((vmap[vi >> 5] >> (vi & 31)) & 1u) != 0u) {
+      const uint4 w = stage[j];
+      v4u o;
+      o.x = word(w.x);
+      o.y = word(w.y);
+      o.z = word(w.z);
+      o.w = word(w.w);
+      __builtin_nontemporal_store(o, &vd[vi]);
+    }
+  }
+}
+
 template <int BLOCK, int DT, int VPG>
 __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out, int V,
                                                        float c2, double yscale, int top_k,
@@ -2696,10 +2749,125 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   unsigned short* vkey = reinterpret_cast<unsigned short*>(sh.cand + kFilterKeyOff);
   const RowGeom<DT> Gm(row, V);
 
+  // Nucleus without top-k on bf16 rows: one streamed read stages the body
+  // vectors that can hold the window (see the one_read branch below); when
+  // the cut lies in that window, only the vectors holding kept tokens are read
+  // again, for the output.
+  const bool one_read =
+      DT == kBF16 && use_p && !use_k && map_ok && top_p <= kFilterOneReadMaxP;
+  uint4* stage = reinterpret_cast<uint4*>(sh.cand);
+  unsigned short* sidx = reinterpret_cast<unsigned short*>(stage + kStageCap);
+  float mref = -__FLT_MAX__;  // reference of rest1's terms: exp2((x - mref) c2)
+  double rest1 = 0.0;
+
   // max, min and NaN
   float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
   unsigned long long nanm = 0;
-  if (skip) {
+  if (one_read) {
+    // Streamed once (non-temporal).  A body vector whose largest value is at
+    // or above zhi, kFilterWindowOne powers of two of probability below the
+    // largest value the block has published so far, is staged in LDS with its
+    // index (a head or tail element as a vector of its own, index 0xFFFF);
+    // since that maximum never exceeds the row's, every value of the window
+    // [m - kFilterWindowOne/c2, m] lies in a staged vector.  The values of
+    // the other vectors lie below that window, and their fp32 masses join
+    // rest1.  The first body group takes the maximum over all waves (one
+    // barrier); later groups read the LDS word without waiting.
+    if (tid == 0) sh.mkey = 0u;
+    __syncthreads();
+    const float wdepth = kFilterWindowOne / c2;
+    unsigned kseen = 0u;
+    bool first = true;
+    float tot1 = 0.0f;  // every term: NaN iff the row holds a NaN
+    for_each_group<BLOCK, DT, VPG, kLoadStream>(row, V, [&](const auto& x, int i0) {
+      constexpr int N = sizeof(x) / sizeof(float);
+      constexpr int NV = N > 1 ? N / EPV : 1;  // vectors
+      constexpr int L = N > 1 ? EPV : 1;       // values per vector
+      float vmx[NV];
+      float gm = -__builtin_huge_valf();
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        vmx[v] = x[v * L];
+#pragma unroll
+        for (int e = 1; e < L; ++e) vmx[v] = fmaxf(vmx[v], x[v * L + e]);
+        gm = fmaxf(gm, vmx[v]);
+      }
+      mx = fmaxf(mx, gm);
+      if (N > 1) {  // padding past the row is -inf and stays out of the minimum
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float vn = x[v * L];
+#pragma unroll
+          for (int e = 1; e < L; ++e) vn = fminf(vn, x[v * L + e]);
+          if (i0 + v * BLOCK < Gm.nvec) mn = fminf(mn, vn);
+        }
+      }
+      const unsigned kg = order_key<DT>(gm);
+      if (N > 1 && first) {
+        const float wm = wave_max(gm);
+        if (lane == 0) atomicMax(&sh.mkey, order_key<DT>(wm));
+        __syncthreads();
+        first = false;
+      } else if (kg > kseen) {
+        atomicMax(&sh.mkey, kg);
+      }
+      const unsigned kb = __hip_atomic_load(&sh.mkey, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_WORKGROUP);
+      kseen = kb > kseen ? kb : kseen;
+      kseen = kg > kseen ? kg : kseen;
+      const float ms = key_value<DT>(kseen);
+      // -inf values stay below zhi (their mass is 0)
+      const float zhi = fmaxf(ms - wdepth, -__FLT_MAX__);
+      // a new reference once the running maximum has risen by a power of two:
+      // every term then stays under 2 (tot1 cannot overflow), and those of the
+      // vectors below zhi under 2^-11
+      if ((ms - mref) * c2 >= 1.0f) {
+        rest1 *= static_cast<double>(__builtin_amdgcn_exp2f((mref - ms) * c2));
+        mref = ms;
+      }
+      bool fl[NV];
+      unsigned c = 0u;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float sv = __builtin_amdgcn_exp2f((x[v * L] - mref) * c2);
+#pragma unroll
+        for (int e = 1; e < L; ++e) sv += __builtin_amdgcn_exp2f((x[v * L + e] - mref) * c2);
+        tot1 += sv;
+        fl[v] = vmx[v] >= zhi;
+        rest1 += static_cast<double>(fl[v] ? 0.0f : sv);
+        c += fl[v] ? 1u : 0u;
+      }
+      if (__ballot(c != 0u) != 0ull) {
+        const unsigned incl = wave_incl_scan_u32(c);
+        const unsigned total =
+            static_cast<unsigned>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
+        unsigned base = 0u;
+        if (lane == 0) base = atomicAdd(&sh.ncand, total);
+        unsigned pos = uniform(base) + incl - c;
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          if (fl[v]) {
+            if (pos < static_cast<unsigned>(kStageCap)) {
+              if constexpr (N > 1) {
+                float z8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z8[e] = x[v * L + e];
+                stage[pos] = pack_bf16_words(z8);
+                sidx[pos] = static_cast<unsigned short>(i0 + v * BLOCK);
+              } else {
+                stage[pos] = make_uint4(0xFF800000u | (__float_as_uint(x[0]) >> 16), 0xFF80FF80u,
+                                        0xFF80FF80u, 0xFF80FF80u);
+                sidx[pos] = 0xFFFFu;
+              }
+            }
+            ++pos;
+          }
+      }
+    });
+    if (tid < Gm.head) mn = fminf(mn, logit_f32<DT>(row, tid));
+    if (tid < V - Gm.tail0) mn = fminf(mn, logit_f32<DT>(row, Gm.tail0 + tid));
+    nanm |= __ballot(tot1 != tot1);
+  } else if (skip) {
     // streamed once (non-temporal); padding entries are -inf and enter
     // neither the minimum nor the keys
     for_each_group<BLOCK, DT, VPG, kLoadStream>(row, V, [&](const auto& x, int i0) {
@@ -2758,13 +2926,73 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     constexpr int KB = DT == kBF16 ? 16 : 32;
     zlo = key_value<DT>(radix_select<BLOCK, DT, false>(fm, 0u, top_k, -1.0, m, yscale, 0u, KB, sh));
   }
-  if (!bad && (use_k || use_p)) {
+  // The one-read nucleus pass: the cut settled over the staged vectors when
+  // the window [zlo1, m] holds at least top_p of the row's mass.
+  bool staged = false;
+  int n_stage = 0;
+  float zlo1 = 0.0f;
+  // f(x) for the staged vectors' values in that window
+  auto fs = [&](auto f) {
+    for (int i = tid; i < n_stage; i += BLOCK) {
+      float z8[8];
+      unpack16<kBF16>(stage[i], z8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (z8[e] >= zlo1) f(z8[e]);
+    }
+  };
+  unsigned n_one = 0u;  // vectors the one-read pass staged (or tried to)
+  if (one_read) {
+    n_one = sh.ncand;
+    __syncthreads();  // read by every thread before a fallback clears it
+  }
+  if constexpr (DT == kBF16) {
+    if (!bad && one_read && n_one <= static_cast<unsigned>(kStageCap)) {
+      n_stage = static_cast<int>(n_one);
+      zlo1 = m - kFilterWindowOne / c2;
+      // the mass below the window: rest1, in units of mref's mass (mref <= m),
+      // and the staged values below zlo1, as fp32 terms like the window pass's
+      double rest = rest1 * static_cast<double>(__builtin_amdgcn_exp2f((mref - m) * c2));
+      for (int i = tid; i < n_stage; i += BLOCK) {
+        float z8[8];
+        unpack16<kBF16>(stage[i], z8);
+        float sv = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sv += z8[e] >= zlo1 ? 0.0f : __builtin_amdgcn_exp2f((z8[e] - m) * c2);
+        rest += static_cast<double>(sv);
+      }
+      unsigned long long win = 0ull;
+      fs([&](float x) { win += mass_fixed(x, m, yscale, sh.tab); });
+      const double rest_all = block_sum<BLOCK>(rest, sh.redd);
+      const unsigned long long win_all = block_sum_u64<BLOCK>(win, sh.redq);
+      const double S = static_cast<double>(win_all) + rint(rest_all * kMassScale);
+      if (static_cast<double>(win_all) >= static_cast<double>(top_p) * S) {
+        staged = true;
+        in_lds = true;
+        unsigned kmin = 0xFFFFFFFFu;
+        fs([&](float x) {
+          const unsigned k = order_key<DT>(x);
+          kmin = k < kmin ? k : kmin;
+        });
+        kmin = block_min_u32<BLOCK>(kmin, sh.redu);
+        const unsigned span = order_key<DT>(m) - kmin;
+        const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
+        thr_key = radix_select<BLOCK, DT, true>(fs, 0u, top_p, S, m, yscale, kmin, bits, sh);
+      }
+    }
+  }
+  if (!bad && (use_k || use_p) && !staged) {
     // the window: values >= zlo go to LDS (one slot range per wave and
     // group, taken with one LDS atomic), and the body vectors that hold them
     // are marked; for the nucleus without top-k the fp32 mass below the
     // window is summed on the way
     const bool masses = use_p && !use_k;
     float rest = 0.0f;
+    if (one_read) {  // the staged window missed the cut: a fresh window pass
+      if (tid == 0) sh.ncand = 0u;
+      __syncthreads();
+    }
     if (skip) {
       // the map from the keys: bit t of word w marks body vector 32w + t when
       // its key reaches zlo's (the dropped low key bits only widen the set,
@@ -2944,7 +3172,25 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   const bool marked = write && in_lds && cut && map_ok &&
                       ((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) == 0;
   double part = 0.0;
-  if (marked) {
+  if (marked && staged) {
+    // the vectors that hold a kept token: written from their staged copies
+    for (int i = tid; i < kFilterMapVecs / 32; i += BLOCK) sh.vmap[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < n_stage; i += BLOCK) {
+      float z8[8];
+      unpack16<kBF16>(stage[i], z8);
+      bool keep = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keep = keep || z8[e] >= thr;
+      const unsigned vi = sidx[i];
+      if (keep && vi < static_cast<unsigned>(Gm.nvec)) atomicOr(&sh.vmap[vi >> 5], 1u << (vi & 31));
+    }
+    __syncthreads();
+  }
+  if (marked && staged) {
+    if constexpr (DT == kBF16)
+      write_staged_row<BLOCK>(row, orow, V, thr, sh.vmap, stage, sidx, n_stage);
+  } else if (marked) {
     write_marked_row<BLOCK, DT>(row, orow, V, thr, sh.vmap);
   } else if (write && want && !s_lds) {
     part = finish_row<BLOCK, DT, true, true>(row, orow, V, cut, thr, m, c2);
@@ -2957,9 +3203,15 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     double sum = 0.0;
     if (s_lds) {
       unsigned long long f = 0ull;
-      for (int i = tid; i < n_lds; i += BLOCK) {
-        const float z = sh.cand[i];
-        if (z >= thr) f += mass_fixed(z, m, yscale, sh.tab);
+      if (staged) {
+        fs([&](float z) {
+          if (z >= thr) f += mass_fixed(z, m, yscale, sh.tab);
+        });
+      } else {
+        for (int i = tid; i < n_lds; i += BLOCK) {
+          const float z = sh.cand[i];
+          if (z >= thr) f += mass_fixed(z, m, yscale, sh.tab);
+        }
       }
       sum = static_cast<double>(block_sum_u64<BLOCK>(f, sh.redq)) * (1.0 / kMassScale);
     } else if (want) {

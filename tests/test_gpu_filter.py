@@ -184,6 +184,56 @@ def test_rows_outside_the_window(case):
     check_filter(z, T, k, p, case)
 
 
+@pytest.mark.parametrize("case", ["late_max", "staging_over_capacity", "tail_below_staged_window",
+                                  "invalid_and_masked", "at_the_top_p_bound", "headline_rows"])
+def test_nucleus_alone_one_read(case):
+    """bf16 nucleus without top-k: one streamed read stages the vectors near the
+    block's running maximum, and the cut is settled over them when their
+    window holds top_p of the mass.  Rows whose maximum comes last (the running
+    maximum rises late, so many vectors are staged), rows that stage more
+    vectors than LDS holds or whose cut lies below the staged window but above
+    the deeper one (both then take the window pass), invalid and masked rows,
+    top_p on both sides of the bound above which the two-read path is taken,
+    and sampled headline rows."""
+    seed = {"late_max": 71, "staging_over_capacity": 72, "tail_below_staged_window": 73,
+            "invalid_and_masked": 74, "at_the_top_p_bound": 75, "headline_rows": 76}[case]
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    if case == "late_max":
+        z = zipf_rows(24, 32000, "f32", seed=61)
+        z[:, -1] = z.max(dim=1).values + 2.0
+        check_filter(z.to(torch.bfloat16), 0.8, 0, 0.9, case)
+    elif case == "staging_over_capacity":
+        z = 0.3 * torch.randn(16, 60000, device="cuda", generator=g)
+        check_filter(z.to(torch.bfloat16), 1.0, 0, 0.5, case)
+    elif case == "tail_below_staged_window":
+        # the maximum (0) carries ~73 % of the mass; 3000 values between 12.3
+        # and 13.7 powers of two of probability below it carry the rest
+        R, V = 12, 32000
+        z = torch.full((R, V), -30.0, device="cuda")
+        for r in range(R):
+            pos = torch.randperm(V, generator=g, device="cuda")
+            z[r, pos[0]] = 0.0
+            z[r, pos[1:3001]] = -9.0 + (torch.rand(3000, generator=g, device="cuda") - 0.5)
+        check_filter(z.to(torch.bfloat16), 1.0, 0, 0.9, case)
+    elif case == "invalid_and_masked":
+        z = zipf_rows(8, 4000, "f32", seed=62)
+        z[1, 7] = float("nan")
+        z[2, :] = float("-inf")
+        z[3, ::2] = float("-inf")
+        z[4, :] = 0.5
+        z[5, 11] = float("inf")
+        z[6, 100:3000] = float("-inf")
+        check_filter(z.to(torch.bfloat16), 0.8, 0, 0.9, case)
+    elif case == "at_the_top_p_bound":
+        z = zipf_rows(24, 32000, "bf16", seed=63)
+        for p in (0.97, float(np.nextafter(np.float32(0.97), np.float32(1.0)))):
+            check_filter(z, 0.8, 0, p, f"{case} p={p!r}")
+    else:
+        inp = synth.make_inputs("headline", seed=6, device="cuda")
+        rows = inp["draft"].reshape(-1, inp["draft"].shape[-1])
+        check_filter(rows, inp["T"], 0, 0.9, case, rows=list(range(0, rows.shape[0], 61)))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_top_k_at_the_block_size(dtype):
     """top_k up to the filter's block size (512 threads) takes the window from
