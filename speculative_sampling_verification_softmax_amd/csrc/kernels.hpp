@@ -2757,7 +2757,9 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
       DT == kBF16 && use_p && !use_k && map_ok && top_p <= kFilterOneReadMaxP;
   uint4* stage = reinterpret_cast<uint4*>(sh.cand);
   unsigned short* sidx = reinterpret_cast<unsigned short*>(stage + kStageCap);
-  float mref = -__FLT_MAX__;  // reference of rest1's terms: exp2((x - mref) c2)
+  // rest1's terms are exp2(x c2 - mc): mc is mref c2 rounded to fp32, and the
+  // terms are exact relative to it (one rounding of the argument, in the fma)
+  float mref = -__FLT_MAX__, mc = -__FLT_MAX__;
   double rest1 = 0.0;
 
   // max, min and NaN
@@ -2793,15 +2795,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
         gm = fmaxf(gm, vmx[v]);
       }
       mx = fmaxf(mx, gm);
-      if (N > 1) {  // padding past the row is -inf and stays out of the minimum
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          float vn = x[v * L];
-#pragma unroll
-          for (int e = 1; e < L; ++e) vn = fminf(vn, x[v * L + e]);
-          if (i0 + v * BLOCK < Gm.nvec) mn = fminf(mn, vn);
-        }
-      }
+      // (no minimum: whether the cut removes anything is counted afterwards)
       const unsigned kg = order_key<DT>(gm);
       if (N > 1 && first) {
         const float wm = wave_max(gm);
@@ -2822,16 +2816,18 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
       // every term then stays under 2 (tot1 cannot overflow), and those of the
       // vectors below zhi under 2^-11
       if ((ms - mref) * c2 >= 1.0f) {
-        rest1 *= static_cast<double>(__builtin_amdgcn_exp2f((mref - ms) * c2));
+        const float mc2 = ms * c2;
+        rest1 *= static_cast<double>(__builtin_amdgcn_exp2f(mc - mc2));
         mref = ms;
+        mc = mc2;
       }
       bool fl[NV];
       unsigned c = 0u;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        float sv = __builtin_amdgcn_exp2f((x[v * L] - mref) * c2);
+        float sv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[v * L], c2, -mc));
 #pragma unroll
-        for (int e = 1; e < L; ++e) sv += __builtin_amdgcn_exp2f((x[v * L + e] - mref) * c2);
+        for (int e = 1; e < L; ++e) sv += __builtin_amdgcn_exp2f(__builtin_fmaf(x[v * L + e], c2, -mc));
         tot1 += sv;
         fl[v] = vmx[v] >= zhi;
         rest1 += static_cast<double>(fl[v] ? 0.0f : sv);
@@ -2864,8 +2860,6 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
           }
       }
     });
-    if (tid < Gm.head) mn = fminf(mn, logit_f32<DT>(row, tid));
-    if (tid < V - Gm.tail0) mn = fminf(mn, logit_f32<DT>(row, Gm.tail0 + tid));
     nanm |= __ballot(tot1 != tot1);
   } else if (skip) {
     // streamed once (non-temporal); padding entries are -inf and enter
@@ -2906,7 +2900,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     });
   }
   const float m = block_max<BLOCK>(mx, sh.redf);
-  const float lo = -block_max<BLOCK>(-mn, sh.redf);
+  float lo = -block_max<BLOCK>(-mn, sh.redf);  // the one-read pass leaves it for later
   if (lane == 0) sh.redu[wv] = nanm != 0ull ? 1u : 0u;
   __syncthreads();
   bool bad = !__builtin_isfinite(m);
@@ -2928,7 +2922,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   }
   // The one-read nucleus pass: the cut settled over the staged vectors when
   // the window [zlo1, m] holds at least top_p of the row's mass.
-  bool staged = false;
+  bool staged = false, staged_all = false;  // staged_all: the cut keeps every value
   int n_stage = 0;
   float zlo1 = 0.0f;
   // f(x) for the staged vectors' values in that window
@@ -2952,7 +2946,8 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
       zlo1 = m - kFilterWindowOne / c2;
       // the mass below the window: rest1, in units of mref's mass (mref <= m),
       // and the staged values below zlo1, as fp32 terms like the window pass's
-      double rest = rest1 * static_cast<double>(__builtin_amdgcn_exp2f((mref - m) * c2));
+      double rest =
+          rest1 * exp2(static_cast<double>(mc) - static_cast<double>(m) * static_cast<double>(c2));
       for (int i = tid; i < n_stage; i += BLOCK) {
         float z8[8];
         unpack16<kBF16>(stage[i], z8);
@@ -2979,6 +2974,12 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
         const unsigned span = order_key<DT>(m) - kmin;
         const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
         thr_key = radix_select<BLOCK, DT, true>(fs, 0u, top_p, S, m, yscale, kmin, bits, sh);
+        // the cut removes something unless every value is kept: all kept
+        // values lie in the window, so counting them there settles it
+        const float tv = key_value<DT>(thr_key);
+        unsigned long long nk = 0ull;
+        fs([&](float x) { nk += x >= tv ? 1ull : 0ull; });
+        staged_all = block_sum_u64<BLOCK>(nk, sh.redq) == static_cast<unsigned long long>(V);
       }
     }
   }
@@ -2992,6 +2993,9 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     if (one_read) {  // the staged window missed the cut: a fresh window pass
       if (tid == 0) sh.ncand = 0u;
       __syncthreads();
+      // which also takes the row's minimum (here from the head and tail)
+      if (tid < Gm.head) mn = fminf(mn, logit_f32<DT>(row, tid));
+      if (tid < V - Gm.tail0) mn = fminf(mn, logit_f32<DT>(row, Gm.tail0 + tid));
     }
     if (skip) {
       // the map from the keys: bit t of word w marks body vector 32w + t when
@@ -3062,6 +3066,15 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
       __syncthreads();
       for_each_group<BLOCK, DT, VPG>(row, V, [&](const auto& x, int i0) {
         constexpr int N = sizeof(x) / sizeof(float);
+        if (N > 1 && one_read) {  // padding past the row stays out of the minimum
+#pragma unroll
+          for (int u = 0; u < N / EPV; ++u) {
+            float vn = x[u * EPV];
+#pragma unroll
+            for (int e = 1; e < EPV; ++e) vn = fminf(vn, x[u * EPV + e]);
+            if (i0 + u * BLOCK < Gm.nvec) mn = fminf(mn, vn);
+          }
+        }
         unsigned c = 0u;
 #pragma unroll
         for (int e = 0; e < N; ++e) c += x[e] >= zlo ? 1u : 0u;
@@ -3098,6 +3111,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
         }
       });
     }
+    if (one_read) lo = -block_max<BLOCK>(-mn, sh.redf);
     const double rest_all = masses ? block_sum<BLOCK>(static_cast<double>(rest), sh.redd) : 0.0;
     __syncthreads();
     const unsigned n = sh.ncand;
@@ -3148,6 +3162,8 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   float thr = -__builtin_huge_valf();
   if (bad) {
     thr = __builtin_nanf("");
+  } else if (staged) {
+    if (!staged_all) thr = key_value<DT>(thr_key);
   } else if ((use_k || use_p) && thr_key > order_key<DT>(lo)) {
     thr = key_value<DT>(thr_key);
   }
