@@ -2327,6 +2327,8 @@ constexpr float kFilterWindow = 16.0f;
 // shallower window: rows whose cut lies deeper fall back to the window pass.
 constexpr float kFilterWindowOne = 12.0f;
 constexpr int kStageCap = 2720;
+// The staged values in the one-read window, compacted once for the selects.
+constexpr int kWinCap = 3072;
 // Above this top_p the cut of a typical row lies deeper than that window, and
 // the two-read path (maximum, then the deeper window) is taken at once.
 constexpr float kFilterOneReadMaxP = 0.97f;
@@ -2474,6 +2476,8 @@ struct FilterShared {
   double sel_need;
   unsigned ncand;
   unsigned mkey;  // the one-read nucleus pass: order key of the running maximum
+  unsigned nwin;  // ... and the count of its window values in win
+  float win[kWinCap];
   // 16-byte aligned: the top-k first pass's vector keys, kept in its upper
   // part, are read back 16 bytes at a time
   alignas(16) float cand[kFilterCap];
@@ -2822,7 +2826,9 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
         mc = mc2;
       }
       bool fl[NV];
-      unsigned c = 0u;
+      // slots in lane-major order from the ballots: the staged vectors of the
+      // lanes below this one, and the wave's total
+      unsigned below = 0u, total = 0u;
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         float sv = __builtin_amdgcn_exp2f(__builtin_fmaf(x[v * L], c2, -mc));
@@ -2831,15 +2837,15 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
         tot1 += sv;
         fl[v] = vmx[v] >= zhi;
         rest1 += static_cast<double>(fl[v] ? 0.0f : sv);
-        c += fl[v] ? 1u : 0u;
+        const unsigned long long bm = __ballot(fl[v]);
+        below += __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bm >> 32),
+                                           __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bm), 0u));
+        total += static_cast<unsigned>(__popcll(bm));
       }
-      if (__ballot(c != 0u) != 0ull) {
-        const unsigned incl = wave_incl_scan_u32(c);
-        const unsigned total =
-            static_cast<unsigned>(__shfl(static_cast<int>(incl), kWave - 1, kWave));
+      if (total != 0u) {  // wave-uniform
         unsigned base = 0u;
         if (lane == 0) base = atomicAdd(&sh.ncand, total);
-        unsigned pos = uniform(base) + incl - c;
+        unsigned pos = uniform(base) + below;
 #pragma unroll
         for (int v = 0; v < NV; ++v)
           if (fl[v]) {
@@ -2921,65 +2927,79 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     zlo = key_value<DT>(radix_select<BLOCK, DT, false>(fm, 0u, top_k, -1.0, m, yscale, 0u, KB, sh));
   }
   // The one-read nucleus pass: the cut settled over the staged vectors when
-  // the window [zlo1, m] holds at least top_p of the row's mass.
+  // the window [zlo1, m] holds at least top_p of the row's mass.  Its values
+  // are compacted into win once, and the selects run over that list alone.
   bool staged = false, staged_all = false;  // staged_all: the cut keeps every value
-  int n_stage = 0;
+  int n_stage = 0, n_win = 0;
   float zlo1 = 0.0f;
-  // f(x) for the staged vectors' values in that window
-  auto fs = [&](auto f) {
-    for (int i = tid; i < n_stage; i += BLOCK) {
-      float z8[8];
-      unpack16<kBF16>(stage[i], z8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (z8[e] >= zlo1) f(z8[e]);
-    }
+  // f(x) for the window's values
+  auto fw = [&](auto f) {
+    for (int i = tid; i < n_win; i += BLOCK) f(sh.win[i]);
   };
   unsigned n_one = 0u;  // vectors the one-read pass staged (or tried to)
   if (one_read) {
     n_one = sh.ncand;
+    if (tid == 0) sh.nwin = 0u;
     __syncthreads();  // read by every thread before a fallback clears it
   }
   if constexpr (DT == kBF16) {
     if (!bad && one_read && n_one <= static_cast<unsigned>(kStageCap)) {
       n_stage = static_cast<int>(n_one);
       zlo1 = m - kFilterWindowOne / c2;
-      // the mass below the window: rest1, in units of mref's mass (mref <= m),
-      // and the staged values below zlo1, as fp32 terms like the window pass's
+      // the mass below the window: rest1, relative to mc (mref c2 rounded,
+      // mref <= m), and the staged values below zlo1 as fp32 terms like the
+      // window pass's; the values at or above zlo1 go to win
       double rest =
           rest1 * exp2(static_cast<double>(mc) - static_cast<double>(m) * static_cast<double>(c2));
       for (int i = tid; i < n_stage; i += BLOCK) {
         float z8[8];
         unpack16<kBF16>(stage[i], z8);
         float sv = 0.0f;
+        unsigned c = 0u;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sv += z8[e] >= zlo1 ? 0.0f : __builtin_amdgcn_exp2f((z8[e] - m) * c2);
+        for (int e = 0; e < 8; ++e) {
+          const bool in = z8[e] >= zlo1;
+          c += in ? 1u : 0u;
+          sv += in ? 0.0f : __builtin_amdgcn_exp2f((z8[e] - m) * c2);
+        }
         rest += static_cast<double>(sv);
+        if (c != 0u) {
+          unsigned pos = atomicAdd(&sh.nwin, c);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (z8[e] >= zlo1) {
+              if (pos < static_cast<unsigned>(kWinCap)) sh.win[pos] = z8[e];
+              ++pos;
+            }
+        }
       }
-      unsigned long long win = 0ull;
-      fs([&](float x) { win += mass_fixed(x, m, yscale, sh.tab); });
-      const double rest_all = block_sum<BLOCK>(rest, sh.redd);
-      const unsigned long long win_all = block_sum_u64<BLOCK>(win, sh.redq);
-      const double S = static_cast<double>(win_all) + rint(rest_all * kMassScale);
-      if (static_cast<double>(win_all) >= static_cast<double>(top_p) * S) {
-        staged = true;
-        in_lds = true;
-        unsigned kmin = 0xFFFFFFFFu;
-        fs([&](float x) {
-          const unsigned k = order_key<DT>(x);
-          kmin = k < kmin ? k : kmin;
-        });
-        kmin = block_min_u32<BLOCK>(kmin, sh.redu);
-        const unsigned span = order_key<DT>(m) - kmin;
-        const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
-        thr_key = radix_select<BLOCK, DT, true>(fs, 0u, top_p, S, m, yscale, kmin, bits, sh);
-        // the cut removes something unless every value is kept: all kept
-        // values lie in the window, so counting them there settles it
-        const float tv = key_value<DT>(thr_key);
-        unsigned long long nk = 0ull;
-        fs([&](float x) { nk += x >= tv ? 1ull : 0ull; });
-        staged_all = block_sum_u64<BLOCK>(nk, sh.redq) == static_cast<unsigned long long>(V);
+      const double rest_all = block_sum<BLOCK>(rest, sh.redd);  // its barriers publish nwin
+      const unsigned nw = sh.nwin;
+      if (nw <= static_cast<unsigned>(kWinCap)) {
+        n_win = static_cast<int>(nw);
+        unsigned long long win = 0ull;
+        fw([&](float x) { win += mass_fixed(x, m, yscale, sh.tab); });
+        const unsigned long long win_all = block_sum_u64<BLOCK>(win, sh.redq);
+        const double S = static_cast<double>(win_all) + rint(rest_all * kMassScale);
+        if (static_cast<double>(win_all) >= static_cast<double>(top_p) * S) {
+          staged = true;
+          in_lds = true;
+          unsigned kmin = 0xFFFFFFFFu;
+          fw([&](float x) {
+            const unsigned k = order_key<DT>(x);
+            kmin = k < kmin ? k : kmin;
+          });
+          kmin = block_min_u32<BLOCK>(kmin, sh.redu);
+          const unsigned span = order_key<DT>(m) - kmin;
+          const int bits = span == 0u ? 0 : 32 - __builtin_clz(span);
+          thr_key = radix_select<BLOCK, DT, true>(fw, 0u, top_p, S, m, yscale, kmin, bits, sh);
+          // the cut removes something unless every value is kept: all kept
+          // values lie in the window, so counting them there settles it
+          const float tv = key_value<DT>(thr_key);
+          unsigned long long nk = 0ull;
+          fw([&](float x) { nk += x >= tv ? 1ull : 0ull; });
+          staged_all = block_sum_u64<BLOCK>(nk, sh.redq) == static_cast<unsigned long long>(V);
+        }
       }
     }
   }
@@ -3220,7 +3240,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
     if (s_lds) {
       unsigned long long f = 0ull;
       if (staged) {
-        fs([&](float z) {
+        fw([&](float z) {
           if (z >= thr) f += mass_fixed(z, m, yscale, sh.tab);
         });
       } else {
