@@ -372,17 +372,19 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
             if ev is not None:
                 ev[0].record(stream)
             binding.filter_rows(tgt, wl.T, args.top_k, args.top_p, out=ft, thresholds=tt,
-                                stream=stream)
+                                write_rows=not args.no_rows, stream=stream)
             binding.filter_rows(dft, wl.T, args.top_k, args.top_p, out=fd, thresholds=td,
-                                stream=stream)
+                                write_rows=not args.no_rows, stream=stream)
             if ev is not None:
                 ev[1].record(stream)
         ms, call_ms = timed(step, args.steps, args.warmup, stream)
         R = B * (2 * K + 1)
-        alg = 2 * R * V * wl.elt + R * 4  # each row read once and written once
+        # each row read once and written once (--no-rows: read once, thresholds only)
+        alg = (1 if args.no_rows else 2) * R * V * wl.elt + R * 4
         units, unit = B, "seqs/s"
         metric = (f"filtered seqs/sec (top-k {args.top_k}, top-p {args.top_p}, target and draft "
-                  f"rows), B={B} K={K} V={V} {wl.dtype}")
+                  f"rows{', thresholds only' if args.no_rows else ''}), B={B} K={K} V={V} "
+                  f"{wl.dtype}")
         kernel = "filter_kernel x2"
         cpu = None
         if args.cpu_seqs > 0:
@@ -479,12 +481,14 @@ def extra_mode(args, wl: synth.Workload, inp: dict, stream) -> dict:
         "config": dict({"workload": wl.name, "mode": args.mode, "B": B, "K": K, "V": V,
                         "logits": wl.dtype, "T": wl.T, "seed": args.seed},
                        **({"top_k": args.top_k, "top_p": args.top_p}
-                          if args.mode in ("filter", "filtered") else {})),
+                          if args.mode in ("filter", "filtered") else {}),
+                       **({"rows": "not written"} if args.mode == "filter" and args.no_rows
+                          else {})),
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": (find_traffic("filter_kernel", wl.name,
                                               filter_setting(args.top_k, args.top_p))
-                                 if args.mode == "filter" else None),
+                                 if args.mode == "filter" and not args.no_rows else None),
                      "launch_us": call_ms * 1e3, "bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }
@@ -931,6 +935,8 @@ def summary_from(files: list, command: str) -> str:
         for r in recs:
             c, rf, cb = r["config"], r["roofline"], r.get("cpu_baseline")
             setting = (f"top-k {c['top_k']}, top-p {c['top_p']}" if "top_k" in c else "—")
+            if c.get("rows") == "not written":
+                setting += ", thresholds only"
             tr = rf.get("traffic")
             trs = "—" if tr is None else f"{tr / rf['bytes_per_launch']:.3f}× algorithmic"
             cbs = "—" if not cb else f3(cb["value"]) + " " + cb["unit"]
@@ -958,6 +964,8 @@ def main() -> int:
     ap.add_argument("--ks", default="1,2,3,4,6,8,12,16", help="K values for --mode ksweep")
     ap.add_argument("--top-k", type=int, default=50, help="top-k for --mode filter (0: off)")
     ap.add_argument("--top-p", type=float, default=0.9, help="nucleus top_p for --mode filter")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="--mode filter: thresholds only, the filtered rows not written")
     ap.add_argument("--path", default="two_call", choices=["three_call", "two_call", "step"],
                     help="three_call: spec_softmax_stats, spec_verify, spec_residual_sample; "
                          "two_call: spec_softmax_stats, spec_verify_sample; "
