@@ -2755,8 +2755,8 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
 
   // Nucleus without top-k on bf16 rows: one streamed read stages the body
   // vectors that can hold the window (see the one_read branch below); when
-  // the cut lies in that window, only the vectors holding kept tokens are read
-  // again, for the output.
+  // the cut lies in that window, the output is written from the staged copies
+  // of the vectors holding kept tokens, and no body vector is read again.
   const bool one_read =
       DT == kBF16 && use_p && !use_k && map_ok && top_p <= kFilterOneReadMaxP;
   uint4* stage = reinterpret_cast<uint4*>(sh.cand);
@@ -3204,7 +3204,7 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   // When the cut was settled in LDS, every kept token lies in the window, so
   // a body vector that held no window value is all -inf in the output and
   // need not be read again: only the marked vectors (and the head and tail
-  // elements) are.
+  // elements) are, and after the one-read pass not even those.
   const bool marked = write && in_lds && cut && map_ok &&
                       ((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) == 0;
   double part = 0.0;

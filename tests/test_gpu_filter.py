@@ -253,6 +253,15 @@ def test_top_k_at_the_block_size(dtype):
     check_filter(view, 0.9, 300, 0.95, f"block-size ragged {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_vocabulary(dtype):
+    """V = 2^20, the largest vocabulary the header admits: rows longer than the
+    vector map (no marked re-read, no one-read nucleus) take the plain passes."""
+    z = zipf_rows(3, 1 << 20, dtype, seed=91)
+    for k, p in [(50, 0.9), (0, 0.9), (700, 1.0)]:
+        check_filter(z, 0.8, k, p, f"V=2^20 {dtype} k={k} p={p}")
+
+
 def test_repeatable():
     from speculative_sampling_verification_softmax_amd import binding
     z = zipf_rows(64, 32000, "f32", seed=41)

@@ -213,6 +213,22 @@ def test_sample_bf16_one_pass_edges(T):
     assert np.all(np.isnan(st[3:7, 1])) and not np.any(np.isnan(st[[0, 1, 2, 7, 8, 9], 1]))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_vocabulary(dtype):
+    """V = 2^20, the largest vocabulary the header admits: the sampler (bf16
+    rows past what its one-pass LDS arrays hold take the stats launch and the
+    per-row table), and greedy verify with K = 2."""
+    V = 1 << 20
+    g = torch.Generator(device="cuda").manual_seed(101)
+    ranks = torch.randperm(V, generator=g, device="cuda").to(torch.float32) + 1.0
+    z = 2.0 * torch.randn(3, V, device="cuda", generator=g) - 1.1 * torch.log(ranks)
+    z = z.to(torch.bfloat16) if dtype == "bf16" else z
+    check_sample(z, 0.8, 41, f"V=2^20 {dtype}")
+    rng = np.random.default_rng(5)
+    t = (2.0 * torch.randn(2, 3, V, device="cuda", generator=g)).to(z.dtype)
+    check_greedy(t, greedy_tokens(host_logits(t), rng, 0.8), f"greedy V=2^20 {dtype}")
+
+
 def test_sample_law_chi_square():
     """The draws follow softmax(z/T): chi-square of 2e5 draws on one row."""
     from scipy import special
