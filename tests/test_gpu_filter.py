@@ -184,19 +184,23 @@ def test_rows_outside_the_window(case):
     check_filter(z, T, k, p, case)
 
 
-@pytest.mark.parametrize("case", ["late_max", "staging_over_capacity", "tail_below_staged_window",
-                                  "invalid_and_masked", "at_the_top_p_bound", "headline_rows"])
+@pytest.mark.parametrize("case", ["late_max", "staging_over_capacity", "window_list_over_capacity",
+                                  "tail_below_staged_window", "invalid_and_masked",
+                                  "at_the_top_p_bound", "headline_rows"])
 def test_nucleus_alone_one_read(case):
     """bf16 nucleus without top-k: one streamed read stages the vectors near the
     block's running maximum, and the cut is settled over them when their
     window holds top_p of the mass.  Rows whose maximum comes last (the running
     maximum rises late, so many vectors are staged), rows that stage more
-    vectors than LDS holds or whose cut lies below the staged window but above
-    the deeper one (both then take the window pass), invalid and masked rows,
+    vectors than LDS holds, whose window holds more values than its list
+    (4000 near-maximal values in 500 consecutive vectors), or whose cut lies
+    below the staged window but above the deeper one (all three then take the
+    window pass), invalid and masked rows,
     top_p on both sides of the bound above which the two-read path is taken,
     and sampled headline rows."""
     seed = {"late_max": 71, "staging_over_capacity": 72, "tail_below_staged_window": 73,
-            "invalid_and_masked": 74, "at_the_top_p_bound": 75, "headline_rows": 76}[case]
+            "invalid_and_masked": 74, "at_the_top_p_bound": 75, "headline_rows": 76,
+            "window_list_over_capacity": 77}[case]
     g = torch.Generator(device="cuda").manual_seed(seed)
     if case == "late_max":
         z = zipf_rows(24, 32000, "f32", seed=61)
@@ -205,6 +209,10 @@ def test_nucleus_alone_one_read(case):
     elif case == "staging_over_capacity":
         z = 0.3 * torch.randn(16, 60000, device="cuda", generator=g)
         check_filter(z.to(torch.bfloat16), 1.0, 0, 0.5, case)
+    elif case == "window_list_over_capacity":
+        z = torch.full((8, 32000), -30.0, device="cuda")
+        z[:, 1000:5000] = 0.3 * torch.randn(8, 4000, device="cuda", generator=g)
+        check_filter(z.to(torch.bfloat16), 1.0, 0, 0.9, case)
     elif case == "tail_below_staged_window":
         # the maximum (0) carries ~73 % of the mass; 3000 values between 12.3
         # and 13.7 powers of two of probability below it carry the rest
