@@ -2753,6 +2753,99 @@ __global__ __launch_bounds__(BLOCK) void filter_kernel(const void* in, void* out
   unsigned short* vkey = reinterpret_cast<unsigned short*>(sh.cand + kFilterKeyOff);
   const RowGeom<DT> Gm(row, V);
 
+  // No transform: the threshold is -inf (NaN for a row that defines no
+  // distribution), the row is copied when the output is another buffer, and
+  // the stats are the row's own.  One streamed pass does all three: each
+  // body vector is stored to the output as it arrives, the maximum and NaN
+  // are tracked, and with stats every value folds into the stats kernel's
+  // accumulator.  (An output at another offset within 16 bytes takes the
+  // general path below.)
+  if (!use_k && !use_p) {
+    char* orow = (out != nullptr && out != in)
+                     ? static_cast<char*>(out) + r * static_cast<int64_t>(V) * Elt<DT>::bytes
+                     : nullptr;
+    if (orow == nullptr ||
+        ((reinterpret_cast<uintptr_t>(row) ^ reinterpret_cast<uintptr_t>(orow)) & 15) == 0) {
+      using Bits = typename std::conditional<DT == kBF16, uint16_t, uint32_t>::type;
+      const bool want = stats_out != nullptr;
+      RowAcc acc;
+      float mx0 = -__builtin_huge_valf();
+      bool nan = false;
+      auto scalar = [&](int i) {
+        const float x[1] = {logit_f32<DT>(row, i)};
+        if (orow != nullptr)
+          reinterpret_cast<Bits*>(orow)[i] = reinterpret_cast<const Bits*>(row)[i];
+        mx0 = fmaxf(mx0, x[0]);
+        nan = nan || x[0] != x[0];
+        if (want) fold(acc, x, c2);
+      };
+      if (tid < Gm.head) scalar(tid);
+      if (tid < V - Gm.tail0) scalar(Gm.tail0 + tid);
+      typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+      v4u* vd = orow != nullptr
+                    ? reinterpret_cast<v4u*>(orow + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes)
+                    : nullptr;
+      stream_body<BLOCK, DT, VPG, kLoadStream>(
+          row + static_cast<int64_t>(Gm.head) * Elt<DT>::bytes, Gm.nvec,
+          [&](const float(&x)[VPG * EPV], int i0) {
+            if (vd != nullptr) {
+#pragma unroll
+              for (int u = 0; u < VPG; ++u)
+                if (i0 + u * BLOCK < Gm.nvec) {  // the stored bits, repacked
+                  v4u o;
+                  if constexpr (DT == kBF16) {
+                    float z8[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) z8[e] = x[u * EPV + e];
+                    const uint4 w = pack_bf16_words(z8);
+                    o.x = w.x;
+                    o.y = w.y;
+                    o.z = w.z;
+                    o.w = w.w;
+                  } else {
+                    o.x = __float_as_uint(x[u * EPV]);
+                    o.y = __float_as_uint(x[u * EPV + 1]);
+                    o.z = __float_as_uint(x[u * EPV + 2]);
+                    o.w = __float_as_uint(x[u * EPV + 3]);
+                  }
+                  __builtin_nontemporal_store(o, &vd[i0 + u * BLOCK]);
+                }
+            }
+            mx0 = fmaxf(mx0, group_max(x));
+#pragma unroll
+            for (int e = 0; e < VPG * EPV; ++e) nan = nan || x[e] != x[e];
+            if (want) fold(acc, x, c2);
+          });
+      const float m0 = block_max<BLOCK>(mx0, sh.redf);
+      const bool wave_nan = __ballot(nan) != 0ull;  // every lane votes
+      if (lane == 0) sh.redu[wv] = wave_nan ? 1u : 0u;
+      __syncthreads();
+      bool bad0 = !__builtin_isfinite(m0);
+      for (int w = 0; w < NW; ++w) bad0 = bad0 || sh.redu[w] != 0u;
+      if (tid == 0) thr_out[r] = bad0 ? __builtin_nanf("") : -__builtin_huge_valf();
+      if (want) {
+        float sf = __builtin_nanf("");
+        if (!bad0) {
+          if (fabsf(m0 * c2) < kShiftMax) {
+            const float kr = rintf(m0 * c2);
+            const double sum =
+                block_sum<BLOCK>(ldexp(acc.s, static_cast<int>(acc.k - kr)), sh.redd);
+            const double t =
+                static_cast<double>(kr) - static_cast<double>(m0) * static_cast<double>(c2);
+            sf = static_cast<float>(sum * exp2(t));
+          } else {
+            sf = static_cast<float>(row_stats_wide<BLOCK, DT>(row, V, c2, m0, sh.redf, sh.redd));
+          }
+        }
+        if (tid == 0) {
+          stats_out[2 * r] = m0;
+          stats_out[2 * r + 1] = sf;
+        }
+      }
+      return;
+    }
+  }
+
   // Nucleus without top-k on bf16 rows: one streamed read stages the body
   // vectors that can hold the window (see the one_read branch below); when
   // the cut lies in that window, the output is written from the staged copies

@@ -262,6 +262,27 @@ def test_top_k_at_the_block_size(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_transform(dtype):
+    """top_k off and top_p = 1: thresholds -inf (NaN for rows that define no
+    distribution), the rows copied bit for bit, their own stats; one streamed
+    pass when the output shares the input's offset within 16 bytes (a new
+    buffer, or in place with nothing written), the general path otherwise."""
+    z = zipf_rows(16, 32000, "f32", seed=81)
+    z[3, 77] = float("nan")
+    z[4, :] = float("-inf")
+    z[5, 9] = float("inf")
+    z[6, ::2] = float("-inf")
+    z = z.to(torch.bfloat16) if dtype == "bf16" else z
+    check_filter(z, 0.8, 0, 1.0, f"no transform {dtype}")
+    check_filter(z.clone(), 0.8, 0, 1.0, f"no transform in place {dtype}", inplace=True)
+    big = torch.empty(16 * 32000 + 3, dtype=z.dtype, device="cuda")
+    view = big[3:].view(16, 32000)  # rows off 16-byte boundaries
+    view.copy_(z)
+    check_filter(view, 0.8, 0, 1.0, f"no transform unaligned {dtype}")
+    check_filter(zipf_rows(9, 7, dtype, seed=82), 1.1, 0, 1.0, f"no transform V=7 {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_maximum_vocabulary(dtype):
     """V = 2^20, the largest vocabulary the header admits: rows longer than the
     vector map (no marked re-read, no one-read nucleus) take the plain passes."""
