@@ -282,6 +282,29 @@ def test_no_transform(dtype):
     check_filter(zipf_rows(9, 7, dtype, seed=82), 1.1, 0, 1.0, f"no transform V=7 {dtype}")
 
 
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (50, 0.9), (0, 0.9), (0, 0.5), (0, 0.99)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_huge_logits(dtype, top_k, top_p):
+    """Logits whose max times log2(e)/T reaches 2^22 and beyond, up to where
+    that product overflows fp32: the statistics switch to the wide route
+    (difference to the max taken first), and no reference or rescale in the
+    passes may overflow; ties at the top, a masked half, and rows far apart in
+    scale."""
+    z = zipf_rows(10, 4000, "f32", seed=85)
+    z[0] *= 1e4              # |m c2| below 2^22
+    z[1] *= 1e7              # above 2^22: the wide statistics
+    z[2, 100:110] = 3e37     # ten tied maxima far above the rest
+    z[3, 3000:3010] = 2.5e38  # m c2 beyond the largest float (T = 0.8)
+    z[4, ::2] = -3e38
+    z[5, :] = 3e37           # every value tied
+    z[6] *= 1e30
+    z[7, 17] = 3.3e38
+    z[7, 18] = 3.2e38
+    z[8] = z[8] * 1e35 + 2e38  # a dense top near the fp32 limit
+    z = z.to(torch.bfloat16) if dtype == "bf16" else z
+    check_filter(z, 0.8, top_k, top_p, f"huge logits {dtype} k={top_k} p={top_p}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_maximum_vocabulary(dtype):
     """V = 2^20, the largest vocabulary the header admits: rows longer than the
