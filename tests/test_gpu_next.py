@@ -213,6 +213,38 @@ def test_sample_bf16_one_pass_edges(T):
     assert np.all(np.isnan(st[3:7, 1])) and not np.any(np.isnan(st[[0, 1, 2, 7, 8, 9], 1]))
 
 
+@pytest.mark.parametrize("T", [0.8, 3.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_huge_logits(dtype, T):
+    """Logits up to the fp32 limit: maxima whose product with log2(e)/T passes
+    2^22 or overflows fp32, ten tied maxima far above the rest (the draw picks
+    among them), one repeated value, a half masked at -3e38, rows far apart in
+    scale; the sampler's tokens and statistics against the oracle, and greedy
+    verify's argmax on the same kinds of rows."""
+    g = torch.Generator(device="cuda").manual_seed(88)
+    R, V = 12, 3000
+    z = torch.randn(R, V, device="cuda", generator=g) * 2
+    z[0] *= 1e4
+    z[1] *= 1e7
+    z[2, 100:110] = 3e37
+    z[3, 2990:3000] = 2.5e38
+    z[4, ::2] = -3e38
+    z[5, :] = 3e37
+    z[6] *= 1e30
+    z[7, 17] = 3.3e38
+    z[7, 18] = 3.2e38
+    z[8] = z[8] * 1e35 + 2e38
+    z[9, :] = -3e38
+    z[9, 5] = -1e38           # one token far above a floor at -3e38
+    z[10, 1500:] = float("-inf")
+    z[10, :1500] *= 1e36
+    z = z.to(torch.bfloat16) if dtype == "bf16" else z
+    check_sample(z, T, 43, f"huge logits {dtype} T={T}")
+    rng = np.random.default_rng(9)
+    t = z[:9].reshape(3, 3, V).contiguous()
+    check_greedy(t, greedy_tokens(host_logits(t), rng, 0.7), f"greedy huge logits {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_maximum_vocabulary(dtype):
     """V = 2^20, the largest vocabulary the header admits: the sampler (bf16
