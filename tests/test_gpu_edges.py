@@ -181,6 +181,25 @@ def test_extreme_logit_magnitudes():
     _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), 1.0), "extreme")
 
 
+@pytest.mark.parametrize("T", [0.8, 3.0])
+def test_extreme_logit_magnitudes_bf16(T):
+    """bf16 rows whose maxima lie far beyond the draw's shared exp(z/T)
+    table (|m|/T > 300): 3e37 tied tops over a -3e37 floor, maxima whose
+    product with log2(e)/T overflows fp32 (2.5e38, and 3.3e38 in some
+    drafts only), and rows scaled to 1e30; every path against the oracle."""
+    rng = np.random.default_rng(16)
+    B, K, V = 16, 3, 1000
+    tgt = (rng.standard_normal((B, K + 1, V)) * 1e4).astype(np.float32)
+    tgt[:, :, :10] = 3e37
+    tgt[:, :, 10:20] = -3e37
+    tgt[::4, :, 500] = 2.5e38
+    tgt[1::4, :, 20:] *= np.float32(1e26)
+    dft = (tgt[:, :K] + 1e3 * rng.standard_normal((B, K, V))).astype(np.float32)
+    dft[2::4, :, 700] = 3.3e38
+    tok = _tokens_from(rng, dft, T)
+    _check(_to_dev(tgt, dft, tok, _uni(rng, B, K), T, "bf16"), f"extreme bf16 T={T}")
+
+
 def test_forced_counts_and_zero_residual_fallback():
     """Caller-supplied accepted counts: identical rows at the rejected position
     give a residual with no mass, so the draw falls back to q (Pitfalls)."""
