@@ -1013,8 +1013,9 @@ def main() -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the verify shards by sequence and needs "
-              "no collective; multi-GPU runs are not part of this build", file=sys.stderr)
+        print("bench.py measures one GPU: sequences are independent, so several GPUs would "
+              "each verify their own share of the batch with no collective; run it with "
+              "--gpus 1 and no WORLD_SIZE above 1", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)

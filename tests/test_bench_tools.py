@@ -170,3 +170,17 @@ def test_overlap_summary(tmp_path):
     out = bench.summary_from([str(f)], "cmd")
     assert "| one stream (two calls) | 193.9 | yes |" in out
     assert "| 128 + 128 | 209.5 | NO |" in out
+
+
+def test_more_than_one_gpu_is_refused():
+    """--gpus above 1 (or a WORLD_SIZE above 1) ends at once with status 2 and
+    a message, before any GPU call."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for args, env in ((["--gpus", "2"], {}), (["--gpus", "1"], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + args,
+                           capture_output=True, text=True, timeout=300,
+                           env={**os.environ, **env})
+        assert r.returncode == 2, r.stderr
+        assert "one GPU" in r.stderr and r.stdout == ""

@@ -5,7 +5,7 @@ checked instead: the C ABI's argument checks, shape and size arithmetic and
 status strings (tests/sanitize/abi_driver.c against a build of the library
 whose host part is instrumented), and the fp64 oracle over seeded inputs and
 the edge cases its callers meet (tests/sanitize/oracle_driver.c).  Any
-sanitizer report ends the driver with a non-zero status; leaks are reported
+sanitizer report ends that test program with a non-zero status; leaks are reported
 too."""
 import os
 import shutil
